@@ -1,0 +1,513 @@
+"""Pins for the CPU oracle: each oracle function checked against something
+other than itself -- textbook known answers (tests/golden), closed forms,
+invariants the method implies, special cases that reduce to a textbook
+result, and brute force on tiny inputs.
+
+Sources: "Technical Summary: ParisKV" (gist.science/paper/2602.07721),
+Core Algorithmic Innovations 1 (normalisation + SRHT rotation, analytic sign
+centroids) and 2 (collision-based coarse candidates; RSQ-IP reranking);
+Problem Statement (Top-k sparse attention).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate, linalg, special
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def signs_for(d, seed=1):
+    return np.where(rng(seed).integers(0, 2, d) == 1, -1, 1).astype(np.int8)
+
+
+def skewed_keys(n, d, seed):
+    r = rng(seed)
+    s = np.exp(0.5 * r.standard_normal(d))
+    s[r.choice(d, 4, replace=False)] *= 8
+    return (r.standard_normal((n, d)) * s).astype(np.float32)
+
+
+# ---------------------------------------------------------------- fp16 ----
+
+def test_f16_golden_known_answers(orc):
+    for line in open(os.path.join(GOLDEN, "binary16_known_answers.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        a, b = line.split()
+        v = np.float32(float(a) if "inf" in a else float.fromhex(a))
+        assert orc.f32_to_f16([v])[0] == int(b, 16), a
+
+
+def test_f16_matches_numpy_rne(orc):
+    r = rng(7)
+    # random bit patterns over the whole finite fp32 range that matters
+    exps = r.integers(100, 145, 20000).astype(np.uint32)
+    mant = r.integers(0, 1 << 23, 20000).astype(np.uint32)
+    sgn = r.integers(0, 2, 20000).astype(np.uint32)
+    bits = (sgn << 31) | (exps << 23) | mant
+    x = bits.view(np.float32)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    got = orc.f32_to_f16(x)
+    assert np.array_equal(got, ref)
+    # exact ties at every exponent (RNE decides them)
+    t = (np.arange(1, 2000, dtype=np.float32) + 0.5) * np.float32(2.0 ** -10)
+    assert np.array_equal(orc.f32_to_f16(t), t.astype(np.float16).view(np.uint16))
+
+
+def test_f16_to_f32_exact(orc):
+    h = np.arange(0, 1 << 16, 97, dtype=np.uint16)
+    ref = h.view(np.float16).astype(np.float32)
+    got = orc.f16_to_f32(h)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin].view(np.uint32), ref[fin].view(np.uint32))
+
+
+# ------------------------------------------------------------ codebook ----
+
+@pytest.mark.parametrize("m", [4, 8])
+def test_codebook_lloyd_max_fixed_point(orc, m):
+    """Levels are conditional means of their cells and thresholds are
+    midpoints, under the density of |u_j| for u uniform on S^{m-1}, checked
+    with scipy's adaptive quadrature in t (an independent integrator)."""
+    L, tau = orc.codebook(m)
+    f = lambda t: (1.0 - t * t) ** ((m - 3) / 2.0)
+    edges = np.concatenate([[0.0], tau, [1.0]])
+    for l in range(8):
+        mass = integrate.quad(f, edges[l], edges[l + 1], epsabs=1e-14,
+                              epsrel=1e-13, limit=200)[0]
+        first = integrate.quad(lambda t: t * f(t), edges[l], edges[l + 1],
+                               epsabs=1e-14, epsrel=1e-13, limit=200)[0]
+        assert abs(first / mass - L[l]) < 1e-9, (l, first / mass, L[l])
+    for l in range(7):
+        assert abs(tau[l] - 0.5 * (L[l] + L[l + 1])) < 1e-15
+    assert np.all(np.diff(L) > 0) and 0 < L[0] and L[-1] < 1
+
+
+@pytest.mark.parametrize("m", [4, 8])
+def test_codebook_prior_is_sphere_marginal(orc, m):
+    """Closed form: E|u_1| = Gamma(m/2) / (sqrt(pi) Gamma((m+1)/2)) for u
+    uniform on S^{m-1}; conditional-mean levels preserve the mean, so
+    sum_l P(cell_l) L_l must equal it.  A wrong Beta exponent fails this."""
+    L, tau = orc.codebook(m)
+    a, b = 0.5, (m - 1) / 2.0   # u_j^2 ~ Beta(1/2, (m-1)/2)
+    edges = np.concatenate([[0.0], tau, [1.0]])
+    probs = np.diff(special.betainc(a, b, edges ** 2))
+    mean_q = float(np.sum(probs * L))
+    exact = math.gamma(m / 2) / (math.sqrt(math.pi) * math.gamma((m + 1) / 2))
+    assert abs(mean_q - exact) < 1e-10
+    # Monte Carlo: empirical cell frequencies of |u_j| match the prior
+    g = rng(3).standard_normal((200000, m))
+    u = np.abs(g / np.linalg.norm(g, axis=1, keepdims=True)).ravel()
+    freq = np.bincount(np.searchsorted(tau, u, side="right"), minlength=8)
+    freq = freq / u.size
+    assert np.max(np.abs(freq - probs)) < 3e-3
+
+
+def test_codebook_f32_is_nearest_fp32(orc):
+    L, tau = orc.codebook(8)
+    L32, tau32 = orc.codebook_f32(8)
+    assert np.array_equal(L32, L.astype(np.float32))
+    assert np.array_equal(tau32, tau.astype(np.float32))
+
+
+# ------------------------------------------------------------ rotation ----
+
+def test_rot_scale_value(orc):
+    assert np.float32(orc.rot_scale(128)).view(np.uint32) == 0x3DB504F3
+    for d in (2, 8, 32, 128, 256, 1024):
+        assert orc.rot_scale(d) == np.float32(1.0 / math.sqrt(d))
+
+
+def test_rotation_golden_sylvester_8(orc):
+    H = np.loadtxt(os.path.join(GOLDEN, "hadamard_sylvester_8.txt"))
+    c = orc.rot_scale(8)
+    plus = np.ones(8, np.int8)
+    for j in range(8):
+        e = np.zeros(8, np.float32)
+        e[j] = 1
+        y = orc.rotate(plus, e)
+        assert np.array_equal(y, (c * H[:, j]).astype(np.float32))
+
+
+def test_rotation_closed_form_basis(orc):
+    d = 128
+    D = signs_for(d)
+    c = orc.rot_scale(d)
+    i = np.arange(d)
+    for j in range(d):
+        e = np.zeros(d, np.float32)
+        e[j] = 1
+        y = orc.rotate(D, e)
+        par = np.array([bin(v & j).count("1") & 1 for v in i])
+        want = (c * D[j] * np.where(par == 1, -1.0, 1.0)).astype(np.float32)
+        assert np.array_equal(y, want)
+
+
+def test_rotation_orthogonal_and_dense_match(orc):
+    d = 128
+    D = signs_for(d, 5)
+    X = skewed_keys(64, d, 11)
+    Y = orc.rotate(D, X)
+    R = linalg.hadamard(d) / math.sqrt(d) * D[None, :].astype(np.float64)
+    Yd = X.astype(np.float64) @ R.T
+    assert np.max(np.abs(Y - Yd)) <= 1e-6 * np.max(np.abs(Yd))
+    nx = np.linalg.norm(X.astype(np.float64), axis=1)
+    ny = np.linalg.norm(Y.astype(np.float64), axis=1)
+    assert np.max(np.abs(nx - ny) / nx) < 2e-6
+    G0 = X.astype(np.float64) @ X.T.astype(np.float64)
+    G1 = Y.astype(np.float64) @ Y.T.astype(np.float64)
+    assert np.max(np.abs(G0 - G1)) < 2e-6 * np.max(np.abs(G0))
+    # c*H is an involution: D * (c H (c H D x)) = x
+    plus = np.ones(d, np.int8)
+    back = orc.rotate(plus, Y) * D[None, :]
+    assert np.max(np.abs(back - X)) < 1e-5 * np.max(np.abs(X))
+
+
+# -------------------------------------------------------------- encode ----
+
+def test_bucket_id_is_nearest_sign_centroid(orc):
+    d, m = 128, 8
+    D = signs_for(d)
+    X = skewed_keys(300, d, 21)
+    ids, nib, w = orc.encode_keys(D, X, m)
+    Y = orc.rotate(D, X).astype(np.float64)
+    P = 1 << m
+    cent = np.array([[-1.0 if (p >> j) & 1 else 1.0 for j in range(m)]
+                     for p in range(P)]) / math.sqrt(m)
+    for b in range(d // m):
+        sims = Y[:, b * m:(b + 1) * m] @ cent.T        # [n, 256]
+        best = np.argmax(sims, axis=1)                 # ties -> lowest p
+        assert np.array_equal(best, ids[:, b])
+
+
+def _unpack(nib):
+    lo = nib & 0xF
+    hi = nib >> 4
+    return np.stack([lo, hi], axis=-1).reshape(nib.shape[0], -1)
+
+
+def test_codes_sign_bits_and_magnitudes(orc):
+    d, m = 128, 8
+    D = signs_for(d)
+    X = skewed_keys(300, d, 22)
+    ids, nib, w = orc.encode_keys(D, X, m)
+    codes = _unpack(nib)                               # [n, 128]
+    Y = orc.rotate(D, X).astype(np.float64)
+    _, tau = orc.codebook(m)
+    for b in range(16):
+        z = Y[:, b * m:(b + 1) * m]
+        sgn = codes[:, b * m:(b + 1) * m] >> 3
+        idbits = (ids[:, b:b + 1] >> np.arange(m)[None]) & 1
+        assert np.array_equal(sgn, idbits)
+        assert np.array_equal(sgn, (z < 0).astype(sgn.dtype))
+        u = np.abs(z) / np.linalg.norm(z, axis=1, keepdims=True)
+        mag = np.searchsorted(tau, u, side="right")
+        near = np.min(np.abs(u[..., None] - tau[None, None]), axis=-1) < 1e-5
+        got = codes[:, b * m:(b + 1) * m] & 7
+        assert np.array_equal(got[~near], mag[~near])
+
+
+def test_nibble_order_on_designed_direction(orc):
+    """A rotated key designed with known per-coordinate magnitudes: coordinate
+    j of subspace 0 has |u_j| inside magnitude cell j (cells 0..7), signs
+    alternating.  Decoding must return codes in coordinate order."""
+    d, m = 128, 8
+    D = signs_for(d)
+    L, tau = orc.codebook(m)
+    mids = L.copy()                                 # a level lies inside its cell
+    u = mids * np.where(np.arange(m) % 2 == 1, -1.0, 1.0)
+    u = u / np.linalg.norm(u)
+    # re-normalisation shrinks |u_j|; rescale so each stays in its cell
+    y = np.zeros(d)
+    y[:m] = u * 3.0
+    y[m:] = 1.0
+    plus = np.ones(d, np.int8)
+    x = (orc.rotate(plus, y.astype(np.float32)).astype(np.float64) * D)
+    ids, nib, w = orc.encode_keys(D, x.astype(np.float32)[None], m)
+    codes = _unpack(nib)[0, :m]
+    yy = orc.rotate(D, x.astype(np.float32)[None])[0, :m].astype(np.float64)
+    uu = np.abs(yy) / np.linalg.norm(yy)
+    want_mag = np.searchsorted(tau, uu, side="right")
+    want = ((yy < 0).astype(int) << 3) | want_mag
+    assert list(codes) == list(want)
+    assert len(set(want_mag.tolist())) >= 6      # magnitudes really differ
+
+
+def test_zero_subspace_gives_zero_w(orc):
+    d, m = 128, 8
+    D = signs_for(d)
+    ids, nib, w = orc.encode_keys(D, np.zeros((1, d), np.float32), m)
+    assert not ids.any() and not nib.any() and not w.any()
+
+
+# ---------------------------------------------------------- query prep ----
+
+def _top_brute(yqb, rho):
+    m = yqb.shape[0]
+    sc = []
+    for p in range(1 << m):
+        s = sum((-yqb[j] if (p >> j) & 1 else yqb[j]) for j in range(m))
+        sc.append((-s, p))
+    return [p for _, p in sorted(sc)[:rho]]
+
+
+def _top_closed_form(yqb):
+    """rho = 4 closed form in exact arithmetic: the sign pattern, then flips
+    of the smallest |yq_j|; flipping set F costs 2 sum_F |yq_j|."""
+    m = yqb.shape[0]
+    r1 = sum(1 << j for j in range(m) if yqb[j] < 0)
+    order = np.argsort(np.abs(yqb), kind="stable")
+    a = np.abs(yqb)[order]
+    j1, j2, j3 = order[:3]
+    r2, r3 = r1 ^ (1 << j1), r1 ^ (1 << j2)
+    r4 = r1 ^ (1 << j3) if a[2] < a[0] + a[1] else r1 ^ (1 << j1) ^ (1 << j2)
+    return [r1, r2, r3, r4]
+
+
+def test_query_prep_top_rho(orc):
+    d, m, rho = 128, 8, 4
+    tiers = [4, 3, 2, 1]
+    D = signs_for(d)
+    for seed in range(6):
+        G = [1, 2, 4][seed % 3]
+        Q = skewed_keys(G, d, 100 + seed)
+        yq, lut, top = orc.query_prep(D, Q, m, rho, tiers)
+        qbar = Q.astype(np.float64).mean(axis=0)
+        R = linalg.hadamard(d) / math.sqrt(d) * D[None, :].astype(np.float64)
+        assert np.max(np.abs(yq - R @ qbar)) < 1e-5 * np.max(np.abs(yq))
+        for b in range(d // m):
+            z = yq[b * m:(b + 1) * m].astype(np.float64)
+            assert list(top[b]) == _top_brute(z, rho)
+            a = np.sort(np.abs(z))
+            if a[1] - a[0] > 1e-5 and a[2] - a[1] > 1e-5 and \
+                    abs(a[2] - a[0] - a[1]) > 1e-5:
+                assert list(top[b]) == _top_closed_form(z)
+            want = np.zeros(1 << m, np.uint8)
+            want[top[b]] = tiers
+            assert np.array_equal(lut[b], want)
+
+
+# --------------------------------------------------------------- votes ----
+
+def test_votes_brute_force_collisions(orc):
+    d, m, rho = 128, 8, 4
+    tiers = np.array([4, 3, 2, 1])
+    D = signs_for(d)
+    X = skewed_keys(2000, d, 31)
+    ids, _, _ = orc.encode_keys(D, X, m)
+    Q = skewed_keys(4, d, 32)
+    yq, lut, top = orc.query_prep(D, Q, m, rho, tiers)
+    S = 5
+    sc = orc.vote_scores(ids, lut, S, m)
+    want = np.zeros(2000 - S, np.int64)
+    for b in range(16):
+        for s in range(rho):
+            want += tiers[s] * (ids[S:, b] == top[b, s])
+    assert np.array_equal(sc, want)
+    assert sc.max() <= 64 and sc.min() >= 0
+
+
+def test_votes_special_cases(orc):
+    """k = alpha q (alpha a power of two, G = 1) collides with the query's
+    top centroid in every subspace -> 16 * 4 = 64; k = -q lands on the
+    opposite sign pattern, which is never among the top rho -> 0."""
+    d, m = 128, 8
+    D = signs_for(d)
+    q = skewed_keys(1, d, 41)
+    K = np.concatenate([q * 2.0, q * 0.25, -q, q]).astype(np.float32)
+    ids, _, _ = orc.encode_keys(D, K, m)
+    yq, lut, top = orc.query_prep(D, q, m, 4, [4, 3, 2, 1])
+    sc = orc.vote_scores(ids, lut, 0, m)
+    assert list(sc) == [64, 64, 0, 64]
+
+
+# ---------------------------------------------------------- candidates ----
+
+def test_candidates_invariants_and_brute(orc):
+    r = rng(51)
+    for E, C, S in [(1000, 50, 0), (1000, 50, 64), (777, 777, 3), (10, 0, 0),
+                    (5000, 1234, 17)]:
+        sc = r.integers(0, 12, E).astype(np.int32)   # many ties
+        cand = orc.candidates(sc, S, C)
+        assert len(cand) == C and np.all(np.diff(cand) > 0)
+        order = np.lexsort((np.arange(E), -sc))[:C]
+        assert np.array_equal(cand, np.sort(order + S))
+        sel = np.zeros(E, bool)
+        sel[cand - S] = True
+        if 0 < C < E:
+            mn = sc[sel].min()
+            assert sc[~sel].max() <= mn
+            tied_sel = np.nonzero(sel & (sc == mn))[0]
+            tied_not = np.nonzero(~sel & (sc == mn))[0]
+            if len(tied_not):
+                assert tied_sel.max() < tied_not.min()
+
+
+def test_cand_count(orc):
+    assert orc.cand_count(4096, 64, 1, 10) == 410
+    assert orc.cand_count(32768, 1024, 1, 20) == 1639
+    assert orc.cand_count(131072 - 64, 2048 - 64, 1, 20) == 6551
+    assert orc.cand_count(1048576, 4096, 1, 20) == 52429
+    assert orc.cand_count(1000, 600, 1, 20) == 600     # C >= k'
+    assert orc.cand_count(100, 10, 1, 1) == 100        # f = 1 -> all
+    assert orc.cand_count(0, 0, 1, 20) == 0
+
+
+# -------------------------------------------------------------- rerank ----
+
+def _aligned_keys(orc, D, n, seed):
+    """Keys whose rotated subspaces have all |y_j| equal (per-subspace
+    scale alpha_b, random signs): every coordinate quantises to the same
+    level, so the dequantised direction is parallel to u."""
+    d = D.shape[0]
+    r = rng(seed)
+    sgn = np.where(r.integers(0, 2, (n, d)) == 1, -1.0, 1.0)
+    alpha = np.repeat(r.uniform(0.2, 3.0, (n, d // 8)), 8, axis=1)
+    y = (sgn * alpha).astype(np.float32)
+    plus = np.ones(d, np.int8)
+    return (orc.rotate(plus, y).astype(np.float64) * D).astype(np.float32)
+
+
+def test_rerank_exact_for_aligned_keys(orc):
+    d, m = 128, 8
+    D = signs_for(d)
+    K = _aligned_keys(orc, D, 200, 61)
+    ids, nib, w = orc.encode_keys(D, K, m)
+    Q = skewed_keys(4, d, 62)
+    yq, _, _ = orc.query_prep(D, Q, m, 4, [4, 3, 2, 1])
+    cand = np.arange(200, dtype=np.int32)
+    est = orc.rerank(nib, w, yq, cand, m)
+    truth = K.astype(np.float64) @ Q.astype(np.float64).mean(axis=0)
+    scale = np.linalg.norm(K, axis=1) * np.linalg.norm(Q.mean(axis=0))
+    assert np.max(np.abs(est - truth) / scale) < 1e-3
+
+
+def test_rerank_self_inner_product(orc):
+    """q = k: w <v, y_b> = (n/<v,u>) n <v,u> = n^2, so est = ||k||^2 up to
+    the fp16 rounding of w (relative 2^-11)."""
+    d, m = 128, 8
+    D = signs_for(d)
+    K = skewed_keys(100, d, 71)
+    ids, nib, w = orc.encode_keys(D, K, m)
+    for i in range(0, 100, 7):
+        yq, _, _ = orc.query_prep(D, K[i:i + 1], m, 4, [4, 3, 2, 1])
+        est = orc.rerank(nib, w, yq, np.array([i], np.int32), m)[0]
+        n2 = float(np.sum(K[i].astype(np.float64) ** 2))
+        assert abs(est - n2) / n2 < 1e-3
+
+
+def test_rerank_linear_in_query(orc):
+    d, m = 128, 8
+    D = signs_for(d)
+    K = skewed_keys(300, d, 81)
+    _, nib, w = orc.encode_keys(D, K, m)
+    q1, q2 = skewed_keys(2, d, 82)
+    cand = np.arange(0, 300, 3, dtype=np.int32)
+    e = []
+    for q in (q1, q2, q1 + q2):
+        yq, _, _ = orc.query_prep(D, q[None].astype(np.float32), m, 4,
+                                  [4, 3, 2, 1])
+        e.append(orc.rerank(nib, w, yq, cand, m).astype(np.float64))
+    ref = np.abs(e[0]) + np.abs(e[1]) + 1e-3 * np.abs(e[2]).max()
+    assert np.max(np.abs(e[2] - e[0] - e[1]) / ref) < 1e-4
+
+
+def test_rerank_sign_of_estimate_tracks_truth(orc):
+    """Loose statistical check of the estimator on skewed keys: the
+    estimate correlates with the true inner product (the pages give no error
+    bound, so only a coarse property is asserted)."""
+    d, m = 128, 8
+    D = signs_for(d)
+    K = skewed_keys(2000, d, 91)
+    _, nib, w = orc.encode_keys(D, K, m)
+    Q = skewed_keys(4, d, 92)
+    yq, _, _ = orc.query_prep(D, Q, m, 4, [4, 3, 2, 1])
+    est = orc.rerank(nib, w, yq, np.arange(2000, dtype=np.int32), m)
+    truth = K.astype(np.float64) @ Q.astype(np.float64).mean(axis=0)
+    assert np.corrcoef(est, truth)[0, 1] > 0.99
+
+
+# ---------------------------------------------------------------- topk ----
+
+def test_topk_brute_force(orc):
+    r = rng(101)
+    for C, kp, S in [(500, 64, 0), (500, 500, 0), (1639, 1024, 0),
+                     (300, 100, 64)]:
+        cand = np.sort(r.choice(np.arange(S, 100000), C, replace=False))
+        cand = cand.astype(np.int32)
+        est = np.round(r.standard_normal(C), 2).astype(np.float32)  # ties
+        est[::17] = 0.0
+        est[5::17] = -0.0
+        out = orc.topk(cand, est, kp, S)
+        e0 = np.where(est == 0, 0.0, est)
+        order = np.lexsort((cand, -e0))[:kp]
+        want = np.sort(np.concatenate([np.arange(S), cand[order]]))
+        assert np.array_equal(out, want)
+
+
+# ----------------------------------------------------------- attention ----
+
+def test_attention_full_equals_textbook(orc):
+    r = rng(111)
+    N, d, G = 300, 128, 4
+    Q = r.standard_normal((G, d)).astype(np.float32)
+    K = r.standard_normal((N, d)).astype(np.float32)
+    V = r.standard_normal((N, d)).astype(np.float32)
+    scale = 1 / math.sqrt(d)
+    got = orc.attention(Q, K, V, np.arange(N, dtype=np.int32), scale)
+    lg = (Q.astype(np.float64) @ K.T.astype(np.float64)) * scale
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    want = p @ V.astype(np.float64)
+    assert np.max(np.abs(got - want)) < 1e-12
+    perm = r.permutation(N).astype(np.int32)
+    got2 = orc.attention(Q, K, V, perm, scale)
+    assert np.max(np.abs(got2 - want)) < 1e-12
+    sub = np.sort(r.choice(N, 40, replace=False)).astype(np.int32)
+    got3 = orc.attention(Q, K, V, sub, scale)
+    lg = lg[:, sub]
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(got3 - p @ V[sub].astype(np.float64))) < 1e-12
+
+
+def test_exact_topk_brute(orc):
+    r = rng(121)
+    N, d, G, S, kp = 2000, 128, 4, 10, 100
+    Q = r.standard_normal((G, d)).astype(np.float32)
+    K = r.standard_normal((N, d)).astype(np.float32)
+    got = orc.exact_topk(Q, K, S, kp)
+    s = K[S:].astype(np.float64) @ Q.astype(np.float64).mean(axis=0)
+    want = np.sort(np.argsort(-s, kind="stable")[:kp] + S)
+    assert np.array_equal(got, want)
+
+
+# ----------------------------------------------------------- end to end ---
+
+def test_tiny_workload_planted_keys_found(orc):
+    """Tiny workload: 8 keys planted at q + 0.1 noise must survive the
+    coarse vote and the rerank (they are the largest inner products by a
+    wide margin)."""
+    import torch
+    from kv_cache_top_srht_amd import synth
+    w = synth.WORKLOADS["tiny"]
+    lay = synth.make_layer(w, "cpu")
+    K = lay["K"][0, 0].float().numpy()
+    Q = lay["Q"][0, :w.G].float().numpy()
+    ids, nib, wq = orc.encode_keys(lay["signs"], K, w.m)
+    res = orc.retrieve_head(lay["signs"], Q, ids, nib, wq, m=w.m, rho=w.rho,
+                            tiers=w.tiers, S=w.sinks, k=w.k, num=w.cand_num,
+                            den=w.cand_den)
+    planted = synth.planted_positions(w)[0][0]
+    assert set(planted.tolist()) <= set(res["idx"].tolist())
+    assert res["C"] == 410 and len(res["idx"]) == 64
+    exact = orc.exact_topk(Q, K, 0, 64)
+    recall = len(set(exact.tolist()) & set(res["idx"].tolist())) / 64
+    assert recall > 0.5
