@@ -1,0 +1,275 @@
+/*
+ * pariskv.h -- C ABI of the MI355X (gfx950) ParisKV decode-step retrieval
+ * library: KV-cache index build and incremental append, two-stage top-k
+ * retrieval (collision votes -> candidates -> RSQ-IP rerank -> exact top-k)
+ * and split-K sparse attention over the selected full-precision rows.
+ *
+ * Method source: "Technical Summary: ParisKV" (gist.science/paper/2602.07721),
+ * cited below as [TS] with its section names, and "ParisKV: Fast and
+ * Drift-Robust KV-Cache Retrieval for Long-Context LLMs" (ICML 2026 poster
+ * abstract).  Each entry point cites the passage that defines its operation.
+ *
+ * Conventions (all entry points):
+ *   - Status codes: PARISKV_OK (0) or a negative PARISKV_ERR_*.  No C++
+ *     exception crosses this boundary.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; nothing synchronises the device except
+ *     the pariskv_debug_* calls, which are documented as synchronous.
+ *   - The library allocates NO device memory.  The caller owns every device
+ *     buffer (index, workspace, inputs, outputs); the only library-owned
+ *     object is the small host-side index handle.
+ *   - Device pointers must be device-accessible (HBM, or mapped pinned host
+ *     memory where stated).  Inputs must be finite; NaN/Inf behaviour is
+ *     undefined (no checking pass: it would cost a full read of the cache).
+ *   - Argument errors are detected on the host, synchronously, before any
+ *     launch.  Asynchronous device faults surface as PARISKV_ERR_HIP on a
+ *     later call or at the caller's stream synchronisation.
+ *   - One index handle must not be used from two streams at once; distinct
+ *     handles are independent.
+ */
+#ifndef PARISKV_H
+#define PARISKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PARISKV_API __attribute__((visibility("default")))
+
+/* status codes */
+#define PARISKV_OK               0
+#define PARISKV_ERR_INVALID_ARG (-1)   /* bad pointer, size, shape or k      */
+#define PARISKV_ERR_UNSUPPORTED (-2)   /* valid for the method, not built    */
+#define PARISKV_ERR_CAPACITY    (-3)   /* append/build beyond capacity       */
+#define PARISKV_ERR_WORKSPACE   (-4)   /* workspace or index buffer too small */
+#define PARISKV_ERR_HIP         (-5)   /* a HIP runtime call failed          */
+#define PARISKV_ERR_NOMEM       (-6)   /* host allocation of the handle failed */
+
+/* element types of K, V, Q and the attention output */
+#define PARISKV_DTYPE_BF16 0
+#define PARISKV_DTYPE_FP32 1
+
+/*
+ * Method parameters and shapes.  Validated by every call that takes it.
+ *   head_dim     d, a power of two (this build: 128).
+ *   n_subspaces  B; m = d / B coordinates per subspace (this build: m = 8).
+ *                [TS] Coarse Candidate Generation: "split into B subspaces".
+ *   rho          centroids the query keeps per subspace, 1..8.
+ *   tier_w[s]    vote weight of the query's (s+1)-th ranked centroid,
+ *                0..255, with B * max(tier_w) <= 255 ("tiered weights").
+ *   cand_num/den candidate fraction f = num/den, 0 < num <= den ("top 5-10%").
+ *                C = min(E, max(k', ceil(E f))), E = N - S, k' = k - S.
+ *   n_sink       S: keys [0, S) are always selected and are not scored.
+ *   batch, n_kv_heads, n_q_heads   n_q_heads % n_kv_heads == 0; the
+ *                G = n_q_heads / n_kv_heads query heads of a KV head share
+ *                one retrieval whose query is their mean.
+ *   key_dtype    PARISKV_DTYPE_BF16 or _FP32, the dtype of K and Q.
+ *   capacity     maximum keys per (batch, KV head) the index can hold.
+ */
+typedef struct pariskv_config {
+    int32_t head_dim;
+    int32_t n_subspaces;
+    int32_t rho;
+    int32_t tier_w[8];
+    int32_t cand_num;
+    int32_t cand_den;
+    int32_t n_sink;
+    int32_t batch;
+    int32_t n_kv_heads;
+    int32_t n_q_heads;
+    int32_t key_dtype;
+    int64_t capacity;
+} pariskv_config;
+
+typedef struct pariskv_index pariskv_index;   /* opaque host-side handle */
+
+/* Number of stages that pariskv_retrieve_topk_profiled brackets. */
+#define PARISKV_RETRIEVE_STAGES 5
+
+/* ---------------------------------------------------------------------- */
+/* Sizing.                                                                 */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of the device index buffer for `cfg` (bucket ids 16 B, RSQ-IP codes
+ * 64 B and fp16 calibration 32 B per key and (b, h), for `capacity` keys).
+ * Errors: INVALID_ARG / UNSUPPORTED for a bad config. */
+PARISKV_API int32_t pariskv_index_bytes(const pariskv_config *cfg,
+                                        size_t *bytes);
+
+/* Bytes of the device workspace pariskv_retrieve_topk needs for any index
+ * size up to cfg->capacity and this k. */
+PARISKV_API int32_t pariskv_retrieve_workspace_bytes(const pariskv_config *cfg,
+                                                     int32_t k, size_t *bytes);
+
+/* Bytes of the device workspace pariskv_sparse_attn needs. */
+PARISKV_API int32_t pariskv_attn_workspace_bytes(int32_t batch,
+                                                 int32_t n_q_heads, int32_t k,
+                                                 int32_t head_dim,
+                                                 size_t *bytes);
+
+/* ---------------------------------------------------------------------- */
+/* Index build and append.                                                 */
+/* [TS] Core Algorithmic Innovations 1 (normalisation + shared SRHT        */
+/* rotation; analytic sign-pattern centroids, data independent, so decode  */
+/* keys join the index without re-clustering) and 2 (bucket id per         */
+/* subspace; 4-bit RSQ-IP code per coordinate; calibration w_{i,b}         */
+/* computed when the key is encoded).                                      */
+/* ---------------------------------------------------------------------- */
+
+/* Creates a handle over the caller's `index_buf` (device, >= index_bytes,
+ * 256-byte aligned, must outlive the handle) and encodes keys [0, n_keys)
+ * of every (b, h), asynchronously on `stream`.
+ *   srht_signs   host array of head_dim int8 values, each +1 or -1: the
+ *                random diagonal D of the rotation c * H * diag(D).  Copied.
+ *   K            device, key_dtype, element (b, h, i, j) at
+ *                K[((b * n_kv_heads + h) * k_rows_per_head + i) * d + j].
+ *   k_rows_per_head   row stride between consecutive (b, h), >= n_keys.
+ * Errors: INVALID_ARG (null pointer, signs not +-1, stride < n_keys),
+ * UNSUPPORTED, WORKSPACE (index_bytes too small), CAPACITY (n_keys >
+ * capacity), NOMEM, HIP.  On error *out is NULL. */
+PARISKV_API int32_t pariskv_build_index(const pariskv_config *cfg,
+                                        const int8_t *srht_signs,
+                                        void *index_buf, size_t index_bytes,
+                                        const void *K, int64_t k_rows_per_head,
+                                        int64_t n_keys, void *stream,
+                                        pariskv_index **out);
+
+/* Encodes n_new keys per (b, h) and appends them at positions [N, N+n_new)
+ * where N is the current size; the host-side size is updated at once, so
+ * later calls know N without a device synchronisation.
+ *   K_new        device, element (b, h, r, j) at
+ *                K_new[((b * n_kv_heads + h) * new_rows_per_head + r) * d + j]
+ *                for r < n_new (a pointer into the KV cache at row N with
+ *                new_rows_per_head = the cache's rows per head works).
+ * Errors: INVALID_ARG, CAPACITY (N + n_new > capacity), HIP. */
+PARISKV_API int32_t pariskv_append_keys(pariskv_index *index,
+                                        const void *K_new,
+                                        int64_t new_rows_per_head,
+                                        int64_t n_new, void *stream);
+
+/* Current number of keys per (b, h), or -1 for a NULL handle. */
+PARISKV_API int64_t pariskv_index_size(const pariskv_index *index);
+
+/* Frees the host handle only (never the caller's index buffer). */
+PARISKV_API void pariskv_index_destroy(pariskv_index *index);
+
+/* ---------------------------------------------------------------------- */
+/* Retrieval.                                                              */
+/* [TS] Core Algorithmic Innovations 2, "Two-Stage GPU-Native Retrieval    */
+/* Pipeline": per subspace the query's top-rho centroids cast tiered votes */
+/* summed into an integer coarse score; the top fraction of keys is kept   */
+/* and reranked with the RSQ-IP estimator                                  */
+/* ||q|| sum_b w_{i,b} <v_{i,b}, q~_b>; the exact top-k of the estimates is */
+/* returned.  Key Contributions 2: the whole selection runs on the GPU.    */
+/* ---------------------------------------------------------------------- */
+
+/* For every (b, h): out_idx[(b * n_kv_heads + h) * k + t], t < k, receives
+ * the selected key positions in ascending order: the S sinks 0..S-1 followed
+ * by the k - S reranked winners (ties broken towards the lower position).
+ *   Q        device, key_dtype, [batch][n_q_heads][d] contiguous.
+ *   out_est  optional (NULL to skip): device float [b][h][k - S], the RSQ-IP
+ *            estimate of each non-sink selected key, aligned with
+ *            out_idx[S..k).
+ *   ws       device workspace of >= pariskv_retrieve_workspace_bytes(k),
+ *            256-byte aligned; its contents need not be initialised.
+ * No host synchronisation and no allocation: capturable in a HIP graph.
+ * Errors: INVALID_ARG (k <= S or k > N, null pointers), WORKSPACE, HIP. */
+PARISKV_API int32_t pariskv_retrieve_topk(const pariskv_index *index,
+                                          const void *Q, int32_t k,
+                                          int32_t *out_idx, float *out_est,
+                                          void *ws, size_t ws_bytes,
+                                          void *stream);
+
+/* Same as pariskv_retrieve_topk, and records events[s] before stage s and
+ * events[PARISKV_RETRIEVE_STAGES] after the last one, on `stream` (events:
+ * PARISKV_RETRIEVE_STAGES + 1 caller-created hipEvent_t).  Stages:
+ * query prep, vote scan, threshold, compact + rerank, top-k. */
+PARISKV_API int32_t pariskv_retrieve_topk_profiled(
+    const pariskv_index *index, const void *Q, int32_t k, int32_t *out_idx,
+    float *out_est, void *ws, size_t ws_bytes, void *stream, void **events);
+
+/* Name of retrieval stage s, or NULL. */
+PARISKV_API const char *pariskv_stage_name(int32_t stage);
+
+/* ---------------------------------------------------------------------- */
+/* Sparse attention.                                                       */
+/* [TS] Problem Statement (attend to a Top-k subset of past tokens) and    */
+/* System-Level Innovations 1 (only the selected Top-k K/V pairs are       */
+/* fetched).  out = softmax(scale * q K_idx^T) V_idx per query head, over   */
+/* the k rows idx of its KV head; fp32 accumulation, output in `dtype`.    */
+/* ---------------------------------------------------------------------- */
+
+/*   Q    device, dtype, [batch][n_q_heads][d].
+ *   K, V device-accessible (HBM or mapped pinned host memory), dtype,
+ *        element (b, h, i, j) at [((b * n_kv_heads + h) * kv_rows_per_head
+ *        + i) * d + j].
+ *   idx  device int32 [batch][n_kv_heads][k]; every entry in
+ *        [0, kv_rows_per_head) (not checked on the device).
+ *   out  device, dtype, [batch][n_q_heads][d].
+ *   ws   device, >= pariskv_attn_workspace_bytes.
+ * Errors: INVALID_ARG, UNSUPPORTED (head_dim != 128), WORKSPACE, HIP. */
+PARISKV_API int32_t pariskv_sparse_attn(const void *Q, const void *K,
+                                        const void *V,
+                                        int64_t kv_rows_per_head,
+                                        const int32_t *idx, int32_t k,
+                                        int32_t batch, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int32_t head_dim,
+                                        int32_t dtype, float scale, void *out,
+                                        void *ws, size_t ws_bytes,
+                                        void *stream);
+
+/* Same, recording events[0] before the split-K kernel, events[1] between
+ * it and the merge kernel and events[2] after (caller-created hipEvent_t). */
+PARISKV_API int32_t pariskv_sparse_attn_profiled(
+    const void *Q, const void *K, const void *V, int64_t kv_rows_per_head,
+    const int32_t *idx, int32_t k, int32_t batch, int32_t n_q_heads,
+    int32_t n_kv_heads, int32_t head_dim, int32_t dtype, float scale,
+    void *out, void *ws, size_t ws_bytes, void *stream, void **events);
+
+/* ---------------------------------------------------------------------- */
+/* Introspection for parity tests (synchronous; not for the hot path).     */
+/* ---------------------------------------------------------------------- */
+
+/* Copies rows [lo, hi) of every (b, h) to host arrays laid out
+ * [b][h][hi - lo][...]: ids_host B bytes, nib_host d/2 bytes (coordinate 2p
+ * in the low nibble of byte p), w_host B fp16 bit patterns per key.  Any of
+ * the three may be NULL.  Synchronises the index's last stream. */
+PARISKV_API int32_t pariskv_debug_export(const pariskv_index *index,
+                                         int64_t lo, int64_t hi,
+                                         uint8_t *ids_host, uint8_t *nib_host,
+                                         uint16_t *w_host);
+
+/* Intermediates of the last pariskv_retrieve_topk that used `ws` (same
+ * index, same k), copied to host after a device synchronisation.
+ *   which = 0: vote LUT   uint8 [b][h][B][2^m]
+ *           1: yq         float [b][h][d] (rotated group query)
+ *           2: scores     uint8 [b][h][E]  (E = N - S)
+ *           3: cand       int32 [b][h][C]  ascending key positions
+ *           4: est        float [b][h][C]  aligned with cand
+ *           5: threshold  int32 [b][h][4]  (T, #score > T, tie quota, C)
+ * Errors: INVALID_ARG (unknown which, dst_bytes too small), HIP. */
+PARISKV_API int32_t pariskv_debug_intermediate(const pariskv_index *index,
+                                               int32_t k, const void *ws,
+                                               size_t ws_bytes, int32_t which,
+                                               void *host_dst,
+                                               size_t dst_bytes);
+
+/* E and C for the index's current size and this k. */
+PARISKV_API int32_t pariskv_retrieve_sizes(const pariskv_index *index,
+                                           int32_t k, int64_t *E, int64_t *C);
+
+/* The library's fp32 RSQ-IP codebook for subspace size m (levels L[8],
+ * thresholds tau[7]) and its rotation scale fp32(1/sqrt(d)).  Host-only. */
+PARISKV_API int32_t pariskv_codebook(int32_t m, float *L, float *tau);
+PARISKV_API float pariskv_rot_scale(int32_t head_dim);
+
+/* Human-readable text for a status code (static storage). */
+PARISKV_API const char *pariskv_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PARISKV_H */

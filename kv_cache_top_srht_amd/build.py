@@ -1,0 +1,58 @@
+"""Builds libpariskv.so (HIP, gfx950) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+SO = os.path.join(PKG, "libpariskv.so")
+SOURCES = ["pariskv_kernels.hip", "pariskv_api.cpp"]
+HEADERS = ["pariskv_internal.h", "codebook_tables.h"]
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-fvisibility=hidden", "-ffp-contract=off",
+    # keep hipcc from forming packed fp32 ops on its own
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(p):
+        raise RuntimeError("hipcc not found: the HIP library cannot be built")
+    return p
+
+
+def sources():
+    return [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles (the build check must compile every time)."""
+    tmp = SO + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *sources(),
+           "-o", tmp]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd, cwd=CSRC)
+    os.replace(tmp, SO)
+    return SO
+
+
+def stale() -> bool:
+    if not os.path.exists(SO):
+        return True
+    t = os.path.getmtime(SO)
+    deps = sources() + [os.path.join(CSRC, h) for h in HEADERS] + \
+        [os.path.join(INCLUDE, "pariskv.h")]
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

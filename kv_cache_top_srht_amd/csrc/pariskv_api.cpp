@@ -1,0 +1,425 @@
+// C ABI of the ParisKV retrieval library: argument validation, buffer
+// layouts and launch sequencing.  Declarations and their contracts are in
+// include/pariskv.h; the kernels are in pariskv_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "pariskv.h"
+#include "pariskv_internal.h"
+
+struct pariskv_index {
+  pariskv_config cfg;
+  pkv::SignMask signs;
+  float rot_c;
+  uint8_t* ids;    // [BH][cap][16]  bucket id per subspace
+  uint32_t* nib;   // [BH][cap][16]  8 RSQ-IP nibbles per subspace
+  uint16_t* w;     // [BH][cap][16]  fp16 calibration per subspace
+  int64_t n;       // keys per (b, h)
+  hipStream_t last;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t cand_count(int64_t E, int64_t kprime, int64_t num, int64_t den) {
+  int64_t c = (E * num + den - 1) / den;
+  if (c < kprime) c = kprime;
+  if (c > E) c = E;
+  return c;
+}
+
+int max_tier(const pariskv_config* c) {
+  int mx = 0;
+  for (int s = 0; s < c->rho; ++s) mx = c->tier_w[s] > mx ? c->tier_w[s] : mx;
+  return mx;
+}
+
+int32_t check_cfg(const pariskv_config* c) {
+  if (!c) return PARISKV_ERR_INVALID_ARG;
+  const int d = c->head_dim;
+  if (d < 2 || d > 1024 || (d & (d - 1))) return PARISKV_ERR_INVALID_ARG;
+  if (c->n_subspaces < 1 || d % c->n_subspaces) return PARISKV_ERR_INVALID_ARG;
+  const int m = d / c->n_subspaces;
+  if (m < 2 || m > 8) return PARISKV_ERR_INVALID_ARG;
+  if (c->rho < 1 || c->rho > 8 || c->rho > (1 << m)) return PARISKV_ERR_INVALID_ARG;
+  for (int s = 0; s < c->rho; ++s)
+    if (c->tier_w[s] < 0 || c->tier_w[s] > 255) return PARISKV_ERR_INVALID_ARG;
+  if ((int64_t)c->n_subspaces * max_tier(c) > 255) return PARISKV_ERR_INVALID_ARG;
+  if (c->cand_num < 1 || c->cand_den < c->cand_num) return PARISKV_ERR_INVALID_ARG;
+  if (c->n_sink < 0 || c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1)
+    return PARISKV_ERR_INVALID_ARG;
+  if (c->n_q_heads % c->n_kv_heads) return PARISKV_ERR_INVALID_ARG;
+  if (c->key_dtype != PARISKV_DTYPE_BF16 && c->key_dtype != PARISKV_DTYPE_FP32)
+    return PARISKV_ERR_INVALID_ARG;
+  if (c->capacity < 1 || c->capacity > 0x7FFFFFFFll || c->n_sink >= c->capacity)
+    return PARISKV_ERR_INVALID_ARG;
+  if ((int64_t)c->batch * c->n_kv_heads > 65535) return PARISKV_ERR_UNSUPPORTED;
+  // kernels of this build: d = 128 split into 16 subspaces of 8
+  if (d != 128 || m != 8) return PARISKV_ERR_UNSUPPORTED;
+  return PARISKV_OK;
+}
+
+struct IndexLayout {
+  size_t ids, nib, w, total;
+};
+
+IndexLayout index_layout(const pariskv_config* c) {
+  const size_t keys = (size_t)c->batch * c->n_kv_heads * (size_t)c->capacity;
+  IndexLayout L;
+  L.ids = 0;
+  L.nib = align_up(keys * 16, kAlign);
+  L.w = L.nib + align_up(keys * 64, kAlign);
+  L.total = L.w + align_up(keys * 32, kAlign);
+  return L;
+}
+
+struct WsLayout {
+  size_t lut, yq, scores, chist, coff, meta, cand, est, total;
+  int64_t Epad, nchunks_max, cstride;
+  int nbins;
+};
+
+WsLayout ws_layout(const pariskv_config* c, int64_t k) {
+  const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
+  const int64_t Emax = c->capacity - c->n_sink;
+  int64_t kp = k - c->n_sink;
+  if (kp > Emax) kp = Emax;
+  const int64_t Cmax = cand_count(Emax, kp, c->cand_num, c->cand_den);
+  WsLayout L;
+  L.nbins = c->n_subspaces * max_tier(c) + 1;
+  L.nchunks_max = ceil_div(Emax, 256);
+  L.Epad = (int64_t)align_up((size_t)Emax, 4096);
+  L.cstride = Cmax > 0 ? Cmax : 1;
+  size_t off = 0;
+  L.lut = off;    off += align_up((size_t)BH * 16 * 256, kAlign);
+  L.yq = off;     off += align_up((size_t)BH * 128 * 4, kAlign);
+  L.scores = off; off += align_up((size_t)BH * L.Epad, kAlign);
+  L.chist = off;  off += align_up((size_t)BH * L.nchunks_max * L.nbins * 4, kAlign);
+  L.coff = off;   off += align_up((size_t)BH * L.nchunks_max * 8, kAlign);
+  L.meta = off;   off += align_up((size_t)BH * 16, kAlign);
+  L.cand = off;   off += align_up((size_t)BH * L.cstride * 4, kAlign);
+  L.est = off;    off += align_up((size_t)BH * L.cstride * 4, kAlign);
+  L.total = off;
+  return L;
+}
+
+// Keys per thread of the scan/compaction chunks: the largest power of two
+// <= 16 that still gives >= 2048 blocks (8 per CU on 256 CUs).
+int pick_kpt(int64_t E, int64_t BH) {
+  int kpt = 16;
+  while (kpt > 1 && ceil_div(E, 256 * kpt) * BH < 2048) kpt >>= 1;
+  return kpt;
+}
+
+float rot_scale(int d) { return (float)(1.0L / std::sqrt((long double)d)); }
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? PARISKV_OK : PARISKV_ERR_HIP; }
+
+int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t* out_idx,
+                      float* out_est, void* ws, size_t ws_bytes, void* stream, void** events) {
+  if (!ix || !Q || !out_idx || !ws) return PARISKV_ERR_INVALID_ARG;
+  const pariskv_config* c = &ix->cfg;
+  const int64_t N = ix->n, S = c->n_sink;
+  if (k <= S || (int64_t)k > N) return PARISKV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return PARISKV_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(c, k);
+  if (ws_bytes < L.total) return PARISKV_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const_cast<pariskv_index*>(ix)->last = st;
+  const int BH = c->batch * c->n_kv_heads;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  const int64_t E = N - S, kp = k - S;
+  const int64_t C = cand_count(E, kp, c->cand_num, c->cand_den);
+  const int kpt = pick_kpt(E, BH);
+  const int nch = (int)ceil_div(E, 256 * kpt);
+  uint8_t* base = (uint8_t*)ws;
+  uint8_t* lut = base + L.lut;
+  float* yq = (float*)(base + L.yq);
+  uint8_t* scores = base + L.scores;
+  uint32_t* chist = (uint32_t*)(base + L.chist);
+  uint32_t* coff = (uint32_t*)(base + L.coff);
+  int32_t* meta = (int32_t*)(base + L.meta);
+  int32_t* cand = (int32_t*)(base + L.cand);
+  float* est = (float*)(base + L.est);
+  pkv::Tiers tw;
+  for (int s = 0; s < 8; ++s) tw.w[s] = c->tier_w[s];
+
+  auto mark = [&](int s) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[s], st) : hipSuccess;
+  };
+  hipError_t e;
+  if ((e = mark(0)) != hipSuccess) return hip_status(e);
+  e = pkv::launch_qprep(c->key_dtype, Q, BH, c->n_kv_heads, G, ix->signs, ix->rot_c, c->rho, tw,
+                        lut, yq, st);
+  if (e != hipSuccess || (e = mark(1)) != hipSuccess) return hip_status(e);
+  e = pkv::launch_scan(kpt, nch, BH, ix->ids, c->capacity, S, E, lut, scores, L.Epad, chist,
+                       (int)L.nchunks_max, L.nbins, st);
+  if (e != hipSuccess || (e = mark(2)) != hipSuccess) return hip_status(e);
+  e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, C, meta, coff, st);
+  if (e != hipSuccess || (e = mark(3)) != hipSuccess) return hip_status(e);
+  e = pkv::launch_compact_rerank(kpt, nch, BH, scores, L.Epad, S, E, meta, coff,
+                                 (int)L.nchunks_max, yq, ix->nib, ix->w, c->capacity, cand, est,
+                                 L.cstride, C, st);
+  if (e != hipSuccess || (e = mark(4)) != hipSuccess) return hip_status(e);
+  e = pkv::launch_topk(BH, est, cand, L.cstride, (int)C, (int)kp, (int)S, k, out_idx, out_est,
+                       st);
+  if (e != hipSuccess || (e = mark(5)) != hipSuccess) return hip_status(e);
+  return PARISKV_OK;
+}
+
+int32_t attn_impl(const void* Q, const void* K, const void* V, int64_t rows_per_head,
+                  const int32_t* idx, int32_t k, int32_t batch, int32_t n_q_heads,
+                  int32_t n_kv_heads, int32_t head_dim, int32_t dtype, float scale, void* out,
+                  void* ws, size_t ws_bytes, void* stream, void** events) {
+  if (!Q || !K || !V || !idx || !out || !ws) return PARISKV_ERR_INVALID_ARG;
+  if (k < 1 || batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || rows_per_head < 1)
+    return PARISKV_ERR_INVALID_ARG;
+  if (n_q_heads % n_kv_heads) return PARISKV_ERR_INVALID_ARG;
+  if (dtype != PARISKV_DTYPE_BF16 && dtype != PARISKV_DTYPE_FP32) return PARISKV_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PARISKV_ERR_INVALID_ARG;
+  const int G = n_q_heads / n_kv_heads;
+  if (head_dim != 128 || (G != 1 && G != 2 && G != 4 && G != 8)) return PARISKV_ERR_UNSUPPORTED;
+  if ((int64_t)batch * n_kv_heads > 65535) return PARISKV_ERR_UNSUPPORTED;
+  size_t need = 0;
+  pariskv_attn_workspace_bytes(batch, n_q_heads, k, head_dim, &need);
+  if (ws_bytes < need) return PARISKV_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int nch = (int)ceil_div(k, 64);
+  const float qscale = scale * 1.4426950408889634f;
+  hipError_t e = events ? hipEventRecord((hipEvent_t)events[0], st) : hipSuccess;
+  if (e != hipSuccess) return hip_status(e);
+  e = pkv::launch_attn_split(dtype, G, Q, K, V, rows_per_head, idx, k, batch, n_kv_heads, qscale,
+                             (float*)ws, nch, st);
+  if (e != hipSuccess) return hip_status(e);
+  if (events && (e = hipEventRecord((hipEvent_t)events[1], st)) != hipSuccess)
+    return hip_status(e);
+  e = pkv::launch_attn_merge(dtype, (const float*)ws, nch, batch * n_q_heads, out, st);
+  if (e != hipSuccess) return hip_status(e);
+  if (events && (e = hipEventRecord((hipEvent_t)events[2], st)) != hipSuccess)
+    return hip_status(e);
+  return PARISKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pariskv_index_bytes(const pariskv_config* cfg, size_t* bytes) {
+  const int32_t rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!bytes) return PARISKV_ERR_INVALID_ARG;
+  *bytes = index_layout(cfg).total;
+  return PARISKV_OK;
+}
+
+int32_t pariskv_retrieve_workspace_bytes(const pariskv_config* cfg, int32_t k, size_t* bytes) {
+  const int32_t rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!bytes || k <= cfg->n_sink || (int64_t)k > cfg->capacity) return PARISKV_ERR_INVALID_ARG;
+  *bytes = ws_layout(cfg, k).total;
+  return PARISKV_OK;
+}
+
+int32_t pariskv_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t k,
+                                     int32_t head_dim, size_t* bytes) {
+  if (!bytes || batch < 1 || n_q_heads < 1 || k < 1 || head_dim < 1)
+    return PARISKV_ERR_INVALID_ARG;
+  *bytes = align_up((size_t)batch * n_q_heads * (size_t)ceil_div(k, 64) * (head_dim + 2) * 4,
+                    kAlign);
+  return PARISKV_OK;
+}
+
+int32_t pariskv_build_index(const pariskv_config* cfg, const int8_t* srht_signs, void* index_buf,
+                            size_t index_bytes, const void* K, int64_t k_rows_per_head,
+                            int64_t n_keys, void* stream, pariskv_index** out) {
+  if (out) *out = nullptr;
+  const int32_t rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!srht_signs || !index_buf || !out || (n_keys > 0 && !K) || n_keys < 0)
+    return PARISKV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(index_buf) & (kAlign - 1)) != 0) return PARISKV_ERR_INVALID_ARG;
+  if (n_keys > 0 && k_rows_per_head < n_keys) return PARISKV_ERR_INVALID_ARG;
+  if (n_keys > cfg->capacity) return PARISKV_ERR_CAPACITY;
+  const IndexLayout L = index_layout(cfg);
+  if (index_bytes < L.total) return PARISKV_ERR_WORKSPACE;
+  pkv::SignMask sg{};
+  for (int j = 0; j < cfg->head_dim; ++j) {
+    if (srht_signs[j] == -1) sg.w[j >> 5] |= 1u << (j & 31);
+    else if (srht_signs[j] != 1) return PARISKV_ERR_INVALID_ARG;
+  }
+  pariskv_index* ix = new (std::nothrow) pariskv_index;
+  if (!ix) return PARISKV_ERR_NOMEM;
+  ix->cfg = *cfg;
+  ix->signs = sg;
+  ix->rot_c = rot_scale(cfg->head_dim);
+  uint8_t* base = (uint8_t*)index_buf;
+  ix->ids = base + L.ids;
+  ix->nib = (uint32_t*)(base + L.nib);
+  ix->w = (uint16_t*)(base + L.w);
+  ix->n = 0;
+  ix->last = (hipStream_t)stream;
+  const int BH = cfg->batch * cfg->n_kv_heads;
+  hipError_t e = pkv::launch_encode(cfg->key_dtype, K, k_rows_per_head, 0, n_keys, BH,
+                                    cfg->capacity, ix->ids, ix->nib, ix->w, ix->signs, ix->rot_c,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) {
+    delete ix;
+    return PARISKV_ERR_HIP;
+  }
+  ix->n = n_keys;
+  *out = ix;
+  return PARISKV_OK;
+}
+
+int32_t pariskv_append_keys(pariskv_index* ix, const void* K_new, int64_t new_rows_per_head,
+                            int64_t n_new, void* stream) {
+  if (!ix || n_new < 0 || (n_new > 0 && (!K_new || new_rows_per_head < n_new)))
+    return PARISKV_ERR_INVALID_ARG;
+  if (ix->n + n_new > ix->cfg.capacity) return PARISKV_ERR_CAPACITY;
+  if (n_new == 0) return PARISKV_OK;
+  const int BH = ix->cfg.batch * ix->cfg.n_kv_heads;
+  ix->last = (hipStream_t)stream;
+  hipError_t e = pkv::launch_encode(ix->cfg.key_dtype, K_new, new_rows_per_head, ix->n, n_new, BH,
+                                    ix->cfg.capacity, ix->ids, ix->nib, ix->w, ix->signs,
+                                    ix->rot_c, (hipStream_t)stream);
+  if (e != hipSuccess) return PARISKV_ERR_HIP;
+  ix->n += n_new;
+  return PARISKV_OK;
+}
+
+int64_t pariskv_index_size(const pariskv_index* ix) { return ix ? ix->n : -1; }
+
+void pariskv_index_destroy(pariskv_index* ix) { delete ix; }
+
+int32_t pariskv_retrieve_topk(const pariskv_index* ix, const void* Q, int32_t k, int32_t* out_idx,
+                              float* out_est, void* ws, size_t ws_bytes, void* stream) {
+  return retrieve_impl(ix, Q, k, out_idx, out_est, ws, ws_bytes, stream, nullptr);
+}
+
+int32_t pariskv_retrieve_topk_profiled(const pariskv_index* ix, const void* Q, int32_t k,
+                                       int32_t* out_idx, float* out_est, void* ws,
+                                       size_t ws_bytes, void* stream, void** events) {
+  if (!events) return PARISKV_ERR_INVALID_ARG;
+  for (int s = 0; s <= PARISKV_RETRIEVE_STAGES; ++s)
+    if (!events[s]) return PARISKV_ERR_INVALID_ARG;
+  return retrieve_impl(ix, Q, k, out_idx, out_est, ws, ws_bytes, stream, events);
+}
+
+const char* pariskv_stage_name(int32_t s) {
+  static const char* names[PARISKV_RETRIEVE_STAGES] = {"query_prep", "vote_scan", "threshold",
+                                                       "compact_rerank", "topk"};
+  return (s >= 0 && s < PARISKV_RETRIEVE_STAGES) ? names[s] : nullptr;
+}
+
+int32_t pariskv_sparse_attn(const void* Q, const void* K, const void* V, int64_t kv_rows_per_head,
+                            const int32_t* idx, int32_t k, int32_t batch, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t head_dim, int32_t dtype, float scale,
+                            void* out, void* ws, size_t ws_bytes, void* stream) {
+  return attn_impl(Q, K, V, kv_rows_per_head, idx, k, batch, n_q_heads, n_kv_heads, head_dim,
+                   dtype, scale, out, ws, ws_bytes, stream, nullptr);
+}
+
+int32_t pariskv_sparse_attn_profiled(const void* Q, const void* K, const void* V,
+                                     int64_t kv_rows_per_head, const int32_t* idx, int32_t k,
+                                     int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                     int32_t head_dim, int32_t dtype, float scale, void* out,
+                                     void* ws, size_t ws_bytes, void* stream, void** events) {
+  if (!events || !events[0] || !events[1] || !events[2]) return PARISKV_ERR_INVALID_ARG;
+  return attn_impl(Q, K, V, kv_rows_per_head, idx, k, batch, n_q_heads, n_kv_heads, head_dim,
+                   dtype, scale, out, ws, ws_bytes, stream, events);
+}
+
+int32_t pariskv_debug_export(const pariskv_index* ix, int64_t lo, int64_t hi, uint8_t* ids_host,
+                             uint8_t* nib_host, uint16_t* w_host) {
+  if (!ix || lo < 0 || hi < lo || hi > ix->cfg.capacity) return PARISKV_ERR_INVALID_ARG;
+  if (hipDeviceSynchronize() != hipSuccess) return PARISKV_ERR_HIP;
+  const int64_t BH = (int64_t)ix->cfg.batch * ix->cfg.n_kv_heads;
+  const int64_t cap = ix->cfg.capacity, n = hi - lo;
+  if (n == 0) return PARISKV_OK;
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    const int64_t key = bh * cap + lo;
+    if (ids_host && hipMemcpy(ids_host + bh * n * 16, ix->ids + key * 16, n * 16,
+                              hipMemcpyDeviceToHost) != hipSuccess)
+      return PARISKV_ERR_HIP;
+    if (nib_host && hipMemcpy(nib_host + bh * n * 64, (const uint8_t*)ix->nib + key * 64, n * 64,
+                              hipMemcpyDeviceToHost) != hipSuccess)
+      return PARISKV_ERR_HIP;
+    if (w_host && hipMemcpy(w_host + bh * n * 16, ix->w + key * 16, n * 32,
+                            hipMemcpyDeviceToHost) != hipSuccess)
+      return PARISKV_ERR_HIP;
+  }
+  return PARISKV_OK;
+}
+
+int32_t pariskv_retrieve_sizes(const pariskv_index* ix, int32_t k, int64_t* E, int64_t* C) {
+  if (!ix || !E || !C) return PARISKV_ERR_INVALID_ARG;
+  const int64_t S = ix->cfg.n_sink;
+  if (k <= S || (int64_t)k > ix->n) return PARISKV_ERR_INVALID_ARG;
+  *E = ix->n - S;
+  *C = cand_count(*E, k - S, ix->cfg.cand_num, ix->cfg.cand_den);
+  return PARISKV_OK;
+}
+
+int32_t pariskv_debug_intermediate(const pariskv_index* ix, int32_t k, const void* ws,
+                                   size_t ws_bytes, int32_t which, void* host_dst,
+                                   size_t dst_bytes) {
+  int64_t E = 0, C = 0;
+  int32_t rc = pariskv_retrieve_sizes(ix, k, &E, &C);
+  if (rc) return rc;
+  if (!ws || !host_dst) return PARISKV_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(&ix->cfg, k);
+  if (ws_bytes < L.total) return PARISKV_ERR_WORKSPACE;
+  const int64_t BH = (int64_t)ix->cfg.batch * ix->cfg.n_kv_heads;
+  const uint8_t* base = (const uint8_t*)ws;
+  if (hipDeviceSynchronize() != hipSuccess) return PARISKV_ERR_HIP;
+  auto rows = [&](size_t off, int64_t stride, int64_t len, int64_t elem) -> int32_t {
+    if (dst_bytes < (size_t)(BH * len * elem)) return PARISKV_ERR_INVALID_ARG;
+    for (int64_t bh = 0; bh < BH; ++bh)
+      if (hipMemcpy((uint8_t*)host_dst + bh * len * elem, base + off + bh * stride * elem,
+                    len * elem, hipMemcpyDeviceToHost) != hipSuccess)
+        return PARISKV_ERR_HIP;
+    return PARISKV_OK;
+  };
+  switch (which) {
+    case 0: return rows(L.lut, 16 * 256, 16 * 256, 1);
+    case 1: return rows(L.yq, 128, 128, 4);
+    case 2: return rows(L.scores, L.Epad, E, 1);
+    case 3: return rows(L.cand, L.cstride, C, 4);
+    case 4: return rows(L.est, L.cstride, C, 4);
+    case 5: return rows(L.meta, 4, 4, 4);
+    default: return PARISKV_ERR_INVALID_ARG;
+  }
+}
+
+int32_t pariskv_codebook(int32_t m, float* L, float* tau) {
+  if (!L || !tau) return PARISKV_ERR_INVALID_ARG;
+  if (m == 8) pkv::codebook_m8(L, tau);
+  else if (m == 4) pkv::codebook_m4(L, tau);
+  else return PARISKV_ERR_UNSUPPORTED;
+  return PARISKV_OK;
+}
+
+float pariskv_rot_scale(int32_t head_dim) { return head_dim > 0 ? rot_scale(head_dim) : 0.0f; }
+
+const char* pariskv_status_string(int32_t s) {
+  switch (s) {
+    case PARISKV_OK: return "ok";
+    case PARISKV_ERR_INVALID_ARG: return "invalid argument";
+    case PARISKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PARISKV_ERR_CAPACITY: return "index capacity exceeded";
+    case PARISKV_ERR_WORKSPACE: return "workspace or index buffer too small";
+    case PARISKV_ERR_HIP: return "HIP runtime error";
+    case PARISKV_ERR_NOMEM: return "host allocation failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

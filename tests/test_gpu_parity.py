@@ -1,0 +1,193 @@
+"""GPU parity: the HIP path, called through the C-ABI binding, against the
+CPU oracle on the same seeded inputs.
+
+Bar: bit-exact bucket ids, RSQ-IP codes, fp16 calibration bits, vote LUT,
+rotated query, vote scores, candidate lists, estimates and top-k lists;
+attention within 2e-2 absolute (bf16 outputs) / 1e-4 (fp32 outputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (ATTN_TOL_BF16, ATTN_TOL_FP32, assert_retrieval_equal,
+                         case, gpu_intermediates, gpu_layer, host_f32, need_gpu,
+                         oracle_encode_heads, oracle_retrieve_heads, pk, synth)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.Workload
+
+
+SMALL = {
+    "tiny": synth.WORKLOADS["tiny"],
+    "gqa_ragged": W("gqa ragged", 2, 2, 8, 128, 5003, "bf16", k=128, seed=11),
+    "sinks": W("sinks", 1, 3, 6, 128, 7001, "bf16", cand_num=1, cand_den=10,
+               k=200, sinks=64, seed=12),
+    "all_selected": W("all selected", 1, 2, 2, 128, 300, "bf16", cand_num=1,
+                      cand_den=1, k=300, seed=13),
+    "c_equals_kprime": W("C == k'", 1, 1, 4, 128, 2000, "fp32", k=500, seed=14),
+    "short": W("N < 256", 2, 1, 8, 128, 100, "bf16", cand_num=1, cand_den=10,
+               k=10, seed=15),
+    "one_head_many_chunks": W("1 head, 70K keys", 1, 1, 4, 128, 70001, "bf16",
+                              k=700, seed=16),
+    "batched_kpt2": W("64 heads, 20K keys", 8, 8, 32, 128, 20000, "bf16",
+                      k=256, sinks=16, seed=17),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def run_case(orc, w, capacity=None, extra_rows=0):
+    case("%s: batch=%d Hkv=%d Hq=%d N=%d k=%d S=%d %s" % (
+        w.name, w.batch, w.n_kv_heads, w.n_q_heads, w.N, w.k, w.sinks, w.dtype))
+    lay, cfg, L = gpu_layer(w, capacity=capacity)
+    BH = w.batch * w.n_kv_heads
+    idx = torch.empty(BH, w.k, dtype=torch.int32, device="cuda")
+    est = torch.empty(BH, w.kprime, dtype=torch.float32, device="cuda")
+    L.retrieve(lay["Q"], idx, est)
+    torch.cuda.synchronize()
+    return lay, cfg, L, idx, est
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_retrieve_parity_small(orc, name):
+    w = SMALL[name]
+    lay, cfg, L, idx, est = run_case(orc, w)
+    BH = w.batch * w.n_kv_heads
+    ids, nib, wq = pk.pariskv_debug_export(L.handle, 0, w.N, BH)
+    Kh = host_f32(lay["K"])
+    Qh = host_f32(lay["Q"])
+    heads = list(range(BH))
+    enc = oracle_encode_heads(orc, w, Kh, lay["signs"], heads)
+    for bh in heads:
+        o_ids, o_nib, o_w = enc[bh]
+        assert np.array_equal(ids[bh], o_ids), bh
+        assert np.array_equal(nib[bh], o_nib), bh
+        assert np.array_equal(wq[bh], o_w), bh
+    ref = oracle_retrieve_heads(orc, w, Qh, enc, lay["signs"], heads)
+    gi = gpu_intermediates(L, BH)
+    ih, eh = idx.cpu().numpy(), est.cpu().numpy()
+    for bh in heads:
+        assert_retrieval_equal(w, gi, ih, eh, ref[bh], bh)
+    # attention over the selected rows
+    out = torch.empty_like(lay["Q"])
+    L.attend(lay["Q"], lay["K"], lay["V"], idx, out)
+    torch.cuda.synchronize()
+    Vh = host_f32(lay["V"])
+    oh = host_f32(out)
+    tol = ATTN_TOL_BF16 if w.dtype == "bf16" else ATTN_TOL_FP32
+    for bh in heads:
+        b, h = divmod(bh, w.n_kv_heads)
+        G = w.G
+        ref_o = orc.attention(Qh[b, h * G:(h + 1) * G], Kh[b, h], Vh[b, h],
+                              ih[bh], w.d ** -0.5)
+        assert np.max(np.abs(oh[b, h * G:(h + 1) * G] - ref_o)) <= tol, bh
+    L.close()
+
+
+@pytest.mark.parametrize("dtype,n0,steps", [("bf16", 1000, [1, 7, 100, 1]),
+                                            ("fp32", 33, [16, 1, 250])])
+def test_append_equals_build(orc, dtype, n0, steps):
+    """Appending keys in pieces encodes exactly what a one-shot build does,
+    and both equal the oracle (decode keys need no re-clustering)."""
+    total = n0 + sum(steps)
+    w = W("append", 2, 2, 8, 128, total, dtype, k=64, seed=21)
+    case("append %s n0=%d steps=%s" % (dtype, n0, steps))
+    lay = synth.make_layer(w, "cuda", capacity=total + 5)
+    cfg = pk.config_for(w, capacity=total + 5)
+    full = pk.Layer(cfg, lay["signs"], lay["K"], total, k=64)
+    inc = pk.Layer(cfg, lay["signs"], lay["K"], n0, k=64)
+    pos = n0
+    for s in steps:
+        inc.append(lay["K"][:, :, pos:], s, rows_per_head=lay["K"].shape[2])
+        pos += s
+    assert inc.size == total
+    torch.cuda.synchronize()
+    BH = w.batch * w.n_kv_heads
+    a = pk.pariskv_debug_export(full.handle, 0, total, BH)
+    b = pk.pariskv_debug_export(inc.handle, 0, total, BH)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    enc = oracle_encode_heads(orc, w, host_f32(lay["K"]), lay["signs"],
+                              list(range(BH)), n=total)
+    for bh in range(BH):
+        for x, y in zip(a, enc[bh]):
+            assert np.array_equal(x[bh], y)
+
+
+def test_ties_duplicates_and_zero_keys(orc):
+    """Duplicated keys tie on both the vote score and the estimate; all-zero
+    keys have w = 0 and estimate 0 (and -0 vs +0 must not matter)."""
+    w = W("ties", 1, 2, 4, 128, 3000, "bf16", cand_num=1, cand_den=5, k=300,
+          seed=31)
+    case("ties/duplicates/zero keys")
+    lay = synth.make_layer(w, "cuda")
+    K = lay["K"]
+    K[:, :, 1000:1600] = K[:, :, 100:700]        # duplicates
+    K[:, :, 2000:2100] = 0                        # zero keys
+    K[:, :, 2100:2200] = -K[:, :, 2200:2300]      # opposite keys
+    cfg = pk.config_for(w)
+    L = pk.Layer(cfg, lay["signs"], K, w.N, k=w.k)
+    BH = 2
+    idx = torch.empty(BH, w.k, dtype=torch.int32, device="cuda")
+    est = torch.empty(BH, w.kprime, dtype=torch.float32, device="cuda")
+    L.retrieve(lay["Q"], idx, est)
+    torch.cuda.synchronize()
+    Kh, Qh = host_f32(K), host_f32(lay["Q"])
+    enc = oracle_encode_heads(orc, w, Kh, lay["signs"], [0, 1])
+    ref = oracle_retrieve_heads(orc, w, Qh, enc, lay["signs"], [0, 1])
+    gi = gpu_intermediates(L, BH)
+    for bh in range(BH):
+        assert_retrieval_equal(w, gi, idx.cpu().numpy(), est.cpu().numpy(),
+                               ref[bh], bh)
+    L.close()
+
+
+def test_deterministic_repeat():
+    w = SMALL["batched_kpt2"]
+    case("determinism")
+    lay, cfg, L = gpu_layer(w)
+    BH = w.batch * w.n_kv_heads
+    outs = []
+    for _ in range(3):
+        idx = torch.empty(BH, w.k, dtype=torch.int32, device="cuda")
+        est = torch.empty(BH, w.kprime, dtype=torch.float32, device="cuda")
+        L.retrieve(lay["Q"], idx, est)
+        outs.append((idx.cpu().numpy(), est.cpu().numpy().view(np.uint32)))
+    for o in outs[1:]:
+        assert np.array_equal(o[0], outs[0][0])
+        assert np.array_equal(o[1], outs[0][1])
+    L.close()
+
+
+@pytest.mark.parametrize("G,dtype,k,N", [(1, "fp32", 77, 500), (2, "bf16", 64, 64),
+                                         (4, "bf16", 1000, 3000),
+                                         (8, "bf16", 129, 4096),
+                                         (4, "bf16", 4096, 4096)])
+def test_attention_dense_and_sparse(orc, G, dtype, k, N):
+    """Split-K attention vs fp64 softmax attention; k = N is full attention."""
+    case("attention G=%d %s k=%d N=%d" % (G, dtype, k, N))
+    Hkv, B = 2, 2
+    w = W("attn", B, Hkv, Hkv * G, 128, N, dtype, k=k, seed=41)
+    lay = synth.make_layer(w, "cuda")
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    idx = torch.stack([torch.sort(torch.randperm(N, generator=gen)[:k]).values
+                       for _ in range(B * Hkv)]).to(torch.int32).cuda()
+    ws = torch.empty(pk.pariskv_attn_workspace_bytes(B, Hkv * G, k, 128),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(lay["Q"])
+    pk.pariskv_sparse_attn(lay["Q"], lay["K"], lay["V"], N, idx, k, B, Hkv * G,
+                           Hkv, 128, pk.PARISKV_DTYPE_BF16 if dtype == "bf16"
+                           else pk.PARISKV_DTYPE_FP32, 128 ** -0.5, out, ws)
+    torch.cuda.synchronize()
+    Qh, Kh, Vh = host_f32(lay["Q"]), host_f32(lay["K"]), host_f32(lay["V"])
+    ih, oh = idx.cpu().numpy(), host_f32(out)
+    tol = ATTN_TOL_BF16 if dtype == "bf16" else ATTN_TOL_FP32
+    for bh in range(B * Hkv):
+        b, h = divmod(bh, Hkv)
+        ref = orc.attention(Qh[b, h * G:(h + 1) * G], Kh[b, h], Vh[b, h], ih[bh],
+                            128 ** -0.5)
+        assert np.max(np.abs(oh[b, h * G:(h + 1) * G] - ref)) <= tol
