@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the ParisKV retrieval path on one MI355X.
+
+One step = for every (batch, KV head) of one layer: append the new decode key
+to the index, retrieve the top-k (query prep, vote scan, threshold, compact +
+RSQ-IP rerank, exact top-k) and run split-K sparse attention over the
+selected rows.  Inputs are synthetic and resident in HBM; `--layers`
+independent layer instances are used in rotation so the 256 MB Infinity
+Cache cannot hold one layer's bucket ids across consecutive steps.
+
+The K timed steps are captured into one HIP graph and replayed once between
+two device synchronisations (so launch overhead of the ctypes binding does
+not pace the GPU).  Per-kernel durations come from the steps that follow,
+launched with start/stop HIP events that each kernel's own dispatch stamps.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("decode retrieval+sparse-attn µs/step/layer and keys scanned/s "
+          "at 128K-1M ctx")
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "kv_cache_top_srht_amd", "csrc",
+                          "pariskv_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="million")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--profile-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the timed steps eagerly instead of as a graph")
+    return ap.parse_args()
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(name: str, launches_bytes: float):
+    """HBM traffic per launch from a committed rocprofv3 --pmc summary, or
+    None when it is missing or was taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_sha256_16") != kernel_sha():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the work shards by (batch, KV head) with no exchange; see the "
+              "design notes).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_top_srht_amd as pk
+    from kv_cache_top_srht_amd import synth
+
+    pk.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    w = synth.WORKLOADS[args.workload]
+    K_steps, W_steps, Lr = args.steps, args.warmup, max(1, args.layers)
+    per_layer = math.ceil((K_steps + W_steps + args.profile_steps) / Lr) + 1
+    cap = w.N + per_layer
+    BH = w.batch * w.n_kv_heads
+    print("[bench] workload=%s layers=%d cap=%d steps=%d warmup=%d" %
+          (args.workload, Lr, cap, K_steps, W_steps), file=sys.stderr, flush=True)
+
+    layers = []
+    for l in range(Lr):
+        lay = synth.make_layer(w.scaled(N=cap), dev, layer=l)
+        cfg = pk.config_for(w, capacity=cap)
+        L = pk.Layer(cfg, lay["signs"], lay["K"], w.N, k=w.k, device=dev)
+        layers.append((L, lay))
+        torch.cuda.synchronize()
+    idx = torch.empty(BH, w.k, dtype=torch.int32, device=dev)
+    out = torch.empty_like(layers[0][1]["Q"])
+    scale = w.d ** -0.5
+    dt_code = pk.PARISKV_DTYPE_BF16 if w.dtype == "bf16" else pk.PARISKV_DTYPE_FP32
+    E_of = []
+
+    def step(t, ev=None):
+        L, lay = layers[t % Lr]
+        n = L.size
+        L.append(lay["K"][:, :, n:], 1, rows_per_head=cap)
+        E_of.append(L.size - w.sinks)
+        if ev is None:
+            L.retrieve(lay["Q"], idx)
+            L.attend(lay["Q"], lay["K"], lay["V"], idx, out, scale)
+        else:
+            # ev[0:10]: start/stop of the 5 retrieval kernels, ev[10:14]: of
+            # the 2 attention kernels, stamped by the dispatches themselves
+            pk.pariskv_retrieve_topk_profiled(L.handle, lay["Q"], w.k, idx, None,
+                                              L.ws, ev[0:10])
+            pk.pariskv_sparse_attn_profiled(lay["Q"], lay["K"], lay["V"], cap, idx,
+                                            w.k, w.batch, w.n_q_heads,
+                                            w.n_kv_heads, w.d, dt_code, scale, out,
+                                            L.attn_ws, ev[10:14])
+
+    for t in range(W_steps):
+        step(t)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, captured as one HIP graph, replayed once
+    E_of.clear()
+    mode = "eager" if args.eager else "hip-graph"
+    g = None
+    if not args.eager:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            for t in range(K_steps):
+                step(W_steps + t)
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if g is None:
+        for t in range(K_steps):
+            step(W_steps + t)
+    else:
+        g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    E_timed = list(E_of)
+
+    # kernel durations: the next P steps launched with dispatch-stamped
+    # start/stop events on every kernel
+    P = min(K_steps, args.profile_steps)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(14)]
+              for _ in range(P)]
+    for row in events:          # torch creates the underlying event lazily
+        for e in row:
+            e.record()
+    E_of.clear()
+    torch.cuda.synchronize()
+    for t in range(P):
+        step(W_steps + K_steps + t, events[t])
+    torch.cuda.synchronize()
+    E_prof = np.array(E_of, dtype=np.float64)
+    kern = np.array([[events[t][2 * i].elapsed_time(events[t][2 * i + 1])
+                      for i in range(7)] for t in range(P)]) * 1e3   # us
+    names = [pk.pariskv_stage_name(i) for i in range(5)] + ["attn_split",
+                                                           "attn_merge"]
+    stage_us = {n: float(kern[:, i].mean()) for i, n in enumerate(names)}
+    step_us = np.array([events[t][0].elapsed_time(events[t][13])
+                        for t in range(P)]) * 1e3
+    E_of[:] = E_timed
+    E = np.array(E_of, dtype=np.float64)
+    keys_scanned = float(E.sum() * BH)
+    value = keys_scanned / wall
+    us_per_step = wall / K_steps * 1e6
+
+    scan_bytes = 16.0 * E_prof.mean() * BH
+    scan_us = float(kern[:, 1].mean())
+    achieved = scan_bytes / (scan_us * 1e-6) / 1e9
+    traffic = read_traffic("vote_scan_%s_traffic.txt" % args.workload, scan_bytes)
+    row_bytes = 2 * w.d * (2 if w.dtype == "bf16" else 4) + 4
+    attn_bytes = float(BH * w.k * row_bytes + 2 * w.batch * w.n_q_heads * w.d *
+                       (2 if w.dtype == "bf16" else 4))
+    attn_us = float(kern[:, 5].mean())
+    C = pk.pariskv_retrieve_sizes(layers[0][0].handle, w.k)[1]
+    rerank_bytes = 96.0 * C * BH
+    rerank_us = float(kern[:, 3].mean())
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": W_steps,
+        "ms_per_step": us_per_step / 1e3,
+        "us_per_step_per_layer": us_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (channel-scaled Gaussian keys with outlier "
+                "channels, Gaussian values; no model weights)",
+        "config": {
+            "workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads,
+            "n_q_heads": w.n_q_heads, "head_dim": w.d, "context": w.N,
+            "k": w.k, "sinks": w.sinks, "subspaces": w.B, "m": w.m,
+            "rho": w.rho, "tiers": list(w.tiers),
+            "candidate_fraction": "%d/%d" % (w.cand_num, w.cand_den),
+            "candidates_per_head": C, "layers_in_rotation": Lr,
+            "parallelism": "single GPU", "launch": mode,
+        },
+        "roofline": {
+            "kernel": "vote_scan",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": scan_bytes,
+            "avg_launch_us": scan_us,
+        },
+        "gather_roofline": {
+            "kernel": "attn_split",
+            "achieved": attn_bytes / (attn_us * 1e-6) / 1e9,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": attn_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": attn_bytes,
+            "avg_launch_us": attn_us,
+        },
+        "rerank_gather": {
+            "kernel": "compact_rerank",
+            "achieved": rerank_bytes / (rerank_us * 1e-6) / 1e9,
+            "unit": "GB/s", "algorithmic_bytes_per_launch": rerank_bytes,
+            "avg_launch_us": rerank_us,
+        },
+        "stage_us": stage_us,
+        "kernel_timing": "%d further steps, each kernel bracketed by start/stop "
+                         "events stamped by its own dispatch" % P,
+        "profiled_step_us": {"mean": float(step_us.mean()),
+                             "p50": float(np.percentile(step_us, 50)),
+                             "p90": float(np.percentile(step_us, 90))},
+        "kernel_sha256_16": kernel_sha(),
+    }
+
+    if not args.no_dense:
+        result["dense_attention"] = dense_attention(pk, torch, w, layers[0],
+                                                    cap, scale, dt_code)
+        result["dense_attention"]["speedup_of_step"] = \
+            result["dense_attention"]["us"] / us_per_step
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, layers[0][1], args.cpu_steps)
+    print(json.dumps(result), flush=True)
+
+
+def dense_attention(pk, torch, w, layer, cap, scale, dt_code, iters=5):
+    """Context: this library's attention kernel over all N rows (k = N)."""
+    L, lay = layer
+    N = w.N
+    BH = w.batch * w.n_kv_heads
+    idx = torch.arange(N, dtype=torch.int32, device="cuda").repeat(BH, 1)
+    ws = torch.empty(pk.pariskv_attn_workspace_bytes(w.batch, w.n_q_heads, N, w.d),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(lay["Q"])
+    run = lambda: pk.pariskv_sparse_attn(lay["Q"], lay["K"], lay["V"], cap, idx, N,
+                                         w.batch, w.n_q_heads, w.n_kv_heads, w.d,
+                                         dt_code, scale, out, ws)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    byts = BH * N * 2 * w.d * (2 if w.dtype == "bf16" else 4)
+    del idx, ws
+    return {"us": us, "gbps": byts / (us * 1e-6) / 1e9, "k": N}
+
+
+def cpu_baseline(w, lay, steps):
+    """The oracle, as it stands, on the host cores: every (batch, KV head) of
+    one layer, `steps` decode steps each (append one key, retrieve, attend);
+    the prefill encode of the sample is untimed."""
+    import numpy as np
+    import torch
+
+    import oracle as orc
+
+    BH = w.batch * w.n_kv_heads
+    nthreads = max(1, min(BH, os.cpu_count() or 1, 16))
+    N0 = w.N
+    Kh = lay["K"][:, :, :N0 + steps].float().cpu().numpy().reshape(BH, N0 + steps, w.d)
+    Vh = lay["V"][:, :, :N0 + steps].cpu().reshape(BH, N0 + steps, w.d)
+    Qh = lay["Q"].float().cpu().numpy()
+    signs = lay["signs"]
+    B = w.B
+    ids = np.zeros((BH, N0 + steps, B), np.uint8)
+    nib = np.zeros((BH, N0 + steps, w.d // 2), np.uint8)
+    wq = np.zeros((BH, N0 + steps, B), np.uint16)
+
+    def prefill(bh):
+        a, b_, c = orc.encode_keys(signs, Kh[bh, :N0], w.m)
+        ids[bh, :N0], nib[bh, :N0], wq[bh, :N0] = a, b_, c
+
+    with cf.ThreadPoolExecutor(nthreads) as ex:
+        list(ex.map(prefill, range(BH)))
+
+    def one(bh, t):
+        n = N0 + t + 1
+        a, b_, c = orc.encode_keys(signs, Kh[bh, n - 1:n], w.m)
+        ids[bh, n - 1], nib[bh, n - 1], wq[bh, n - 1] = a[0], b_[0], c[0]
+        b, h = divmod(bh, w.n_kv_heads)
+        Qg = Qh[b, h * w.G:(h + 1) * w.G]
+        r = orc.retrieve_head(signs, Qg, ids[bh, :n], nib[bh, :n], wq[bh, :n],
+                              m=w.m, rho=w.rho, tiers=w.tiers, S=w.sinks, k=w.k,
+                              num=w.cand_num, den=w.cand_den)
+        sel = r["idx"]
+        Vsel = Vh[bh][torch.from_numpy(sel).long()].float().numpy()
+        orc.attention(Qg, Kh[bh][sel], Vsel, np.arange(len(sel), dtype=np.int32),
+                      w.d ** -0.5)
+        return n - w.sinks
+
+    keys = 0
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(nthreads) as ex:
+        for t in range(steps):
+            keys += sum(ex.map(lambda bh: one(bh, t), range(BH)))
+    dt = time.perf_counter() - t0
+    return {"value": keys / dt, "unit": "keys/s", "cores": nthreads,
+            "kind": "oracle",
+            "us_per_step_per_layer": dt / steps * 1e6,
+            "sample": "all %d (batch, KV head) pairs of one %s layer, %d decode "
+                      "steps (append + retrieve + attention), index prefill "
+                      "untimed" % (BH, w.name, steps)}
+
+
+if __name__ == "__main__":
+    main()

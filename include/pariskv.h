@@ -183,10 +183,12 @@ PARISKV_API int32_t pariskv_retrieve_topk(const pariskv_index *index,
                                           void *ws, size_t ws_bytes,
                                           void *stream);
 
-/* Same as pariskv_retrieve_topk, and records events[s] before stage s and
- * events[PARISKV_RETRIEVE_STAGES] after the last one, on `stream` (events:
- * PARISKV_RETRIEVE_STAGES + 1 caller-created hipEvent_t).  Stages:
- * query prep, vote scan, threshold, compact + rerank, top-k. */
+/* Same as pariskv_retrieve_topk, and times each stage's kernel: events
+ * holds 2 * PARISKV_RETRIEVE_STAGES caller-created hipEvent_t (timing
+ * enabled); events[2s] and events[2s+1] are stamped by the dispatch of stage
+ * s itself when that kernel starts and ends (hipExtLaunchKernel), so the
+ * pair brackets exactly that kernel.  Stages: query prep, vote scan,
+ * threshold, compact + rerank, top-k.  Not for use under stream capture. */
 PARISKV_API int32_t pariskv_retrieve_topk_profiled(
     const pariskv_index *index, const void *Q, int32_t k, int32_t *out_idx,
     float *out_est, void *ws, size_t ws_bytes, void *stream, void **events);
@@ -221,8 +223,9 @@ PARISKV_API int32_t pariskv_sparse_attn(const void *Q, const void *K,
                                         void *ws, size_t ws_bytes,
                                         void *stream);
 
-/* Same, recording events[0] before the split-K kernel, events[1] between
- * it and the merge kernel and events[2] after (caller-created hipEvent_t). */
+/* Same, with events[0..1] stamped around the split-K kernel and
+ * events[2..3] around the merge kernel by their own dispatches
+ * (caller-created hipEvent_t, timing enabled). */
 PARISKV_API int32_t pariskv_sparse_attn_profiled(
     const void *Q, const void *K, const void *V, int64_t kv_rows_per_head,
     const int32_t *idx, int32_t k, int32_t batch, int32_t n_q_heads,

@@ -152,26 +152,32 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   pkv::Tiers tw;
   for (int s = 0; s < 8; ++s) tw.w[s] = c->tier_w[s];
 
-  auto mark = [&](int s) -> hipError_t {
-    return events ? hipEventRecord((hipEvent_t)events[s], st) : hipSuccess;
+  // events (optional): start/stop pair per stage, stamped by the dispatch
+  auto ev = [&](int s) {
+    pkv::EvPair p;
+    if (events) {
+      p.start = (hipEvent_t)events[2 * s];
+      p.stop = (hipEvent_t)events[2 * s + 1];
+    }
+    return p;
   };
+  (void)hipGetLastError();  // launches below report only their own errors
   hipError_t e;
-  if ((e = mark(0)) != hipSuccess) return hip_status(e);
   e = pkv::launch_qprep(c->key_dtype, Q, BH, c->n_kv_heads, G, ix->signs, ix->rot_c, c->rho, tw,
-                        lut, yq, st);
-  if (e != hipSuccess || (e = mark(1)) != hipSuccess) return hip_status(e);
+                        lut, yq, st, ev(0));
+  if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_scan(kpt, nch, BH, ix->ids, c->capacity, S, E, lut, scores, L.Epad, chist,
-                       (int)L.nchunks_max, L.nbins, st);
-  if (e != hipSuccess || (e = mark(2)) != hipSuccess) return hip_status(e);
-  e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, C, meta, coff, st);
-  if (e != hipSuccess || (e = mark(3)) != hipSuccess) return hip_status(e);
+                       (int)L.nchunks_max, L.nbins, st, ev(1));
+  if (e != hipSuccess) return hip_status(e);
+  e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, C, meta, coff, st, ev(2));
+  if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_compact_rerank(kpt, nch, BH, scores, L.Epad, S, E, meta, coff,
                                  (int)L.nchunks_max, yq, ix->nib, ix->w, c->capacity, cand, est,
-                                 L.cstride, C, st);
-  if (e != hipSuccess || (e = mark(4)) != hipSuccess) return hip_status(e);
+                                 L.cstride, C, st, ev(3));
+  if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_topk(BH, est, cand, L.cstride, (int)C, (int)kp, (int)S, k, out_idx, out_est,
-                       st);
-  if (e != hipSuccess || (e = mark(5)) != hipSuccess) return hip_status(e);
+                       st, ev(4));
+  if (e != hipSuccess) return hip_status(e);
   return PARISKV_OK;
 }
 
@@ -194,17 +200,19 @@ int32_t attn_impl(const void* Q, const void* K, const void* V, int64_t rows_per_
   hipStream_t st = (hipStream_t)stream;
   const int nch = (int)ceil_div(k, 64);
   const float qscale = scale * 1.4426950408889634f;
-  hipError_t e = events ? hipEventRecord((hipEvent_t)events[0], st) : hipSuccess;
+  pkv::EvPair e0, e1;
+  if (events) {
+    e0.start = (hipEvent_t)events[0];
+    e0.stop = (hipEvent_t)events[1];
+    e1.start = (hipEvent_t)events[2];
+    e1.stop = (hipEvent_t)events[3];
+  }
+  (void)hipGetLastError();
+  hipError_t e = pkv::launch_attn_split(dtype, G, Q, K, V, rows_per_head, idx, k, batch,
+                                        n_kv_heads, qscale, (float*)ws, nch, st, e0);
   if (e != hipSuccess) return hip_status(e);
-  e = pkv::launch_attn_split(dtype, G, Q, K, V, rows_per_head, idx, k, batch, n_kv_heads, qscale,
-                             (float*)ws, nch, st);
+  e = pkv::launch_attn_merge(dtype, (const float*)ws, nch, batch * n_q_heads, out, st, e1);
   if (e != hipSuccess) return hip_status(e);
-  if (events && (e = hipEventRecord((hipEvent_t)events[1], st)) != hipSuccess)
-    return hip_status(e);
-  e = pkv::launch_attn_merge(dtype, (const float*)ws, nch, batch * n_q_heads, out, st);
-  if (e != hipSuccess) return hip_status(e);
-  if (events && (e = hipEventRecord((hipEvent_t)events[2], st)) != hipSuccess)
-    return hip_status(e);
   return PARISKV_OK;
 }
 
@@ -267,9 +275,10 @@ int32_t pariskv_build_index(const pariskv_config* cfg, const int8_t* srht_signs,
   ix->n = 0;
   ix->last = (hipStream_t)stream;
   const int BH = cfg->batch * cfg->n_kv_heads;
+  (void)hipGetLastError();
   hipError_t e = pkv::launch_encode(cfg->key_dtype, K, k_rows_per_head, 0, n_keys, BH,
                                     cfg->capacity, ix->ids, ix->nib, ix->w, ix->signs, ix->rot_c,
-                                    (hipStream_t)stream);
+                                    (hipStream_t)stream, pkv::EvPair{});
   if (e != hipSuccess) {
     delete ix;
     return PARISKV_ERR_HIP;
@@ -287,9 +296,10 @@ int32_t pariskv_append_keys(pariskv_index* ix, const void* K_new, int64_t new_ro
   if (n_new == 0) return PARISKV_OK;
   const int BH = ix->cfg.batch * ix->cfg.n_kv_heads;
   ix->last = (hipStream_t)stream;
+  (void)hipGetLastError();
   hipError_t e = pkv::launch_encode(ix->cfg.key_dtype, K_new, new_rows_per_head, ix->n, n_new, BH,
                                     ix->cfg.capacity, ix->ids, ix->nib, ix->w, ix->signs,
-                                    ix->rot_c, (hipStream_t)stream);
+                                    ix->rot_c, (hipStream_t)stream, pkv::EvPair{});
   if (e != hipSuccess) return PARISKV_ERR_HIP;
   ix->n += n_new;
   return PARISKV_OK;
@@ -308,7 +318,7 @@ int32_t pariskv_retrieve_topk_profiled(const pariskv_index* ix, const void* Q, i
                                        int32_t* out_idx, float* out_est, void* ws,
                                        size_t ws_bytes, void* stream, void** events) {
   if (!events) return PARISKV_ERR_INVALID_ARG;
-  for (int s = 0; s <= PARISKV_RETRIEVE_STAGES; ++s)
+  for (int s = 0; s < 2 * PARISKV_RETRIEVE_STAGES; ++s)
     if (!events[s]) return PARISKV_ERR_INVALID_ARG;
   return retrieve_impl(ix, Q, k, out_idx, out_est, ws, ws_bytes, stream, events);
 }
@@ -332,7 +342,8 @@ int32_t pariskv_sparse_attn_profiled(const void* Q, const void* K, const void* V
                                      int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                      int32_t head_dim, int32_t dtype, float scale, void* out,
                                      void* ws, size_t ws_bytes, void* stream, void** events) {
-  if (!events || !events[0] || !events[1] || !events[2]) return PARISKV_ERR_INVALID_ARG;
+  if (!events || !events[0] || !events[1] || !events[2] || !events[3])
+    return PARISKV_ERR_INVALID_ARG;
   return attn_impl(Q, K, V, kv_rows_per_head, idx, k, batch, n_q_heads, n_kv_heads, head_dim,
                    dtype, scale, out, ws, ws_bytes, stream, events);
 }

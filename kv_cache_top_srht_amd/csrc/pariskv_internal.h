@@ -16,32 +16,46 @@ struct Tiers {
   int32_t w[8];
 };
 
+// Optional timing events stamped by a kernel's own dispatch (null: none).
+struct EvPair {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 hipError_t launch_encode(int dtype, const void* K, int64_t rows_per_head, int64_t lo, int64_t n,
                          int BH, int64_t cap, uint8_t* ids, uint32_t* nib, uint16_t* wq,
-                         const SignMask& sg, float c, hipStream_t st);
+                         const SignMask& sg, float c, hipStream_t st,
+                         const EvPair& ev);
 hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
                         const SignMask& sg, float c, int rho, const Tiers& tw, uint8_t* lut,
-                        float* yq, hipStream_t st);
+                        float* yq, hipStream_t st,
+                         const EvPair& ev);
 hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t cap, int64_t S,
                        int64_t E, const uint8_t* lut, uint8_t* scores, int64_t Epad,
-                       uint32_t* chist, int chunk_stride, int nbins, hipStream_t st);
+                       uint32_t* chist, int chunk_stride, int nbins, hipStream_t st,
+                         const EvPair& ev);
 hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nchunks, int nbins,
-                         int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st);
+                         int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st,
+                         const EvPair& ev);
 hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* scores,
                                  int64_t Epad, int64_t S, int64_t E, const int32_t* meta,
                                  const uint32_t* coff, int chunk_stride, const float* yq,
                                  const uint32_t* nib, const uint16_t* wq, int64_t cap,
                                  int32_t* cand, float* est, int64_t cstride, int64_t C,
-                                 hipStream_t st);
+                                 hipStream_t st,
+                         const EvPair& ev);
 hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cstride, int C,
                        int kprime, int S, int k, int32_t* out_idx, float* out_est,
-                       hipStream_t st);
+                       hipStream_t st,
+                         const EvPair& ev);
 hipError_t launch_attn_split(int dtype, int G, const void* Q, const void* K, const void* V,
                              int64_t rows_per_head, const int32_t* idx, int k, int batch,
                              int n_kv_heads, float qscale, float* part, int nch,
-                             hipStream_t st);
+                             hipStream_t st,
+                         const EvPair& ev);
 hipError_t launch_attn_merge(int dtype, const float* part, int nch, int rows, void* out,
-                             hipStream_t st);
+                             hipStream_t st,
+                         const EvPair& ev);
 void codebook_m8(float* L, float* tau);
 void codebook_m4(float* L, float* tau);
 

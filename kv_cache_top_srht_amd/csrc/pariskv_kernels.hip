@@ -11,6 +11,7 @@
 // file is built with -ffp-contract=off; division and square root are the
 // correctly rounded HIP defaults).  Attention is tolerance-checked and uses
 // explicit fused multiply-adds.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -695,59 +696,64 @@ __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ pa
 }
 
 // ---------------------------------------------------------------------------
-// Launchers (host side, called from the C ABI).
+// Launchers (host side, called from the C ABI).  Every launch goes through
+// hipExtLaunchKernelGGL: with a non-null start/stop event pair the dispatch
+// itself timestamps the kernel's execution (exact per-kernel durations even
+// when launches are host-bound); with null events it is a plain launch.
 // ---------------------------------------------------------------------------
+template <typename F, typename... Args>
+static hipError_t launch(F kernel, dim3 grid, dim3 block, hipStream_t st, const EvPair& ev,
+                         Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev.start, ev.stop, 0, args...);
+  return hipGetLastError();
+}
+
 hipError_t launch_encode(int dtype, const void* K, int64_t rows_per_head, int64_t lo, int64_t n,
                          int BH, int64_t cap, uint8_t* ids, uint32_t* nib, uint16_t* wq,
-                         const SignMask& sg, float c, hipStream_t st) {
+                         const SignMask& sg, float c, hipStream_t st, const EvPair& ev) {
   const int64_t total = (int64_t)BH * n;
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)((total + 15) / 16));
   if (dtype == 0)
-    hipLaunchKernelGGL(k_encode<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)K,
-                       rows_per_head, lo, n, total, cap, ids, nib, wq, sg, c);
-  else
-    hipLaunchKernelGGL(k_encode<float>, grid, dim3(256), 0, st, (const float*)K, rows_per_head,
-                       lo, n, total, cap, ids, nib, wq, sg, c);
-  return hipGetLastError();
+    return launch(k_encode<uint16_t>, grid, dim3(256), st, ev, (const uint16_t*)K,
+                  rows_per_head, lo, n, total, cap, ids, nib, wq, sg, c);
+  return launch(k_encode<float>, grid, dim3(256), st, ev, (const float*)K, rows_per_head, lo, n,
+                total, cap, ids, nib, wq, sg, c);
 }
 
 hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
                         const SignMask& sg, float c, int rho, const Tiers& tw, uint8_t* lut,
-                        float* yq, hipStream_t st) {
+                        float* yq, hipStream_t st, const EvPair& ev) {
   const float invG = 1.0f / (float)G;
   if (dtype == 0)
-    hipLaunchKernelGGL(k_qprep<uint16_t>, dim3(BH), dim3(256), 0, st, (const uint16_t*)Q,
-                       n_kv_heads, G, invG, sg, c, rho, tw, lut, yq);
-  else
-    hipLaunchKernelGGL(k_qprep<float>, dim3(BH), dim3(256), 0, st, (const float*)Q, n_kv_heads,
-                       G, invG, sg, c, rho, tw, lut, yq);
-  return hipGetLastError();
+    return launch(k_qprep<uint16_t>, dim3(BH), dim3(256), st, ev, (const uint16_t*)Q,
+                  n_kv_heads, G, invG, sg, c, rho, tw, lut, yq);
+  return launch(k_qprep<float>, dim3(BH), dim3(256), st, ev, (const float*)Q, n_kv_heads, G,
+                invG, sg, c, rho, tw, lut, yq);
 }
 
 hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t cap, int64_t S,
                        int64_t E, const uint8_t* lut, uint8_t* scores, int64_t Epad,
-                       uint32_t* chist, int chunk_stride, int nbins, hipStream_t st) {
+                       uint32_t* chist, int chunk_stride, int nbins, hipStream_t st,
+                       const EvPair& ev) {
   const dim3 grid(nchunks, BH);
   const uint4* id4 = (const uint4*)ids;
   switch (kpt) {
-#define PKV_SCAN(K)                                                                             \
-  case K:                                                                                       \
-    hipLaunchKernelGGL(k_scan<K>, grid, dim3(256), 0, st, id4, cap, S, E, lut, scores, Epad, \
-                       chist, chunk_stride, nbins);                                             \
-    break;
+#define PKV_SCAN(K)                                                                          \
+  case K:                                                                                    \
+    return launch(k_scan<K>, grid, dim3(256), st, ev, id4, cap, S, E, lut, scores, Epad,     \
+                  chist, chunk_stride, nbins);
     PKV_SCAN(1) PKV_SCAN(2) PKV_SCAN(4) PKV_SCAN(8) PKV_SCAN(16)
 #undef PKV_SCAN
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nchunks, int nbins,
-                         int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st) {
-  hipLaunchKernelGGL(k_thresh, dim3(BH), dim3(256), 0, st, chist, chunk_stride, nchunks, nbins,
-                     C, meta, coff);
-  return hipGetLastError();
+                         int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st,
+                         const EvPair& ev) {
+  return launch(k_thresh, dim3(BH), dim3(256), st, ev, chist, chunk_stride, nchunks, nbins, C,
+                meta, coff);
 }
 
 hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* scores,
@@ -755,69 +761,61 @@ hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* sc
                                  const uint32_t* coff, int chunk_stride, const float* yq,
                                  const uint32_t* nib, const uint16_t* wq, int64_t cap,
                                  int32_t* cand, float* est, int64_t cstride, int64_t C,
-                                 hipStream_t st) {
+                                 hipStream_t st, const EvPair& ev) {
   const dim3 grid(nchunks, BH);
   const uint4* n4 = (const uint4*)nib;
   const uint4* w4 = (const uint4*)wq;
   switch (kpt) {
-#define PKV_CR(K)                                                                               \
-  case K:                                                                                       \
-    hipLaunchKernelGGL(k_compact_rerank<K>, grid, dim3(256), 0, st, scores, Epad, S, E, meta, \
-                       coff, chunk_stride, yq, n4, w4, cap, cand, est, cstride, C);            \
-    break;
+#define PKV_CR(K)                                                                            \
+  case K:                                                                                    \
+    return launch(k_compact_rerank<K>, grid, dim3(256), st, ev, scores, Epad, S, E, meta,    \
+                  coff, chunk_stride, yq, n4, w4, cap, cand, est, cstride, C);
     PKV_CR(1) PKV_CR(2) PKV_CR(4) PKV_CR(8) PKV_CR(16)
 #undef PKV_CR
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cstride, int C,
                        int kprime, int S, int k, int32_t* out_idx, float* out_est,
-                       hipStream_t st) {
-  hipLaunchKernelGGL(k_topk, dim3(BH), dim3(1024), 0, st, est, cand, cstride, C, kprime, S, k,
-                     out_idx, out_est);
-  return hipGetLastError();
+                       hipStream_t st, const EvPair& ev) {
+  return launch(k_topk, dim3(BH), dim3(1024), st, ev, est, cand, cstride, C, kprime, S, k,
+                out_idx, out_est);
 }
 
 hipError_t launch_attn_split(int dtype, int G, const void* Q, const void* K, const void* V,
                              int64_t rows_per_head, const int32_t* idx, int k, int batch,
-                             int n_kv_heads, float qscale, float* part, int nch,
-                             hipStream_t st) {
+                             int n_kv_heads, float qscale, float* part, int nch, hipStream_t st,
+                             const EvPair& ev) {
   const dim3 grid(nch, batch * n_kv_heads);
-#define PKV_AS(T, GG)                                                                          \
-  hipLaunchKernelGGL((k_attn_split<T, GG>), grid, dim3(256), 0, st, (const T*)Q, (const T*)K, \
-                     (const T*)V, rows_per_head, idx, k, n_kv_heads, qscale, part, nch)
+#define PKV_AS(T, GG)                                                                         \
+  return launch(k_attn_split<T, GG>, grid, dim3(256), st, ev, (const T*)Q, (const T*)K,     \
+                (const T*)V, rows_per_head, idx, k, n_kv_heads, qscale, part, nch)
   if (dtype == 0) {
     switch (G) {
-      case 1: PKV_AS(uint16_t, 1); break;
-      case 2: PKV_AS(uint16_t, 2); break;
-      case 4: PKV_AS(uint16_t, 4); break;
-      case 8: PKV_AS(uint16_t, 8); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (G) {
-      case 1: PKV_AS(float, 1); break;
-      case 2: PKV_AS(float, 2); break;
-      case 4: PKV_AS(float, 4); break;
-      case 8: PKV_AS(float, 8); break;
+      case 1: PKV_AS(uint16_t, 1);
+      case 2: PKV_AS(uint16_t, 2);
+      case 4: PKV_AS(uint16_t, 4);
+      case 8: PKV_AS(uint16_t, 8);
       default: return hipErrorInvalidValue;
     }
   }
+  switch (G) {
+    case 1: PKV_AS(float, 1);
+    case 2: PKV_AS(float, 2);
+    case 4: PKV_AS(float, 4);
+    case 8: PKV_AS(float, 8);
+    default: return hipErrorInvalidValue;
+  }
 #undef PKV_AS
-  return hipGetLastError();
 }
 
 hipError_t launch_attn_merge(int dtype, const float* part, int nch, int rows, void* out,
-                             hipStream_t st) {
+                             hipStream_t st, const EvPair& ev) {
   if (dtype == 0)
-    hipLaunchKernelGGL(k_attn_merge<uint16_t>, dim3(rows), dim3(128), 0, st, part, nch,
-                       (uint16_t*)out);
-  else
-    hipLaunchKernelGGL(k_attn_merge<float>, dim3(rows), dim3(128), 0, st, part, nch,
-                       (float*)out);
-  return hipGetLastError();
+    return launch(k_attn_merge<uint16_t>, dim3(rows), dim3(128), st, ev, part, nch,
+                  (uint16_t*)out);
+  return launch(k_attn_merge<float>, dim3(rows), dim3(128), st, ev, part, nch, (float*)out);
 }
 
 void codebook_m8(float* L, float* tau) {
