@@ -122,14 +122,14 @@ def main():
             L.retrieve(lay["Q"], idx)
             L.attend(lay["Q"], lay["K"], lay["V"], idx, out, scale)
         else:
-            # ev[0:10]: start/stop of the 5 retrieval kernels, ev[10:14]: of
+            # ev[0:12]: start/stop of the 6 retrieval kernels, ev[12:16]: of
             # the 2 attention kernels, stamped by the dispatches themselves
             pk.pariskv_retrieve_topk_profiled(L.handle, lay["Q"], w.k, idx, None,
-                                              L.ws, ev[0:10])
+                                              L.ws, ev[0:12])
             pk.pariskv_sparse_attn_profiled(lay["Q"], lay["K"], lay["V"], cap, idx,
                                             w.k, w.batch, w.n_q_heads,
                                             w.n_kv_heads, w.d, dt_code, scale, out,
-                                            L.attn_ws, ev[10:14])
+                                            L.attn_ws, ev[12:16])
 
     for t in range(W_steps):
         step(t)
@@ -159,7 +159,7 @@ def main():
     # kernel durations: the next P steps launched with dispatch-stamped
     # start/stop events on every kernel
     P = min(K_steps, args.profile_steps)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(14)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(16)]
               for _ in range(P)]
     for row in events:          # torch creates the underlying event lazily
         for e in row:
@@ -171,11 +171,11 @@ def main():
     torch.cuda.synchronize()
     E_prof = np.array(E_of, dtype=np.float64)
     kern = np.array([[events[t][2 * i].elapsed_time(events[t][2 * i + 1])
-                      for i in range(7)] for t in range(P)]) * 1e3   # us
-    names = [pk.pariskv_stage_name(i) for i in range(5)] + ["attn_split",
-                                                           "attn_merge"]
+                      for i in range(8)] for t in range(P)]) * 1e3   # us
+    names = [pk.pariskv_stage_name(i) for i in range(pk.PARISKV_RETRIEVE_STAGES)] + \
+        ["attn_split", "attn_merge"]
     stage_us = {n: float(kern[:, i].mean()) for i, n in enumerate(names)}
-    step_us = np.array([events[t][0].elapsed_time(events[t][13])
+    step_us = np.array([events[t][0].elapsed_time(events[t][15])
                         for t in range(P)]) * 1e3
     E_of[:] = E_timed
     E = np.array(E_of, dtype=np.float64)
@@ -190,7 +190,7 @@ def main():
     row_bytes = 2 * w.d * (2 if w.dtype == "bf16" else 4) + 4
     attn_bytes = float(BH * w.k * row_bytes + 2 * w.batch * w.n_q_heads * w.d *
                        (2 if w.dtype == "bf16" else 4))
-    attn_us = float(kern[:, 5].mean())
+    attn_us = float(kern[:, 6].mean())
     C = pk.pariskv_retrieve_sizes(layers[0][0].handle, w.k)[1]
     rerank_bytes = 96.0 * C * BH
     rerank_us = float(kern[:, 3].mean())
@@ -253,6 +253,8 @@ def main():
         "kernel_sha256_16": kernel_sha(),
     }
 
+    result["stream_copy"] = stream_copy(torch)
+    result["roofline"]["frac_of_stream_copy"] = achieved / result["stream_copy"]["gbps"]
     if not args.no_dense:
         result["dense_attention"] = dense_attention(pk, torch, w, layers[0],
                                                     cap, scale, dt_code)
@@ -261,6 +263,24 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, layers[0][1], args.cpu_steps)
     print(json.dumps(result), flush=True)
+
+
+def stream_copy(torch, nbytes=2 << 30, iters=5):
+    """Achievable HBM bandwidth on this machine: a device-to-device copy of
+    nbytes (read + write counted), for comparison with the vendor peak."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    del a, b
+    return {"bytes": 2 * nbytes, "us": us, "gbps": 2 * nbytes / (us * 1e-6) / 1e9}
 
 
 def dense_attention(pk, torch, w, layer, cap, scale, dt_code, iters=5):

@@ -87,14 +87,16 @@ typedef struct pariskv_config {
 typedef struct pariskv_index pariskv_index;   /* opaque host-side handle */
 
 /* Number of stages that pariskv_retrieve_topk_profiled brackets. */
-#define PARISKV_RETRIEVE_STAGES 5
+#define PARISKV_RETRIEVE_STAGES 6
 
 /* ---------------------------------------------------------------------- */
 /* Sizing.                                                                 */
 /* ---------------------------------------------------------------------- */
 
-/* Bytes of the device index buffer for `cfg` (bucket ids 16 B, RSQ-IP codes
- * 64 B and fp16 calibration 32 B per key and (b, h), for `capacity` keys).
+/* Bytes of the device index buffer for `cfg`: per key and (b, h), 16 B of
+ * bucket ids and a 128-byte record holding the 64 B of RSQ-IP codes and the
+ * 32 B of fp16 calibration factors (one aligned line per key, so a rerank
+ * gather touches one line), for `capacity` keys.
  * Errors: INVALID_ARG / UNSUPPORTED for a bad config. */
 PARISKV_API int32_t pariskv_index_bytes(const pariskv_config *cfg,
                                         size_t *bytes);
@@ -144,6 +146,12 @@ PARISKV_API int32_t pariskv_build_index(const pariskv_config *cfg,
  *                K_new[((b * n_kv_heads + h) * new_rows_per_head + r) * d + j]
  *                for r < n_new (a pointer into the KV cache at row N with
  *                new_rows_per_head = the cache's rows per head works).
+ * A decode step's few keys (n_new <= 48) are encoded lazily: by the first
+ * kernel of the next pariskv_retrieve_topk on the same stream, or, if
+ * something else comes first (another append, a retrieval on another stream,
+ * pariskv_debug_export, pariskv_index_destroy), by a kernel launched then on
+ * this call's stream.  K_new must stay valid and unmodified until then.
+ * Larger appends are encoded at once on `stream`.
  * Errors: INVALID_ARG, CAPACITY (N + n_new > capacity), HIP. */
 PARISKV_API int32_t pariskv_append_keys(pariskv_index *index,
                                         const void *K_new,
@@ -153,7 +161,8 @@ PARISKV_API int32_t pariskv_append_keys(pariskv_index *index,
 /* Current number of keys per (b, h), or -1 for a NULL handle. */
 PARISKV_API int64_t pariskv_index_size(const pariskv_index *index);
 
-/* Frees the host handle only (never the caller's index buffer). */
+/* Encodes any deferred appended keys (on the stream they were appended on),
+ * then frees the host handle (never the caller's index buffer). */
 PARISKV_API void pariskv_index_destroy(pariskv_index *index);
 
 /* ---------------------------------------------------------------------- */
@@ -176,7 +185,8 @@ PARISKV_API void pariskv_index_destroy(pariskv_index *index);
  *   ws       device workspace of >= pariskv_retrieve_workspace_bytes(k),
  *            256-byte aligned; its contents need not be initialised.
  * No host synchronisation and no allocation: capturable in a HIP graph.
- * Errors: INVALID_ARG (k <= S or k > N, null pointers), WORKSPACE, HIP. */
+ * Errors: INVALID_ARG (k <= S or k > N, null pointers), WORKSPACE,
+ * UNSUPPORTED (more than 4,194,304 candidates per (b, h)), HIP. */
 PARISKV_API int32_t pariskv_retrieve_topk(const pariskv_index *index,
                                           const void *Q, int32_t k,
                                           int32_t *out_idx, float *out_est,
@@ -188,7 +198,8 @@ PARISKV_API int32_t pariskv_retrieve_topk(const pariskv_index *index,
  * enabled); events[2s] and events[2s+1] are stamped by the dispatch of stage
  * s itself when that kernel starts and ends (hipExtLaunchKernel), so the
  * pair brackets exactly that kernel.  Stages: query prep, vote scan,
- * threshold, compact + rerank, top-k.  Not for use under stream capture. */
+ * threshold, compact + rerank, top-k histogram, top-k select.
+ * Not for use under stream capture. */
 PARISKV_API int32_t pariskv_retrieve_topk_profiled(
     const pariskv_index *index, const void *Q, int32_t k, int32_t *out_idx,
     float *out_est, void *ws, size_t ws_bytes, void *stream, void **events);

@@ -19,7 +19,7 @@ SO_PATH = os.path.join(_PKG, "libpariskv.so")
 PARISKV_OK = 0
 PARISKV_DTYPE_BF16 = 0
 PARISKV_DTYPE_FP32 = 1
-PARISKV_RETRIEVE_STAGES = 5
+PARISKV_RETRIEVE_STAGES = 6
 
 DEBUG_LUT, DEBUG_YQ, DEBUG_SCORES, DEBUG_CAND, DEBUG_EST, DEBUG_THRESH = range(6)
 

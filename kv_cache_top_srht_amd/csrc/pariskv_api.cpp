@@ -16,10 +16,11 @@ struct pariskv_index {
   pkv::SignMask signs;
   float rot_c;
   uint8_t* ids;    // [BH][cap][16]  bucket id per subspace
-  uint32_t* nib;   // [BH][cap][16]  8 RSQ-IP nibbles per subspace
-  uint16_t* w;     // [BH][cap][16]  fp16 calibration per subspace
-  int64_t n;       // keys per (b, h)
+  uint32_t* rec;   // [BH][cap][32]  128-byte record: 16 code dwords, 16 fp16 w, pad
+  int64_t n;       // keys per (b, h), including appended keys not yet encoded
   hipStream_t last;
+  pkv::AppendJob pending;       // appended rows the next retrieval encodes
+  hipStream_t pending_stream;
 };
 
 namespace {
@@ -68,22 +69,22 @@ int32_t check_cfg(const pariskv_config* c) {
 }
 
 struct IndexLayout {
-  size_t ids, nib, w, total;
+  size_t ids, rec, total;
 };
 
 IndexLayout index_layout(const pariskv_config* c) {
   const size_t keys = (size_t)c->batch * c->n_kv_heads * (size_t)c->capacity;
   IndexLayout L;
   L.ids = 0;
-  L.nib = align_up(keys * 16, kAlign);
-  L.w = L.nib + align_up(keys * 64, kAlign);
-  L.total = L.w + align_up(keys * 32, kAlign);
+  L.rec = align_up(keys * 16, kAlign);
+  L.total = L.rec + align_up(keys * 128, kAlign);
   return L;
 }
 
 struct WsLayout {
-  size_t lut, yq, scores, chist, coff, meta, cand, est, total;
-  int64_t Epad, nchunks_max, cstride;
+  size_t lut, yq, ptab, scores, chist, coff, meta, cand, est, mmc, range, tkmeta, rows, sorted,
+      total;
+  int64_t Epad, nchunks_max, cstride, tk_blocks_max;
   int nbins;
 };
 
@@ -97,24 +98,32 @@ WsLayout ws_layout(const pariskv_config* c, int64_t k) {
   L.nbins = c->n_subspaces * max_tier(c) + 1;
   L.nchunks_max = ceil_div(Emax, 256);
   L.Epad = (int64_t)align_up((size_t)Emax, 4096);
-  L.cstride = Cmax > 0 ? Cmax : 1;
+  L.cstride = (int64_t)align_up((size_t)(Cmax > 0 ? Cmax : 1), 64);  // 256-byte rows
   size_t off = 0;
   L.lut = off;    off += align_up((size_t)BH * 16 * 256, kAlign);
   L.yq = off;     off += align_up((size_t)BH * 128 * 4, kAlign);
+  L.ptab = off;   off += align_up((size_t)BH * 2048 * 4, kAlign);
   L.scores = off; off += align_up((size_t)BH * L.Epad, kAlign);
   L.chist = off;  off += align_up((size_t)BH * L.nchunks_max * L.nbins * 4, kAlign);
   L.coff = off;   off += align_up((size_t)BH * L.nchunks_max * 8, kAlign);
   L.meta = off;   off += align_up((size_t)BH * 16, kAlign);
   L.cand = off;   off += align_up((size_t)BH * L.cstride * 4, kAlign);
   L.est = off;    off += align_up((size_t)BH * L.cstride * 4, kAlign);
+  L.tk_blocks_max = ceil_div(L.cstride, pkv::kTopkSlice);
+  L.mmc = off;    off += align_up((size_t)BH * L.nchunks_max * 8, kAlign);
+  L.range = off;  off += align_up((size_t)BH * 8, kAlign);
+  L.tkmeta = off; off += align_up((size_t)BH * 16, kAlign);
+  L.rows = off;   off += align_up((size_t)BH * L.tk_blocks_max * 2048 * 4, kAlign);
+  L.sorted = off; off += align_up((size_t)BH * L.tk_blocks_max * pkv::kTopkSlice * 8, kAlign);
   L.total = off;
   return L;
 }
 
 // Keys per thread of the scan/compaction chunks: the largest power of two
-// <= 16 that still gives >= 2048 blocks (8 per CU on 256 CUs).
+// <= 8 that still gives >= 2048 blocks (8 per CU on 256 CUs).  8 keys per
+// thread keeps the scan at 8 waves per SIMD, so a full wave of blocks fits.
 int pick_kpt(int64_t E, int64_t BH) {
-  int kpt = 16;
+  int kpt = 8;
   while (kpt > 1 && ceil_div(E, 256 * kpt) * BH < 2048) kpt >>= 1;
   return kpt;
 }
@@ -122,6 +131,18 @@ int pick_kpt(int64_t E, int64_t BH) {
 float rot_scale(int d) { return (float)(1.0L / std::sqrt((long double)d)); }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? PARISKV_OK : PARISKV_ERR_HIP; }
+
+// Encodes deferred appended keys now, on the stream they were appended on.
+int32_t flush_pending(pariskv_index* ix) {
+  if (ix->pending.n == 0) return PARISKV_OK;
+  const pkv::AppendJob job = ix->pending;
+  ix->pending.n = 0;
+  const int BH = ix->cfg.batch * ix->cfg.n_kv_heads;
+  (void)hipGetLastError();
+  return hip_status(pkv::launch_encode(ix->cfg.key_dtype, job.K, job.rows_per_head, job.lo, job.n,
+                                       BH, ix->cfg.capacity, ix->ids, ix->rec, ix->signs,
+                                       ix->rot_c, ix->pending_stream, pkv::EvPair{}));
+}
 
 int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t* out_idx,
                       float* out_est, void* ws, size_t ws_bytes, void* stream, void** events) {
@@ -133,22 +154,42 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   const WsLayout L = ws_layout(c, k);
   if (ws_bytes < L.total) return PARISKV_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  const_cast<pariskv_index*>(ix)->last = st;
+  pariskv_index* mix = const_cast<pariskv_index*>(ix);
+  mix->last = st;
+  // deferred appends: encoded by the query-prep kernel when they were
+  // appended on this stream, else first on their own stream
+  pkv::AppendJob app;
+  if (mix->pending.n > 0) {
+    if (mix->pending_stream == st) {
+      app = mix->pending;
+      mix->pending.n = 0;
+    } else if (int32_t rc = flush_pending(mix)) {
+      return rc;
+    }
+  }
   const int BH = c->batch * c->n_kv_heads;
   const int G = c->n_q_heads / c->n_kv_heads;
   const int64_t E = N - S, kp = k - S;
   const int64_t C = cand_count(E, kp, c->cand_num, c->cand_den);
+  if (C > 1024ll * pkv::kTopkSlice) return PARISKV_ERR_UNSUPPORTED;  // > 4M candidates per head
   const int kpt = pick_kpt(E, BH);
+  const int P = (int)ceil_div(C, pkv::kTopkSlice);
   const int nch = (int)ceil_div(E, 256 * kpt);
   uint8_t* base = (uint8_t*)ws;
   uint8_t* lut = base + L.lut;
   float* yq = (float*)(base + L.yq);
+  float* ptab = (float*)(base + L.ptab);
   uint8_t* scores = base + L.scores;
   uint32_t* chist = (uint32_t*)(base + L.chist);
   uint32_t* coff = (uint32_t*)(base + L.coff);
   int32_t* meta = (int32_t*)(base + L.meta);
   int32_t* cand = (int32_t*)(base + L.cand);
   float* est = (float*)(base + L.est);
+  uint32_t* mmc = (uint32_t*)(base + L.mmc);
+  uint32_t* range = (uint32_t*)(base + L.range);
+  int32_t* tkmeta = (int32_t*)(base + L.tkmeta);
+  uint32_t* rows = (uint32_t*)(base + L.rows);
+  uint2* sorted = (uint2*)(base + L.sorted);
   pkv::Tiers tw;
   for (int s = 0; s < 8; ++s) tw.w[s] = c->tier_w[s];
 
@@ -164,7 +205,7 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   (void)hipGetLastError();  // launches below report only their own errors
   hipError_t e;
   e = pkv::launch_qprep(c->key_dtype, Q, BH, c->n_kv_heads, G, ix->signs, ix->rot_c, c->rho, tw,
-                        lut, yq, st, ev(0));
+                        lut, yq, ptab, app, st, ev(0));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_scan(kpt, nch, BH, ix->ids, c->capacity, S, E, lut, scores, L.Epad, chist,
                        (int)L.nchunks_max, L.nbins, st, ev(1));
@@ -172,11 +213,12 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, C, meta, coff, st, ev(2));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_compact_rerank(kpt, nch, BH, scores, L.Epad, S, E, meta, coff,
-                                 (int)L.nchunks_max, yq, ix->nib, ix->w, c->capacity, cand, est,
-                                 L.cstride, C, st, ev(3));
+                                 (int)L.nchunks_max, ptab, ix->rec, c->capacity, cand, est,
+                                 L.cstride, C, mmc, st, ev(3));
   if (e != hipSuccess) return hip_status(e);
-  e = pkv::launch_topk(BH, est, cand, L.cstride, (int)C, (int)kp, (int)S, k, out_idx, out_est,
-                       st, ev(4));
+  e = pkv::launch_topk(BH, est, cand, L.cstride, (int)C, (int)kp, (int)S, k, P, mmc,
+                       (int)L.nchunks_max, nch, range, rows, tkmeta, sorted, out_idx, out_est, st,
+                       ev(4), ev(5));
   if (e != hipSuccess) return hip_status(e);
   return PARISKV_OK;
 }
@@ -270,14 +312,15 @@ int32_t pariskv_build_index(const pariskv_config* cfg, const int8_t* srht_signs,
   ix->rot_c = rot_scale(cfg->head_dim);
   uint8_t* base = (uint8_t*)index_buf;
   ix->ids = base + L.ids;
-  ix->nib = (uint32_t*)(base + L.nib);
-  ix->w = (uint16_t*)(base + L.w);
+  ix->rec = (uint32_t*)(base + L.rec);
   ix->n = 0;
   ix->last = (hipStream_t)stream;
+  ix->pending = pkv::AppendJob{};
+  ix->pending_stream = nullptr;
   const int BH = cfg->batch * cfg->n_kv_heads;
   (void)hipGetLastError();
   hipError_t e = pkv::launch_encode(cfg->key_dtype, K, k_rows_per_head, 0, n_keys, BH,
-                                    cfg->capacity, ix->ids, ix->nib, ix->w, ix->signs, ix->rot_c,
+                                    cfg->capacity, ix->ids, ix->rec, ix->signs, ix->rot_c,
                                     (hipStream_t)stream, pkv::EvPair{});
   if (e != hipSuccess) {
     delete ix;
@@ -294,11 +337,27 @@ int32_t pariskv_append_keys(pariskv_index* ix, const void* K_new, int64_t new_ro
     return PARISKV_ERR_INVALID_ARG;
   if (ix->n + n_new > ix->cfg.capacity) return PARISKV_ERR_CAPACITY;
   if (n_new == 0) return PARISKV_OK;
-  const int BH = ix->cfg.batch * ix->cfg.n_kv_heads;
+  if (int32_t rc = flush_pending(ix)) return rc;
   ix->last = (hipStream_t)stream;
+  if (n_new <= pkv::kMaxFusedAppend) {
+    // a decode step's few keys: encoded by the next retrieval's first kernel
+    pkv::AppendJob job;
+    job.K = K_new;
+    job.rows_per_head = new_rows_per_head;
+    job.lo = ix->n;
+    job.cap = ix->cfg.capacity;
+    job.ids = ix->ids;
+    job.rec = ix->rec;
+    job.n = (int)n_new;
+    ix->pending = job;
+    ix->pending_stream = (hipStream_t)stream;
+    ix->n += n_new;
+    return PARISKV_OK;
+  }
+  const int BH = ix->cfg.batch * ix->cfg.n_kv_heads;
   (void)hipGetLastError();
   hipError_t e = pkv::launch_encode(ix->cfg.key_dtype, K_new, new_rows_per_head, ix->n, n_new, BH,
-                                    ix->cfg.capacity, ix->ids, ix->nib, ix->w, ix->signs,
+                                    ix->cfg.capacity, ix->ids, ix->rec, ix->signs,
                                     ix->rot_c, (hipStream_t)stream, pkv::EvPair{});
   if (e != hipSuccess) return PARISKV_ERR_HIP;
   ix->n += n_new;
@@ -307,7 +366,10 @@ int32_t pariskv_append_keys(pariskv_index* ix, const void* K_new, int64_t new_ro
 
 int64_t pariskv_index_size(const pariskv_index* ix) { return ix ? ix->n : -1; }
 
-void pariskv_index_destroy(pariskv_index* ix) { delete ix; }
+void pariskv_index_destroy(pariskv_index* ix) {
+  if (ix) (void)flush_pending(ix);  // the caller's index buffer gets every key
+  delete ix;
+}
 
 int32_t pariskv_retrieve_topk(const pariskv_index* ix, const void* Q, int32_t k, int32_t* out_idx,
                               float* out_est, void* ws, size_t ws_bytes, void* stream) {
@@ -324,8 +386,8 @@ int32_t pariskv_retrieve_topk_profiled(const pariskv_index* ix, const void* Q, i
 }
 
 const char* pariskv_stage_name(int32_t s) {
-  static const char* names[PARISKV_RETRIEVE_STAGES] = {"query_prep", "vote_scan", "threshold",
-                                                       "compact_rerank", "topk"};
+  static const char* names[PARISKV_RETRIEVE_STAGES] = {
+      "query_prep", "vote_scan", "threshold", "compact_rerank", "topk_histogram", "topk_select"};
   return (s >= 0 && s < PARISKV_RETRIEVE_STAGES) ? names[s] : nullptr;
 }
 
@@ -351,6 +413,7 @@ int32_t pariskv_sparse_attn_profiled(const void* Q, const void* K, const void* V
 int32_t pariskv_debug_export(const pariskv_index* ix, int64_t lo, int64_t hi, uint8_t* ids_host,
                              uint8_t* nib_host, uint16_t* w_host) {
   if (!ix || lo < 0 || hi < lo || hi > ix->cfg.capacity) return PARISKV_ERR_INVALID_ARG;
+  if (flush_pending(const_cast<pariskv_index*>(ix))) return PARISKV_ERR_HIP;
   if (hipDeviceSynchronize() != hipSuccess) return PARISKV_ERR_HIP;
   const int64_t BH = (int64_t)ix->cfg.batch * ix->cfg.n_kv_heads;
   const int64_t cap = ix->cfg.capacity, n = hi - lo;
@@ -360,11 +423,12 @@ int32_t pariskv_debug_export(const pariskv_index* ix, int64_t lo, int64_t hi, ui
     if (ids_host && hipMemcpy(ids_host + bh * n * 16, ix->ids + key * 16, n * 16,
                               hipMemcpyDeviceToHost) != hipSuccess)
       return PARISKV_ERR_HIP;
-    if (nib_host && hipMemcpy(nib_host + bh * n * 64, (const uint8_t*)ix->nib + key * 64, n * 64,
-                              hipMemcpyDeviceToHost) != hipSuccess)
+    const uint8_t* rec = (const uint8_t*)ix->rec + key * 128;
+    if (nib_host && hipMemcpy2D(nib_host + bh * n * 64, 64, rec, 128, 64, n,
+                                hipMemcpyDeviceToHost) != hipSuccess)
       return PARISKV_ERR_HIP;
-    if (w_host && hipMemcpy(w_host + bh * n * 16, ix->w + key * 16, n * 32,
-                            hipMemcpyDeviceToHost) != hipSuccess)
+    if (w_host && hipMemcpy2D(w_host + bh * n * 16, 32, rec + 64, 128, 32, n,
+                              hipMemcpyDeviceToHost) != hipSuccess)
       return PARISKV_ERR_HIP;
   }
   return PARISKV_OK;

@@ -16,6 +16,20 @@ struct Tiers {
   int32_t w[8];
 };
 
+// Keys appended to the index but not yet encoded: rows [0, n) of each (b, h)
+// of K go to positions [lo, lo + n).  The query-prep kernel of the next
+// retrieval encodes them (n <= kMaxFusedAppend).
+struct AppendJob {
+  const void* K = nullptr;
+  int64_t rows_per_head = 0;
+  int64_t lo = 0;
+  int64_t cap = 0;
+  uint8_t* ids = nullptr;
+  uint32_t* rec = nullptr;
+  int n = 0;
+};
+constexpr int kMaxFusedAppend = 48;
+
 // Optional timing events stamped by a kernel's own dispatch (null: none).
 struct EvPair {
   hipEvent_t start = nullptr;
@@ -23,13 +37,12 @@ struct EvPair {
 };
 
 hipError_t launch_encode(int dtype, const void* K, int64_t rows_per_head, int64_t lo, int64_t n,
-                         int BH, int64_t cap, uint8_t* ids, uint32_t* nib, uint16_t* wq,
-                         const SignMask& sg, float c, hipStream_t st,
-                         const EvPair& ev);
+                         int BH, int64_t cap, uint8_t* ids, uint32_t* rec, const SignMask& sg,
+                         float c, hipStream_t st, const EvPair& ev);
 hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
                         const SignMask& sg, float c, int rho, const Tiers& tw, uint8_t* lut,
-                        float* yq, hipStream_t st,
-                         const EvPair& ev);
+                        float* yq, float* ptab, const AppendJob& app, hipStream_t st,
+                        const EvPair& ev);
 hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t cap, int64_t S,
                        int64_t E, const uint8_t* lut, uint8_t* scores, int64_t Epad,
                        uint32_t* chist, int chunk_stride, int nbins, hipStream_t st,
@@ -39,15 +52,18 @@ hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nc
                          const EvPair& ev);
 hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* scores,
                                  int64_t Epad, int64_t S, int64_t E, const int32_t* meta,
-                                 const uint32_t* coff, int chunk_stride, const float* yq,
-                                 const uint32_t* nib, const uint16_t* wq, int64_t cap,
-                                 int32_t* cand, float* est, int64_t cstride, int64_t C,
-                                 hipStream_t st,
-                         const EvPair& ev);
+                                 const uint32_t* coff, int chunk_stride, const float* ptab,
+                                 const uint32_t* rec, int64_t cap, int32_t* cand, float* est,
+                                 int64_t cstride, int64_t C, uint32_t* mm, hipStream_t st,
+                                 const EvPair& ev);
 hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cstride, int C,
-                       int kprime, int S, int k, int32_t* out_idx, float* out_est,
-                       hipStream_t st,
-                         const EvPair& ev);
+                       int kprime, int S, int k, int P, const uint32_t* mmc, int chunk_stride,
+                       int nchunks, uint32_t* range, uint32_t* rows, int32_t* tkmeta,
+                       uint2* sorted, int32_t* out_idx, float* out_est, hipStream_t st,
+                       const EvPair& ev_hist, const EvPair& ev_select);
+// candidates per top-k block and the largest threshold bin ranked pairwise
+constexpr int kTopkSlice = 4096;
+constexpr int kTopkMaxMembers = 4096;
 hipError_t launch_attn_split(int dtype, int G, const void* Q, const void* K, const void* V,
                              int64_t rows_per_head, const int32_t* idx, int k, int batch,
                              int n_kv_heads, float qscale, float* part, int nch,

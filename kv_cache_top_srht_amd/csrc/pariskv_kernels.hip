@@ -47,6 +47,17 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// Order key of an estimate: unsigned order == (est desc) order, -0 == +0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f == 0.0f) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Inverse of order_key (a -0 input comes back as +0).
+__device__ __forceinline__ float key_float(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
 // ---------------------------------------------------------------------------
 // Shared SRHT rotation, [TS] Core Algorithmic Innovations 1 ("Normalization
 // and Rotation"): y = c * H * (D .* x), H Sylvester-ordered, d = 128.
@@ -99,19 +110,17 @@ __device__ __forceinline__ uint32_t sign_byte_of(const SignMask& sg, int sub) {
 //   u_j  = z_j / n; mag_j = #{l : |u_j| >= tau_l}; code_j = sign_j << 3 | mag_j
 //   a    = ((v_0 u_0 + v_1 u_1) + ...), v_j = +-L[mag_j]
 //   w    = fp16_rne(n / a)           (n == 0: magnitudes 0, w = 0)
-// Index layout per (b,h): ids [cap][16] bytes, codes [cap][16] dwords
-// (nibble j of dword s = coordinate 8 s + j), w [cap][16] fp16.
+// Index layout per (b,h): ids [cap][16] bytes and a 128-byte record per key
+// (one L2 line): dwords 0..15 = codes (nibble j of dword s = coordinate
+// 8 s + j), bytes 64..95 = w as 16 fp16, bytes 96..127 unused.
 // ---------------------------------------------------------------------------
+// Encodes key row r of (b, h) = bh (16 lanes, lane `sub` = subspace `sub`)
+// into index position `pos`.
 template <typename T>
-__global__ __launch_bounds__(256) void k_encode(const T* __restrict__ K, int64_t rows_per_head,
-                                                int64_t lo, int64_t n, int64_t total, int64_t cap,
-                                                uint8_t* __restrict__ ids, uint32_t* __restrict__ nib,
-                                                uint16_t* __restrict__ wq, SignMask sg, float c) {
-  const int sub = threadIdx.x & 15;
-  const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  if (g >= total) return;  // whole 16-lane groups leave together
-  const int64_t bh = g / n;
-  const int64_t r = g - bh * n;
+__device__ __forceinline__ void encode_key(const T* __restrict__ K, int64_t rows_per_head,
+                                           int64_t bh, int64_t r, int64_t pos, int64_t cap,
+                                           uint8_t* __restrict__ ids, uint32_t* __restrict__ rec,
+                                           const SignMask& sg, float c, int sub) {
   float x[8];
   load8(K + ((bh * rows_per_head + r) << 7) + sub * 8, x);
   srht16(x, sign_byte_of(sg, sub), sub, c);
@@ -147,10 +156,23 @@ __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ K, int64_t
 #pragma unroll
     for (int j = 0; j < 8; ++j) code |= ((id >> j) & 1u) << (4 * j + 3);
   }
-  const int64_t key = bh * cap + lo + r;
+  const int64_t key = bh * cap + pos;
   ids[key * 16 + sub] = (uint8_t)id;
-  nib[key * 16 + sub] = code;
-  wq[key * 16 + sub] = wbits;
+  rec[key * 32 + sub] = code;
+  reinterpret_cast<uint16_t*>(rec)[key * 64 + 32 + sub] = wbits;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_encode(const T* __restrict__ K, int64_t rows_per_head,
+                                                int64_t lo, int64_t n, int64_t total, int64_t cap,
+                                                uint8_t* __restrict__ ids, uint32_t* __restrict__ rec,
+                                                SignMask sg, float c) {
+  const int sub = threadIdx.x & 15;
+  const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (g >= total) return;  // whole 16-lane groups leave together
+  const int64_t bh = g / n;
+  const int64_t r = g - bh * n;
+  encode_key(K, rows_per_head, bh, r, lo + r, cap, ids, rec, sg, c, sub);
 }
 
 // ---------------------------------------------------------------------------
@@ -186,18 +208,32 @@ __device__ __forceinline__ uint2 block_exscan2(uint2 v, uint2* s_warp, uint2& to
 // Per subspace s, the 256 centroid scores sc_p = sum_j (bit j of p ? -yq : +yq)
 // (sequential in j from the j = 0 term); the rho best by (sc desc, p asc)
 // get tier weights in the vote LUT, all other centroids 0.
-// One block (256 threads) per (b, h).
+// One 1024-thread block per (b, h): wave s handles subspace s, lane l scores
+// centroids 4 l .. 4 l + 3 and keeps them in order; rho rounds of a wave
+// arg-max (6 xor-shuffle steps) pick the winners.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ bool better(float va, int pa, float vb, int pb) {
+  return va > vb || (va == vb && pa < pb);
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_qprep(const T* __restrict__ Q, int n_kv_heads, int G,
-                                               float invG, SignMask sg, float c, int rho, Tiers tw,
-                                               uint8_t* __restrict__ lut_out, float* __restrict__ yq_out) {
+__global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_kv_heads, int G,
+                                                float invG, SignMask sg, float c, int rho, Tiers tw,
+                                                uint8_t* __restrict__ lut_out, float* __restrict__ yq_out,
+                                                float* __restrict__ ptab_out, AppendJob app) {
   const int bh = blockIdx.x;
   const int b = bh / n_kv_heads, h = bh - b * n_kv_heads;
   const int Hq = n_kv_heads * G;
   const int tid = threadIdx.x;
   __shared__ float s_yq[128];
-  __shared__ float s_sc[16][256];
+  // keys appended since the last retrieval are encoded here (threads 256+,
+  // 16 per key), so the vote scan that follows sees them
+  if (app.n > 0 && tid >= 256) {
+    const int r = (tid - 256) >> 4;
+    if (r < app.n)
+      encode_key((const T*)app.K, app.rows_per_head, bh, r, app.lo + r, app.cap, app.ids,
+                 app.rec, sg, c, tid & 15);
+  }
   if (tid < 16) {
     const int sub = tid;
     float x[8];
@@ -213,51 +249,67 @@ __global__ __launch_bounds__(256) void k_qprep(const T* __restrict__ Q, int n_kv
     for (int j = 0; j < 8; ++j) x[j] = x[j] * invG;
     srht16(x, sign_byte_of(sg, sub), sub, c);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      s_yq[sub * 8 + j] = x[j];
-      yq_out[(int64_t)bh * 128 + sub * 8 + j] = x[j];
-    }
+    for (int j = 0; j < 8; ++j) s_yq[sub * 8 + j] = x[j];
+    reinterpret_cast<float4*>(yq_out + (int64_t)bh * 128 + sub * 8)[0] =
+        make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4*>(yq_out + (int64_t)bh * 128 + sub * 8)[1] =
+        make_float4(x[4], x[5], x[6], x[7]);
   }
   __syncthreads();
-  {
-    const int p = tid;
-#pragma unroll 4
-    for (int s = 0; s < 16; ++s) {
-      const float* z = s_yq + s * 8;
-      float acc = (p & 1) ? -z[0] : z[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) acc = acc + (((p >> j) & 1) ? -z[j] : z[j]);
-      s_sc[s][p] = acc;
-    }
+  // product table for the rerank: ptab[j][code] = fl((code & 8 ? -1 : 1) L[code & 7] yq_j)
+  for (int e = tid; e < 2048; e += 1024) {
+    const int j = e >> 4, code = e & 15;
+    const float pr = c_levels[code & 7] * s_yq[j];
+    ptab_out[(int64_t)bh * 2048 + e] = (code & 8) ? -pr : pr;
   }
-  __syncthreads();
-  const int lane = tid & 63, wv = tid >> 6;
-  for (int s = wv; s < 16; s += 4) {
-    float v[4];
-    int pi[4];
-    bool taken[4] = {false, false, false, false};
-    uint32_t lv[4] = {0, 0, 0, 0};
+  const int s = tid >> 6, l = tid & 63;
+  float z[8];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) { pi[t] = lane + 64 * t; v[t] = s_sc[s][pi[t]]; }
-    for (int r = 0; r < rho; ++r) {
-      float bv = -INFINITY;
-      int bp = 0x7FFFFFFF;
+  for (int j = 0; j < 8; ++j) z[j] = s_yq[s * 8 + j];
+  float bv[4];
+  int bp[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (!taken[t] && (v[t] > bv || (v[t] == bv && pi[t] < bp))) { bv = v[t]; bp = pi[t]; }
+  for (int q = 0; q < 4; ++q) {
+    const int p = l * 4 + q;
+    float acc = (p & 1) ? -z[0] : z[0];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int op = __shfl_xor(bp, off);
-        if (ov > bv || (ov == bv && op < bp)) { bv = ov; bp = op; }
+    for (int j = 1; j < 8; ++j) acc = acc + (((p >> j) & 1) ? -z[j] : z[j]);
+    bv[q] = acc;
+    bp[q] = p;
+  }
+  // sort the lane's 4 in (sc desc, p asc) order
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int j = 0; j < 3 - i; ++j)
+      if (better(bv[j + 1], bp[j + 1], bv[j], bp[j])) {
+        const float tv = bv[j]; bv[j] = bv[j + 1]; bv[j + 1] = tv;
+        const int tp = bp[j]; bp[j] = bp[j + 1]; bp[j + 1] = tp;
       }
+  uint32_t lv[4] = {0, 0, 0, 0};
+  for (int r = 0; r < rho; ++r) {
+    float wv = bv[0];
+    int wp = bp[0];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (pi[t] == bp) { taken[t] = true; lv[t] = (uint32_t)tw.w[r]; }
+    for (int off = 1; off < 64; off <<= 1) {
+      const float ov = __shfl_xor(wv, off);
+      const int op = __shfl_xor(wp, off);
+      if (better(ov, op, wv, wp)) { wv = ov; wp = op; }
     }
+    if ((wp >> 2) == l) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) lut_out[((int64_t)bh * 16 + s) * 256 + pi[t]] = (uint8_t)lv[t];
+      for (int q = 0; q < 4; ++q)
+        if ((wp & 3) == q) lv[q] = (uint32_t)tw.w[r];
+    }
+    if (bp[0] == wp) {  // the owner lane drops its head
+      bv[0] = bv[1]; bp[0] = bp[1];
+      bv[1] = bv[2]; bp[1] = bp[2];
+      bv[2] = bv[3]; bp[2] = bp[3];
+      bv[3] = -INFINITY; bp[3] = 0x7FFFFFFF;
+    }
   }
+  reinterpret_cast<uint32_t*>(lut_out + ((int64_t)bh * 16 + s) * 256)[l] =
+      lv[0] | (lv[1] << 8) | (lv[2] << 16) | (lv[3] << 24);
 }
 
 // ---------------------------------------------------------------------------
@@ -267,7 +319,8 @@ __global__ __launch_bounds__(256) void k_qprep(const T* __restrict__ Q, int n_kv
 // sits in LDS; one ds_read_u8 per subspace (each subspace's 256-byte row
 // spans 64 dwords, so a wave's lookups for one subspace conflict at most
 // 2-way).  Writes one score byte per key and a per-chunk histogram of the
-// scores (zeros counted by wave ballot, the rest by LDS atomics).
+// scores (zeros counted by wave ballot, the rest by LDS atomics), stored
+// cumulatively: row[v] = #(score >= v) within the chunk.
 // Grid: (chunks, b*H_kv); chunk = KPT * 256 keys.
 // ---------------------------------------------------------------------------
 template <int KPT>
@@ -279,10 +332,7 @@ __global__ __launch_bounds__(256) void k_scan(const uint4* __restrict__ ids, int
   const int lane = tid & 63, wv = tid >> 6;
   __shared__ uint8_t s_lut[16 * 256];
   __shared__ uint32_t s_hist[4][256];
-  reinterpret_cast<uint4*>(s_lut)[tid] = reinterpret_cast<const uint4*>(lut + (int64_t)bh * 4096)[tid];
-  for (int i = tid; i < 4 * 256; i += 256) (&s_hist[0][0])[i] = 0;
-  __syncthreads();
-
+  // the key loads go out first; the LUT and histogram are set up meanwhile
   const int64_t p0 = (int64_t)chunk * (KPT * 256) + tid;
   const uint4* src = ids + bh * cap + S;
   uint8_t* dst = scores + bh * Epad;
@@ -292,6 +342,9 @@ __global__ __launch_bounds__(256) void k_scan(const uint4* __restrict__ ids, int
     const int64_t p = p0 + t * 256;
     x[t] = (p < E) ? src[p] : make_uint4(0, 0, 0, 0);
   }
+  reinterpret_cast<uint4*>(s_lut)[tid] = reinterpret_cast<const uint4*>(lut + (int64_t)bh * 4096)[tid];
+  for (int i = tid; i < 4 * 256; i += 256) (&s_hist[0][0])[i] = 0;
+  __syncthreads();
   uint32_t zeros = 0;
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
@@ -311,8 +364,29 @@ __global__ __launch_bounds__(256) void k_scan(const uint4* __restrict__ ids, int
   if (lane == 0) s_hist[wv][0] = zeros;
   __syncthreads();
   for (int v = tid; v < nbins; v += 256)
-    chist[((int64_t)bh * chunk_stride + chunk) * nbins + v] =
-        s_hist[0][v] + s_hist[1][v] + s_hist[2][v] + s_hist[3][v];
+    s_hist[0][v] = s_hist[0][v] + s_hist[1][v] + s_hist[2][v] + s_hist[3][v];
+  __syncthreads();
+  // chunk row = #(score >= v) for every v: suffix sums by wave 0, lane l
+  // owning bins 4 l .. 4 l + 3
+  if (wv == 0) {
+    uint32_t h[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = (4 * lane + r < nbins) ? s_hist[0][4 * lane + r] : 0u;
+    const uint32_t loc = h[0] + h[1] + h[2] + h[3];
+    uint32_t inc = loc;  // sum over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t t = __shfl_down(inc, off);
+      if (lane + off < 64) inc += t;
+    }
+    uint32_t ge = inc - loc;
+    uint32_t* row = chist + ((int64_t)bh * chunk_stride + chunk) * nbins;
+#pragma unroll
+    for (int r = 3; r >= 0; --r) {
+      ge += h[r];
+      if (4 * lane + r < nbins) row[4 * lane + r] = ge;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -320,59 +394,66 @@ __global__ __launch_bounds__(256) void k_scan(const uint4* __restrict__ ids, int
 // Candidates = the first C eligible keys in (score desc, index asc) order:
 // T = largest v with #(score >= v) >= C; every key with score > T, plus the
 // first Q = C - #(score > T) keys with score == T in index order.  From the
-// per-chunk histograms: per chunk, the ties before it and the output offset
-// of its first candidate (exclusive scans over chunks).
-// One block per (b, h).  meta[bh] = (T, #gt, Q, C).
+// cumulative per-chunk rows: totals (column sums over the rows read as one
+// flat array), T, then per chunk the ties before it and the output offset of
+// its first candidate (block scans over chunks, 1024 per pass).
+// One 1024-thread block per (b, h).  meta[bh] = (T, #gt, Q, C).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_thresh(const uint32_t* __restrict__ chist, int chunk_stride,
-                                                int nchunks, int nbins, int64_t C,
-                                                int32_t* __restrict__ meta, uint32_t* __restrict__ coff) {
+__global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ chist, int chunk_stride,
+                                                 int nchunks, int nbins, int64_t C,
+                                                 int32_t* __restrict__ meta, uint32_t* __restrict__ coff) {
   const int bh = blockIdx.x, tid = threadIdx.x;
-  __shared__ uint32_t s_tot[256];
+  __shared__ uint32_t s_tot[257];
   __shared__ int s_T;
-  __shared__ uint32_t s_gt;
-  __shared__ uint2 s_w[4];
+  __shared__ uint2 s_w[16];
   const uint32_t* hb = chist + (int64_t)bh * chunk_stride * nbins;
-  for (int v = tid; v < nbins; v += 256) {
-    uint32_t acc = 0;
-    for (int c = 0; c < nchunks; ++c) acc += hb[(int64_t)c * nbins + v];
-    s_tot[v] = acc;
+  for (int v = tid; v < 257; v += 1024) s_tot[v] = 0;
+  __syncthreads();
+  {
+    // column sums over the chunks: flat, coalesced reads, 8 in flight per thread
+    const int nw = nchunks * nbins;
+    for (int w0 = 0; w0 < nw; w0 += 8 * 1024) {
+      uint32_t val[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int w = w0 + r * 1024 + tid;
+        val[r] = (w < nw) ? hb[w] : 0u;
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int w = w0 + r * 1024 + tid;
+        if (w < nw && val[r]) atomicAdd(&s_tot[w % nbins], val[r]);
+      }
+    }
   }
   __syncthreads();
-  if (tid == 0) {
-    uint64_t cum = 0;
-    int T = 0;
-    for (int v = nbins - 1; v >= 0; --v) {
-      if (cum + s_tot[v] >= (uint64_t)C) { T = v; break; }
-      cum += s_tot[v];
-    }
-    s_T = T;
-    s_gt = (uint32_t)cum;
-    meta[bh * 4 + 0] = T;
-    meta[bh * 4 + 1] = (int32_t)cum;
-    meta[bh * 4 + 2] = (int32_t)(C - (int64_t)cum);
+  if (tid < nbins && (int64_t)s_tot[tid] >= C && (int64_t)s_tot[tid + 1] < C) {
+    s_T = tid;
+    meta[bh * 4 + 0] = tid;
+    meta[bh * 4 + 1] = (int32_t)s_tot[tid + 1];
+    meta[bh * 4 + 2] = (int32_t)(C - (int64_t)s_tot[tid + 1]);
     meta[bh * 4 + 3] = (int32_t)C;
   }
   __syncthreads();
   const int T = s_T;
-  const int64_t Q = C - (int64_t)s_gt;
+  const int64_t Q = C - (int64_t)s_tot[T + 1];
   uint32_t carry_tie = 0, carry_off = 0;
-  for (int c0 = 0; c0 < nchunks; c0 += 256) {
+  for (int c0 = 0; c0 < nchunks; c0 += 1024) {
     const int c = c0 + tid;
     uint32_t gt = 0, eq = 0;
     if (c < nchunks) {
       const uint32_t* hc = hb + (int64_t)c * nbins;
-      for (int v = T + 1; v < nbins; ++v) gt += hc[v];
-      eq = hc[T];
+      gt = (T + 1 < nbins) ? hc[T + 1] : 0u;
+      eq = hc[T] - gt;
     }
     uint2 tot;
-    const uint2 ex = block_exscan2<256>(make_uint2(eq, 0), s_w, tot);
+    const uint2 ex = block_exscan2<1024>(make_uint2(eq, 0), s_w, tot);
     const uint32_t tie_before = carry_tie + ex.x;
     int64_t quota = Q - (int64_t)tie_before;
     if (quota < 0) quota = 0;
     const uint32_t sel = gt + (uint32_t)((int64_t)eq < quota ? eq : quota);
     uint2 tot2;
-    const uint2 ex2 = block_exscan2<256>(make_uint2(sel, 0), s_w, tot2);
+    const uint2 ex2 = block_exscan2<1024>(make_uint2(sel, 0), s_w, tot2);
     if (c < nchunks) {
       coff[((int64_t)bh * chunk_stride + c) * 2 + 0] = carry_off + ex2.x;
       coff[((int64_t)bh * chunk_stride + c) * 2 + 1] = tie_before;
@@ -383,43 +464,20 @@ __global__ __launch_bounds__(256) void k_thresh(const uint32_t* __restrict__ chi
 }
 
 // ---------------------------------------------------------------------------
-// K4b + K5 compact and rerank.  Ordered compaction of this chunk's
-// candidates (see K4a), then [TS] Candidate Reranking (RSQ-IP) "Estimation"
-// for each: est = sum_b w_b <v_b, yq_b>, evaluated in fp32 as
+// K4b + K5 compact and rerank.  Ordered compaction of two consecutive
+// chunks' candidates (see K4a), then [TS] Candidate Reranking (RSQ-IP)
+// "Estimation" for each: est = sum_b w_b <v_b, yq_b>, evaluated in fp32 as
 //   est = 0; for b: { p = 0; for j: p = p + fl(v_{b,j} yq_{b,j}); est = est + fl(w_b p) }
-// The products fl(v yq) for all 16 codes of each coordinate are tabulated in
-// LDS (fl(-L yq) = -fl(L yq) exactly), so each coordinate costs one LDS read
-// and one add in the stated order.  Reads 64 B of codes + 32 B of w per
-// candidate; writes (position, estimate) at the candidate's rank in
-// ascending-position order.  Grid (chunks, b*H_kv), same chunking as K3.
+// The products fl(v yq) for all 16 codes of each coordinate come from the
+// table K2 wrote (fl(-L yq) = -fl(L yq) exactly), staged in LDS, so each
+// coordinate costs one LDS read and one add in the stated order.  Reads the
+// candidate's 128-byte record (96 B used); writes (position, estimate) at the
+// candidate's rank in ascending-position order, and the block's estimate
+// range (order keys) for K6.  Grid (ceil(chunks / 2), b*H_kv): two chunks per
+// block keep every block resident in one round.
 // ---------------------------------------------------------------------------
 template <int KPT>
-__global__ __launch_bounds__(256) void k_compact_rerank(
-    const uint8_t* __restrict__ scores, int64_t Epad, int64_t S, int64_t E,
-    const int32_t* __restrict__ meta, const uint32_t* __restrict__ coff, int chunk_stride,
-    const float* __restrict__ yq, const uint4* __restrict__ nib, const uint4* __restrict__ wq,
-    int64_t cap, int32_t* __restrict__ cand, float* __restrict__ est, int64_t cstride,
-    int64_t C) {
-  constexpr int CH = KPT * 256;
-  const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
-  __shared__ float s_P[128 * 16];
-  __shared__ uint16_t s_list[CH];
-  __shared__ uint2 s_w[4];
-  for (int e = tid; e < 2048; e += 256) {
-    const int j = e >> 4, code = e & 15;
-    const float pr = c_levels[code & 7] * yq[(int64_t)bh * 128 + j];
-    s_P[e] = (code & 8) ? -pr : pr;
-  }
-  const int T = meta[bh * 4 + 0];
-  const int64_t Q = meta[bh * 4 + 2];
-  const uint32_t off_c = coff[((int64_t)bh * chunk_stride + chunk) * 2 + 0];
-  const uint32_t tieb_c = coff[((int64_t)bh * chunk_stride + chunk) * 2 + 1];
-  int64_t quota = Q - (int64_t)tieb_c;
-  if (quota < 0) quota = 0;
-
-  const int64_t pbase = (int64_t)chunk * CH + tid * KPT;
-  const uint8_t* sp = scores + bh * Epad + pbase;
-  uint8_t sc[KPT];
+__device__ __forceinline__ void load_scores(const uint8_t* sp, uint8_t (&sc)[KPT]) {
   if constexpr (KPT == 16) {
     const uint4 v = *reinterpret_cast<const uint4*>(sp);
     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
@@ -437,84 +495,178 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
 #pragma unroll
     for (int t = 0; t < KPT; ++t) sc[t] = sp[t];
   }
-  uint32_t ngt = 0, neq = 0;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(256) void k_compact_rerank(
+    const uint8_t* __restrict__ scores, int64_t Epad, int64_t S, int64_t E,
+    const int32_t* __restrict__ meta, const uint32_t* __restrict__ coff, int chunk_stride,
+    int nchunks, const float* __restrict__ ptab, const uint32_t* __restrict__ rec,
+    int64_t cap, int32_t* __restrict__ cand,
+    float* __restrict__ est, int64_t cstride, int64_t C, uint32_t* __restrict__ mm) {
+  constexpr int CH = KPT * 256;
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int c0 = blockIdx.x * 2;
+  const int nc = (c0 + 1 < nchunks) ? 2 : 1;
+  __shared__ float s_P[128 * 16];
+  __shared__ uint16_t s_list[2 * CH];
+  __shared__ uint2 s_w[4];
+  __shared__ uint32_t s_mm[8];
+  // global reads first
+  const int T = meta[bh * 4 + 0];
+  const int64_t Q = meta[bh * 4 + 2];
+  uint32_t off_c[2], tieb_c[2];
+  uint8_t sc[2][KPT];
 #pragma unroll
-  for (int t = 0; t < KPT; ++t) {
-    const bool valid = pbase + t < E;
-    ngt += (valid && sc[t] > T) ? 1u : 0u;
-    neq += (valid && sc[t] == T) ? 1u : 0u;
+  for (int h = 0; h < 2; ++h) {
+    const int chunk = c0 + (h < nc ? h : 0);
+    off_c[h] = coff[((int64_t)bh * chunk_stride + chunk) * 2 + 0];
+    tieb_c[h] = coff[((int64_t)bh * chunk_stride + chunk) * 2 + 1];
+    load_scores<KPT>(scores + bh * Epad + (int64_t)chunk * CH + tid * KPT, sc[h]);
   }
-  uint2 tot;
-  const uint2 ex = block_exscan2<256>(make_uint2(ngt, neq), s_w, tot);
-  uint32_t pos = ex.x + (uint32_t)((int64_t)ex.y < quota ? ex.y : quota);
-  uint32_t tie_seen = ex.y;
+  {
+    const uint4* pt = reinterpret_cast<const uint4*>(ptab + (int64_t)bh * 2048);
+    reinterpret_cast<uint4*>(s_P)[tid] = pt[tid];
+    reinterpret_cast<uint4*>(s_P)[tid + 256] = pt[tid + 256];
+  }
+  uint32_t nsel[2];
 #pragma unroll
-  for (int t = 0; t < KPT; ++t) {
-    const bool valid = pbase + t < E;
-    bool sel = false;
-    if (valid) {
-      if (sc[t] > T) sel = true;
-      else if (sc[t] == T) { sel = (int64_t)tie_seen < quota; ++tie_seen; }
+  for (int h = 0; h < 2; ++h) {
+    if (h >= nc) { nsel[h] = 0; continue; }  // uniform across the block
+    const int64_t pbase = (int64_t)(c0 + h) * CH + tid * KPT;
+    int64_t quota = Q - (int64_t)tieb_c[h];
+    if (quota < 0) quota = 0;
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) {
+      const bool valid = pbase + t < E;
+      ngt += (valid && sc[h][t] > T) ? 1u : 0u;
+      neq += (valid && sc[h][t] == T) ? 1u : 0u;
     }
-    if (sel) s_list[pos++] = (uint16_t)(tid * KPT + t);
+    uint2 tot;
+    const uint2 ex = block_exscan2<256>(make_uint2(ngt, neq), s_w, tot);
+    uint32_t pos = (h ? nsel[0] : 0u) + ex.x + (uint32_t)((int64_t)ex.y < quota ? ex.y : quota);
+    uint32_t tie_seen = ex.y;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) {
+      const bool valid = pbase + t < E;
+      bool sel = false;
+      if (valid) {
+        if (sc[h][t] > T) sel = true;
+        else if (sc[h][t] == T) { sel = (int64_t)tie_seen < quota; ++tie_seen; }
+      }
+      if (sel) s_list[pos++] = (uint16_t)((h << 14) | (tid * KPT + t));
+    }
+    nsel[h] = tot.x + (uint32_t)((int64_t)tot.y < quota ? tot.y : quota);
   }
-  const uint32_t nsel = tot.x + (uint32_t)((int64_t)tot.y < quota ? tot.y : quota);
   __syncthreads();
 
-  for (uint32_t j = tid; j < nsel; j += 256) {
-    const int64_t i = S + (int64_t)chunk * CH + s_list[j];
-    const uint4* np = nib + (bh * cap + i) * 4;
-    const uint4* wp = wq + (bh * cap + i) * 2;
-    const uint4 n0 = np[0], n1 = np[1], n2 = np[2], n3 = np[3];
-    const uint4 w0 = wp[0], w1 = wp[1];
-    const uint32_t cw[16] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w,
-                             n2.x, n2.y, n2.z, n2.w, n3.x, n3.y, n3.z, n3.w};
-    const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    float e = 0.0f;
+  const uint32_t ntot = nsel[0] + nsel[1];
+  // 4 lanes per candidate: lane q of the group reads codes of subspaces
+  // 4q..4q+3 (16 B) and their w (8 B) from the candidate's 128-byte record,
+  // forms w_b p_b for them, and the running sum is handed from lane to lane
+  // so est accumulates b = 0, 1, ..., 15 in order.
+  const int q = tid & 3;
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;  // order keys of this block's estimates
+  for (uint32_t j0 = 0; j0 < ntot; j0 += 64) {
+    const uint32_t j = j0 + (tid >> 2);
+    const bool has = j < ntot;
+    const uint32_t ent = has ? s_list[j] : 0u;
+    const int h = (int)(ent >> 14);
+    const int64_t i = S + (int64_t)(c0 + h) * CH + (ent & 0x3FFFu);
+    const uint32_t* rp = rec + (bh * cap + i) * 32;
+    uint4 cw = make_uint4(0, 0, 0, 0);
+    uint2 ww = make_uint2(0, 0);
+    if (has) {
+      cw = reinterpret_cast<const uint4*>(rp)[q];
+      ww = reinterpret_cast<const uint2*>(rp + 16)[q];
+    }
+    const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+    float t[4];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
+    for (int bb = 0; bb < 4; ++bb) {
+      const int b = 4 * q + bb;
       float p = 0.0f;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) p = p + s_P[(b * 8 + jj) * 16 + ((cw[b] >> (4 * jj)) & 15u)];
-      const uint16_t hb = (uint16_t)(ww[b >> 1] >> ((b & 1) * 16));
-      const float wf = (float)__builtin_bit_cast(_Float16, hb);
-      e = e + wf * p;
+      for (int jj = 0; jj < 8; ++jj) p = p + s_P[(b * 8 + jj) * 16 + ((cws[bb] >> (4 * jj)) & 15u)];
+      const uint16_t hb = (uint16_t)(((bb < 2) ? ww.x : ww.y) >> ((bb & 1) * 16));
+      t[bb] = (float)__builtin_bit_cast(_Float16, hb) * p;
     }
-    if ((int64_t)off_c + j < C) {  // always true when K4a and this kernel agree
-      cand[bh * cstride + off_c + j] = (int32_t)i;
-      est[bh * cstride + off_c + j] = e;
+    float e = 0.0f;
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      if (q == step) e = (((e + t[0]) + t[1]) + t[2]) + t[3];
+      e = __shfl(e, (tid & 63 & ~3) + step);
     }
+    if (has) {
+      if (q == 0) {
+        const uint32_t o = (h ? off_c[1] + (j - nsel[0]) : off_c[0] + j);
+        if ((int64_t)o < C) {  // always true when K4a and this kernel agree
+          cand[bh * cstride + o] = (int32_t)i;
+          est[bh * cstride + o] = e;
+        }
+      }
+      const uint32_t ok = order_key(e);
+      kmn = min(kmn, ok);
+      kmx = max(kmx, ok);
+    }
+  }
+  // this block's estimate range (order keys; no candidates: max key 0 < min)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, off));
+    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, off));
+  }
+  if ((tid & 63) == 0) { s_mm[tid >> 6] = kmn; s_mm[4 + (tid >> 6)] = kmx; }
+  __syncthreads();
+  if (tid < 2) {
+    const int chunk = c0 + (tid < nc ? tid : 0);
+    mm[((int64_t)bh * chunk_stride + chunk) * 2 + 0] = min(min(s_mm[0], s_mm[1]), min(s_mm[2], s_mm[3]));
+    mm[((int64_t)bh * chunk_stride + chunk) * 2 + 1] = max(max(s_mm[4], s_mm[5]), max(s_mm[6], s_mm[7]));
   }
 }
 
 // ---------------------------------------------------------------------------
 // K6 exact top-k over the reranked candidates ([TS] Key Contributions 2:
 // Top-k selection on the compressed codes).  Order: (est desc, position asc),
-// -0 == +0.  Radix select of the k'-th largest order key (11 + 11 + 10 bits,
-// LDS histograms), then an ordered compaction: keys above the threshold plus
-// the first `remaining` ties in position order, written after the S sinks
-// in ascending position order.  One 1024-thread block per (b, h).
+// -0 == +0.  Two kernels over blocks of TK_SL candidates, no atomics on
+// global memory and no cross-block waiting:
+//  * k_topk_hist: every block reduces the per-chunk estimate ranges that
+//    K4b+K5 wrote to this (b, h)'s minimum and maximum, bins its candidates
+//    linearly between them (fp32: bin = min(2047, trunc((e - min) * 2047 /
+//    (max - min))), monotone non-decreasing in e, -0 and +0 alike) and writes
+//    a cumulative row #(bin >= b).
+//  * k_topk_select: every block sums the rows, finds the bin b1 holding rank
+//    k', gathers b1's members (usually a few dozen; the counting sort in
+//    k_topk_hist left each block's members contiguous), ranks them exactly
+//    by (est desc, position asc) and keeps the first `remaining` -- the same
+//    result in every block -- then writes its own selected candidates (bin >
+//    b1, or a kept member of b1) in position order at its offset, after the
+//    sinks.  A bin with more than TK_MAXMEM members is resolved instead by a
+//    whole-(b, h) radix select in block 0.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (f == 0.0f) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+constexpr int TK_SL = kTopkSlice;           // candidates per block (1024 threads x 4)
+constexpr int TK_MAXMEM = kTopkMaxMembers;  // largest threshold bin ranked pairwise
+
+__device__ __forceinline__ void range_scale(uint32_t kmin, uint32_t kmax, float& fmin,
+                                            float& scale) {
+  fmin = key_float(kmin);
+  const float fmax = key_float(kmax);
+  scale = (fmax > fmin) ? 2047.0f / (fmax - fmin) : 0.0f;
+  if (!(scale < INFINITY)) scale = 0.0f;
+}
+__device__ __forceinline__ uint32_t est_bin(float f, float fmin, float scale) {
+  return (uint32_t)fminf((f - fmin) * scale, 2047.0f);
 }
 
-__global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ est,
-                                               const int32_t* __restrict__ cand, int64_t cstride,
-                                               int C, int kprime, int S, int k,
-                                               int32_t* __restrict__ out_idx,
-                                               float* __restrict__ out_est) {
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const float* e = est + bh * cstride;
-  const int32_t* cd = cand + bh * cstride;
-  int32_t* oi = out_idx + (int64_t)bh * k;
-  __shared__ uint32_t s_hist[2048];
-  __shared__ uint2 s_w[16];
-  __shared__ uint32_t s_digit, s_rem;
+// Whole-(b, h) exact selection by an 11 + 11 + 10-bit radix select of the
+// order keys, for 1024 threads; writes sinks, positions and estimates.
+__device__ void topk_radix_block(const float* __restrict__ e, const int32_t* __restrict__ cd,
+                                 int C, int kprime, int S, int32_t* __restrict__ oi,
+                                 float* __restrict__ oe, uint32_t* s_hist, uint2* s_w,
+                                 uint32_t* s_sel) {
+  const int tid = threadIdx.x;
   for (int t = tid; t < S; t += 1024) oi[t] = t;
-
   uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)kprime;
   const int shifts[3] = {21, 10, 0};
   const int widths[3] = {11, 11, 10};
@@ -527,7 +679,6 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ est,
       if ((o & pmask) == prefix) atomicAdd(&s_hist[(o >> sh) & (nb - 1)], 1u);
     }
     __syncthreads();
-    // bins in descending order; thread t owns bins nb-1-bpt*t ... (bpt bins)
     const int bpt = nb / 1024;
     uint32_t mine = 0;
     for (int q = 0; q < bpt; ++q) mine += s_hist[nb - 1 - (tid * bpt + q)];
@@ -537,20 +688,16 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ est,
     for (int q = 0; q < bpt; ++q) {
       const int bin = nb - 1 - (tid * bpt + q);
       const uint32_t cnt = s_hist[bin];
-      if (above < remaining && remaining <= above + cnt) {
-        s_digit = (uint32_t)bin;
-        s_rem = remaining - above;
-      }
+      if (above < remaining && remaining <= above + cnt) { s_sel[0] = bin; s_sel[1] = remaining - above; }
       above += cnt;
     }
     __syncthreads();
-    prefix |= s_digit << sh;
+    prefix |= s_sel[0] << sh;
     pmask |= (uint32_t)(nb - 1) << sh;
-    remaining = s_rem;
+    remaining = s_sel[1];
     __syncthreads();
   }
   const uint32_t thr = prefix;
-  // ordered compaction over contiguous per-thread ranges
   const int per = (C + 1023) / 1024;
   const int c0 = tid * per;
   const int c1 = (c0 + per < C) ? c0 + per : C;
@@ -571,7 +718,223 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ est,
     if (o == thr) { sel = tie_seen < remaining; ++tie_seen; }
     if (sel && pos < (uint32_t)kprime) {  // bound holds by construction
       oi[S + pos] = cd[c];
-      if (out_est) out_est[(int64_t)bh * kprime + pos] = ev;
+      if (oe) oe[pos] = ev;
+      ++pos;
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_topk_hist(
+    const float* __restrict__ est, int64_t cstride, int C, int P,
+    const uint32_t* __restrict__ mmc, int chunk_stride, int nchunks,
+    uint32_t* __restrict__ rows, uint32_t* __restrict__ range, uint2* __restrict__ sorted) {
+  const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const float* e = est + bh * cstride;
+  __shared__ uint32_t s_hist[2048];
+  __shared__ uint2 s_w[16];
+  __shared__ uint32_t s_r[32];
+  // this (b, h)'s estimate range from the per-chunk ranges
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  const uint32_t* mb = mmc + (int64_t)bh * chunk_stride * 2;
+  for (int c = tid; c < nchunks; c += 1024) {
+    kmin = min(kmin, mb[2 * c]);
+    kmax = max(kmax, mb[2 * c + 1]);
+  }
+  for (int i = tid; i < 2048; i += 1024) s_hist[i] = 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  if ((tid & 63) == 0) { s_r[tid >> 6] = kmin; s_r[16 + (tid >> 6)] = kmax; }
+  __syncthreads();
+  kmin = s_r[0];
+  kmax = s_r[16];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) { kmin = min(kmin, s_r[w]); kmax = max(kmax, s_r[16 + w]); }
+  if (p == 0 && tid == 0) { range[2 * bh] = kmin; range[2 * bh + 1] = kmax; }
+  float fmin, scale;
+  range_scale(kmin, kmax, fmin, scale);
+  const int c0 = p * TK_SL + tid * 4;
+  float f[4];
+  if (c0 + 3 < C) {
+    const float4 t = *reinterpret_cast<const float4*>(e + c0);
+    f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[r] = (c0 + r < C) ? e[c0 + r] : 0.0f;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (c0 + r < C) atomicAdd(&s_hist[est_bin(f[r], fmin, scale)], 1u);
+  __syncthreads();
+  // cumulative row #(bin >= b); thread t owns bins 2047 - 2t and 2046 - 2t
+  const uint32_t hh = s_hist[2047 - 2 * tid], hl = s_hist[2046 - 2 * tid];
+  uint2 tot;
+  const uint2 ex = block_exscan2<1024>(make_uint2(hh + hl, 0), s_w, tot);
+  uint32_t* row = rows + ((int64_t)bh * P + p) * 2048;
+  row[2047 - 2 * tid] = ex.x + hh;
+  row[2046 - 2 * tid] = ex.x + hh + hl;
+  // counting sort of the block's candidates by bin, descending: bin b's
+  // entries start at #(bin > b), so a bin's members are contiguous
+  s_hist[2047 - 2 * tid] = ex.x;
+  s_hist[2046 - 2 * tid] = ex.x + hh;
+  __syncthreads();
+  uint2* out = sorted + ((int64_t)bh * P + p) * TK_SL;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (c0 + r < C) {
+      const uint32_t slot = atomicAdd(&s_hist[est_bin(f[r], fmin, scale)], 1u);
+      out[slot] = make_uint2(order_key(f[r]), (uint32_t)(c0 + r));
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_topk_select(
+    const float* __restrict__ est, const int32_t* __restrict__ cand, int64_t cstride, int C,
+    int kprime, int S, int k, int P, const uint32_t* __restrict__ range,
+    const uint32_t* __restrict__ rows, const uint2* __restrict__ sorted,
+    int32_t* __restrict__ tkmeta, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
+  const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const float* e = est + bh * cstride;
+  const int32_t* cd = cand + bh * cstride;
+  int32_t* oi = out_idx + (int64_t)bh * k;
+  __shared__ uint32_t s_hist[2049];
+  __shared__ uint32_t s_mk[TK_MAXMEM];
+  __shared__ uint32_t s_mc[TK_MAXMEM];
+  __shared__ uint32_t s_pref[1024];
+  __shared__ uint32_t s_start[1024];
+  __shared__ uint32_t s_bits[TK_SL / 32];
+  __shared__ uint2 s_w[16];
+  __shared__ uint32_t s_sel[4];
+  // this block's candidates: loads go out first
+  const int c0 = p * TK_SL + tid * 4;
+  float f[4];
+  int32_t ci[4];
+  if (c0 + 3 < C) {
+    const float4 t = *reinterpret_cast<const float4*>(e + c0);
+    const int4 u = *reinterpret_cast<const int4*>(cd + c0);
+    f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w;
+    ci[0] = u.x; ci[1] = u.y; ci[2] = u.z; ci[3] = u.w;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      f[r] = (c0 + r < C) ? e[c0 + r] : 0.0f;
+      ci[r] = (c0 + r < C) ? cd[c0 + r] : 0;
+    }
+  }
+  // resolve (every block of this (b, h) does it, identically): the bin b1
+  // holding rank k' and the kept members of b1
+  const uint32_t* rb = rows + (int64_t)bh * P * 2048;
+  for (int b = tid; b < 2048; b += 1024) {
+    uint32_t acc = 0;
+    for (int q0 = 0; q0 < P; q0 += 8) {  // 8 rows in flight
+      uint32_t v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = (q0 + r < P) ? rb[(int64_t)(q0 + r) * 2048 + b] : 0u;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc += v[r];
+    }
+    s_hist[b] = acc;
+  }
+  if (tid == 0) { s_hist[2048] = 0; s_sel[2] = 0; s_sel[3] = 0; }
+  if (tid < TK_SL / 32) s_bits[tid] = 0;
+  __syncthreads();
+  for (int b = tid; b < 2048; b += 1024)
+    if (s_hist[b] >= (uint32_t)kprime && s_hist[b + 1] < (uint32_t)kprime) s_sel[0] = b;
+  __syncthreads();
+  const uint32_t b1 = s_sel[0];
+  const uint32_t above_tot = s_hist[b1 + 1];
+  const uint32_t M = s_hist[b1] - above_tot;
+  const uint32_t remaining = (uint32_t)kprime - above_tot;
+  if (M > (uint32_t)TK_MAXMEM) {
+    // tie-heavy threshold bin: block 0 selects exactly for the whole (b, h)
+    if (p == 0) {
+      __syncthreads();
+      topk_radix_block(e, cd, C, kprime, S, oi,
+                       out_est ? out_est + (int64_t)bh * kprime : nullptr, s_hist, s_w, s_sel);
+    }
+    if (p == 0 && tid == 0) {
+      tkmeta[bh * 4 + 0] = (int32_t)b1;
+      tkmeta[bh * 4 + 1] = (int32_t)remaining;
+      tkmeta[bh * 4 + 2] = 1;
+      tkmeta[bh * 4 + 3] = (int32_t)M;
+    }
+    return;
+  }
+  // gather b1's members: block q holds them contiguously in its sorted array
+  // from #(bin > b1) on; also the rows-above counts of the blocks before p
+  uint32_t above_before = 0;
+  {
+    const int q = tid;
+    uint32_t nq = 0, sq = 0;
+    if (q < P) {
+      sq = (b1 + 1 < 2048) ? rb[(int64_t)q * 2048 + b1 + 1] : 0u;
+      nq = rb[(int64_t)q * 2048 + b1] - sq;
+    }
+    uint2 tt;
+    const uint2 ex = block_exscan2<1024>(make_uint2(nq, q < p ? sq : 0u), s_w, tt);
+    s_pref[q] = ex.x;
+    s_start[q] = sq;
+    above_before = tt.y;
+  }
+  __syncthreads();
+  for (uint32_t j = tid; j < M; j += 1024) {
+    int lo = 0, hi = P - 1;  // last block q with s_pref[q] <= j
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    const uint2 pr = sorted[((int64_t)bh * P + lo) * TK_SL + s_start[lo] + (j - s_pref[lo])];
+    s_mk[j] = pr.x;
+    s_mc[j] = pr.y;
+  }
+  __syncthreads();
+  // rank the members by (est desc, position asc); keep the first `remaining`
+  for (uint32_t j = tid; j < M; j += 1024) {
+    const uint32_t kj = s_mk[j], cj = s_mc[j];
+    uint32_t rank = 0;
+    for (uint32_t q = 0; q < M; ++q) {
+      const uint32_t kq = s_mk[q], cq = s_mc[q];
+      rank += (kq > kj || (kq == kj && cq < cj)) ? 1u : 0u;
+    }
+    if (rank < remaining) {
+      const uint32_t qb = cj / TK_SL;
+      if (qb < (uint32_t)p) atomicAdd(&s_sel[3], 1u);
+      else if (qb == (uint32_t)p) atomicOr(&s_bits[(cj % TK_SL) >> 5], 1u << (cj & 31));
+    }
+  }
+  __syncthreads();
+  if (p == 0) {
+    for (int t = tid; t < S; t += 1024) oi[t] = t;
+    if (tid == 0) {
+      tkmeta[bh * 4 + 0] = (int32_t)b1;
+      tkmeta[bh * 4 + 1] = (int32_t)remaining;
+      tkmeta[bh * 4 + 2] = 0;
+      tkmeta[bh * 4 + 3] = (int32_t)M;
+    }
+  }
+  // ordered compaction of this block's selection at its offset
+  float fmin, scale;
+  range_scale(range[2 * bh], range[2 * bh + 1], fmin, scale);
+  uint32_t selm = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int c = c0 + r;
+    if (c < C) {
+      const uint32_t bn = est_bin(f[r], fmin, scale);
+      if (bn > b1 || (bn == b1 && ((s_bits[(c % TK_SL) >> 5] >> (c & 31)) & 1u)))
+        selm |= 1u << r;
+    }
+  }
+  uint2 tot;
+  const uint2 ex = block_exscan2<1024>(make_uint2((uint32_t)__popc(selm), 0), s_w, tot);
+  uint32_t pos = above_before + s_sel[3] + ex.x;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (((selm >> r) & 1u) && pos < (uint32_t)kprime) {  // bound holds by construction
+      oi[S + pos] = ci[r];
+      if (out_est) out_est[(int64_t)bh * kprime + pos] = f[r];
       ++pos;
     }
   }
@@ -671,18 +1034,43 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, con
 }
 
 // K8 log-sum-exp merge of the split-K partials -> output row per query head.
+// The block stages its (m, l) pairs in LDS first (one coalesced pass), so the
+// per-element loop reads LDS, not dependent global loads.
 template <typename T>
 __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part, int nch,
                                                     T* __restrict__ out) {
   const int bq = blockIdx.x, j = threadIdx.x;
   const float* pp = part + (int64_t)bq * nch * 130;
-  float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, pp[c * 130 + 128]);
+  __shared__ float s_f[2048];
+  __shared__ float s_l[2048];
+  __shared__ float s_red[2];
   float o = 0.0f, l = 0.0f;
-  for (int c = 0; c < nch; ++c) {
-    const float f = exp2f(pp[c * 130 + 128] - M);
-    o = __builtin_fmaf(f, pp[c * 130 + j], o);
-    l = __builtin_fmaf(f, pp[c * 130 + 129], l);
+  // running maximum over tiles of up to 2048 chunks
+  float M = -INFINITY;
+  for (int t0 = 0; t0 < nch; t0 += 2048) {
+    const int nt = min(2048, nch - t0);
+    for (int c = j; c < nt; c += 128) {
+      s_f[c] = pp[(int64_t)(t0 + c) * 130 + 128];
+      s_l[c] = pp[(int64_t)(t0 + c) * 130 + 129];
+    }
+    __syncthreads();
+    float tm = -INFINITY;
+    for (int c = j; c < nt; c += 128) tm = fmaxf(tm, s_f[c]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) tm = fmaxf(tm, __shfl_xor(tm, off));
+    if ((j & 63) == 0) s_red[j >> 6] = tm;
+    __syncthreads();
+    const float Mn = fmaxf(M, fmaxf(s_red[0], s_red[1]));
+    const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+    o *= r;
+    l *= r;
+    M = Mn;
+    for (int c = 0; c < nt; ++c) {
+      const float f = exp2f(s_f[c] - M);
+      o = __builtin_fmaf(f, pp[(int64_t)(t0 + c) * 130 + j], o);
+      l = __builtin_fmaf(f, s_l[c], l);
+    }
+    __syncthreads();
   }
   const float r = o / l;
   if constexpr (sizeof(T) == 2) {
@@ -709,27 +1097,28 @@ static hipError_t launch(F kernel, dim3 grid, dim3 block, hipStream_t st, const 
 }
 
 hipError_t launch_encode(int dtype, const void* K, int64_t rows_per_head, int64_t lo, int64_t n,
-                         int BH, int64_t cap, uint8_t* ids, uint32_t* nib, uint16_t* wq,
-                         const SignMask& sg, float c, hipStream_t st, const EvPair& ev) {
+                         int BH, int64_t cap, uint8_t* ids, uint32_t* rec, const SignMask& sg,
+                         float c, hipStream_t st, const EvPair& ev) {
   const int64_t total = (int64_t)BH * n;
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)((total + 15) / 16));
   if (dtype == 0)
     return launch(k_encode<uint16_t>, grid, dim3(256), st, ev, (const uint16_t*)K,
-                  rows_per_head, lo, n, total, cap, ids, nib, wq, sg, c);
+                  rows_per_head, lo, n, total, cap, ids, rec, sg, c);
   return launch(k_encode<float>, grid, dim3(256), st, ev, (const float*)K, rows_per_head, lo, n,
-                total, cap, ids, nib, wq, sg, c);
+                total, cap, ids, rec, sg, c);
 }
 
 hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
                         const SignMask& sg, float c, int rho, const Tiers& tw, uint8_t* lut,
-                        float* yq, hipStream_t st, const EvPair& ev) {
+                        float* yq, float* ptab, const AppendJob& app, hipStream_t st,
+                        const EvPair& ev) {
   const float invG = 1.0f / (float)G;
   if (dtype == 0)
-    return launch(k_qprep<uint16_t>, dim3(BH), dim3(256), st, ev, (const uint16_t*)Q,
-                  n_kv_heads, G, invG, sg, c, rho, tw, lut, yq);
-  return launch(k_qprep<float>, dim3(BH), dim3(256), st, ev, (const float*)Q, n_kv_heads, G,
-                invG, sg, c, rho, tw, lut, yq);
+    return launch(k_qprep<uint16_t>, dim3(BH), dim3(1024), st, ev, (const uint16_t*)Q,
+                  n_kv_heads, G, invG, sg, c, rho, tw, lut, yq, ptab, app);
+  return launch(k_qprep<float>, dim3(BH), dim3(1024), st, ev, (const float*)Q, n_kv_heads, G,
+                invG, sg, c, rho, tw, lut, yq, ptab, app);
 }
 
 hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t cap, int64_t S,
@@ -752,24 +1141,22 @@ hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t
 hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nchunks, int nbins,
                          int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st,
                          const EvPair& ev) {
-  return launch(k_thresh, dim3(BH), dim3(256), st, ev, chist, chunk_stride, nchunks, nbins, C,
+  return launch(k_thresh, dim3(BH), dim3(1024), st, ev, chist, chunk_stride, nchunks, nbins, C,
                 meta, coff);
 }
 
 hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* scores,
                                  int64_t Epad, int64_t S, int64_t E, const int32_t* meta,
-                                 const uint32_t* coff, int chunk_stride, const float* yq,
-                                 const uint32_t* nib, const uint16_t* wq, int64_t cap,
-                                 int32_t* cand, float* est, int64_t cstride, int64_t C,
-                                 hipStream_t st, const EvPair& ev) {
-  const dim3 grid(nchunks, BH);
-  const uint4* n4 = (const uint4*)nib;
-  const uint4* w4 = (const uint4*)wq;
+                                 const uint32_t* coff, int chunk_stride, const float* ptab,
+                                 const uint32_t* rec, int64_t cap, int32_t* cand, float* est,
+                                 int64_t cstride, int64_t C, uint32_t* mm, hipStream_t st,
+                                 const EvPair& ev) {
+  const dim3 grid((nchunks + 1) / 2, BH);
   switch (kpt) {
 #define PKV_CR(K)                                                                            \
   case K:                                                                                    \
     return launch(k_compact_rerank<K>, grid, dim3(256), st, ev, scores, Epad, S, E, meta,    \
-                  coff, chunk_stride, yq, n4, w4, cap, cand, est, cstride, C);
+                  coff, chunk_stride, nchunks, ptab, rec, cap, cand, est, cstride, C, mm);
     PKV_CR(1) PKV_CR(2) PKV_CR(4) PKV_CR(8) PKV_CR(16)
 #undef PKV_CR
     default: return hipErrorInvalidValue;
@@ -777,9 +1164,16 @@ hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* sc
 }
 
 hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cstride, int C,
-                       int kprime, int S, int k, int32_t* out_idx, float* out_est,
-                       hipStream_t st, const EvPair& ev) {
-  return launch(k_topk, dim3(BH), dim3(1024), st, ev, est, cand, cstride, C, kprime, S, k,
+                       int kprime, int S, int k, int P, const uint32_t* mmc, int chunk_stride,
+                       int nchunks, uint32_t* range, uint32_t* rows, int32_t* tkmeta,
+                       uint2* sorted, int32_t* out_idx, float* out_est, hipStream_t st,
+                       const EvPair& ev_hist, const EvPair& ev_select) {
+  const dim3 grid(P, BH);
+  hipError_t e = launch(k_topk_hist, grid, dim3(1024), st, ev_hist, est, cstride, C, P, mmc,
+                        chunk_stride, nchunks, rows, range, sorted);
+  if (e != hipSuccess) return e;
+  return launch(k_topk_select, grid, dim3(1024), st, ev_select, est, cand, cstride, C, kprime, S,
+                k, P, (const uint32_t*)range, (const uint32_t*)rows, (const uint2*)sorted, tkmeta,
                 out_idx, out_est);
 }
 

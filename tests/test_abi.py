@@ -60,8 +60,8 @@ def test_rot_scale_matches_oracle(pk, orc):
 
 def test_sizes(pk):
     c = pk.make_config(capacity=1 << 20, batch=1, n_kv_heads=8, n_q_heads=32)
-    # ids 16 B + codes 64 B + w 32 B per key and head
-    assert pk.pariskv_index_bytes(c) == 8 * (1 << 20) * 112
+    # ids 16 B + a 128-byte record (codes 64 B + w 32 B) per key and head
+    assert pk.pariskv_index_bytes(c) == 8 * (1 << 20) * 144
     ws = pk.pariskv_retrieve_workspace_bytes(c, 4096)
     assert 8 * (1 << 20) < ws < 64 * (1 << 20)
     assert pk.pariskv_attn_workspace_bytes(1, 32, 4096, 128) == 32 * 64 * 130 * 4
@@ -134,5 +134,7 @@ def test_host_side_argument_errors(pk):
 def test_status_strings(pk):
     for rc in range(0, -7, -1):
         assert pk.pariskv_status_string(rc) != "unknown status"
-    assert [pk.pariskv_stage_name(s) for s in range(5)] == [
-        "query_prep", "vote_scan", "threshold", "compact_rerank", "topk"]
+    assert [pk.pariskv_stage_name(s) for s in range(6)] == [
+        "query_prep", "vote_scan", "threshold", "compact_rerank",
+        "topk_histogram", "topk_select"]
+    assert pk.pariskv_stage_name(6) is None
