@@ -64,7 +64,7 @@ def read_traffic(name: str, launches_bytes: float):
         return None
     kv = {}
     for line in open(p):
-        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        m = re.match(r"^\s*([a-z0-9_]+)\s*:\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
     if kv.get("kernel_sha256_16") != kernel_sha():
