@@ -198,7 +198,10 @@ PARISKV_API int32_t pariskv_retrieve_topk(const pariskv_index *index,
  * enabled); events[2s] and events[2s+1] are stamped by the dispatch of stage
  * s itself when that kernel starts and ends (hipExtLaunchKernel), so the
  * pair brackets exactly that kernel.  Stages: query prep, vote scan,
- * threshold, compact + rerank, top-k histogram, top-k select.
+ * threshold, compact + rerank, top-k, top-k second pass.  Top-k is one
+ * kernel for up to 4096 candidates per (batch, KV head); above that it is
+ * a histogram kernel (stage 4) and a select kernel (stage 5).  A stage that
+ * a call does not run has its two events recorded back to back.
  * Not for use under stream capture. */
 PARISKV_API int32_t pariskv_retrieve_topk_profiled(
     const pariskv_index *index, const void *Q, int32_t k, int32_t *out_idx,

@@ -85,7 +85,7 @@ struct WsLayout {
   size_t lut, yq, ptab, scores, chist, coff, meta, cand, est, mmc, range, tkmeta, rows, sorted,
       total;
   int64_t Epad, nchunks_max, cstride, tk_blocks_max;
-  int nbins;
+  int nbins, rstride;
 };
 
 WsLayout ws_layout(const pariskv_config* c, int64_t k) {
@@ -96,6 +96,7 @@ WsLayout ws_layout(const pariskv_config* c, int64_t k) {
   const int64_t Cmax = cand_count(Emax, kp, c->cand_num, c->cand_den);
   WsLayout L;
   L.nbins = c->n_subspaces * max_tier(c) + 1;
+  L.rstride = (int)align_up((size_t)L.nbins, 4);  // chunk rows are 16-byte aligned
   L.nchunks_max = ceil_div(Emax, 256);
   L.Epad = (int64_t)align_up((size_t)Emax, 4096);
   L.cstride = (int64_t)align_up((size_t)(Cmax > 0 ? Cmax : 1), 64);  // 256-byte rows
@@ -104,7 +105,7 @@ WsLayout ws_layout(const pariskv_config* c, int64_t k) {
   L.yq = off;     off += align_up((size_t)BH * 128 * 4, kAlign);
   L.ptab = off;   off += align_up((size_t)BH * 2048 * 4, kAlign);
   L.scores = off; off += align_up((size_t)BH * L.Epad, kAlign);
-  L.chist = off;  off += align_up((size_t)BH * L.nchunks_max * L.nbins * 4, kAlign);
+  L.chist = off;  off += align_up((size_t)BH * L.nchunks_max * L.rstride * 4, kAlign);
   L.coff = off;   off += align_up((size_t)BH * L.nchunks_max * 8, kAlign);
   L.meta = off;   off += align_up((size_t)BH * 16, kAlign);
   L.cand = off;   off += align_up((size_t)BH * L.cstride * 4, kAlign);
@@ -208,9 +209,10 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
                         lut, yq, ptab, app, st, ev(0));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_scan(kpt, nch, BH, ix->ids, c->capacity, S, E, lut, scores, L.Epad, chist,
-                       (int)L.nchunks_max, L.nbins, st, ev(1));
+                       (int)L.nchunks_max, L.nbins, L.rstride, st, ev(1));
   if (e != hipSuccess) return hip_status(e);
-  e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, C, meta, coff, st, ev(2));
+  e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, L.rstride, C, meta, coff,
+                         st, ev(2));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_compact_rerank(kpt, nch, BH, scores, L.Epad, S, E, meta, coff,
                                  (int)L.nchunks_max, ptab, ix->rec, c->capacity, cand, est,
@@ -282,7 +284,7 @@ int32_t pariskv_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t k
                                      int32_t head_dim, size_t* bytes) {
   if (!bytes || batch < 1 || n_q_heads < 1 || k < 1 || head_dim < 1)
     return PARISKV_ERR_INVALID_ARG;
-  *bytes = align_up((size_t)batch * n_q_heads * (size_t)ceil_div(k, 64) * (head_dim + 2) * 4,
+  *bytes = align_up((size_t)batch * n_q_heads * (size_t)ceil_div(k, 64) * (head_dim + 4) * 4,
                     kAlign);
   return PARISKV_OK;
 }
@@ -387,7 +389,7 @@ int32_t pariskv_retrieve_topk_profiled(const pariskv_index* ix, const void* Q, i
 
 const char* pariskv_stage_name(int32_t s) {
   static const char* names[PARISKV_RETRIEVE_STAGES] = {
-      "query_prep", "vote_scan", "threshold", "compact_rerank", "topk_histogram", "topk_select"};
+      "query_prep", "vote_scan", "threshold", "compact_rerank", "topk", "topk_second_pass"};
   return (s >= 0 && s < PARISKV_RETRIEVE_STAGES) ? names[s] : nullptr;
 }
 

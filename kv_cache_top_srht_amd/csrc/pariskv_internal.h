@@ -29,6 +29,8 @@ struct AppendJob {
   int n = 0;
 };
 constexpr int kMaxFusedAppend = 48;
+// scan chunks per compact + rerank block (1 or 2)
+constexpr int kCompactChunks = 2;
 
 // Optional timing events stamped by a kernel's own dispatch (null: none).
 struct EvPair {
@@ -45,10 +47,10 @@ hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
                         const EvPair& ev);
 hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t cap, int64_t S,
                        int64_t E, const uint8_t* lut, uint8_t* scores, int64_t Epad,
-                       uint32_t* chist, int chunk_stride, int nbins, hipStream_t st,
-                         const EvPair& ev);
+                       uint32_t* chist, int chunk_stride, int nbins, int rstride,
+                       hipStream_t st, const EvPair& ev);
 hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nchunks, int nbins,
-                         int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st,
+                         int rstride, int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st,
                          const EvPair& ev);
 hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* scores,
                                  int64_t Epad, int64_t S, int64_t E, const int32_t* meta,
@@ -64,6 +66,12 @@ hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cs
 // candidates per top-k block and the largest threshold bin ranked pairwise
 constexpr int kTopkSlice = 4096;
 constexpr int kTopkMaxMembers = 4096;
+// up to this many slices per (b, h), top-k runs as one kernel
+constexpr int kTopkFusedSlices = 1;
+// up to this many slices, the select kernel loads all histogram rows at once
+constexpr int kTopkFewSlices = 16;
+// split-K attention partial per (query head, chunk): o[128], m, l, 2 unused
+constexpr int kPartStride = 132;
 hipError_t launch_attn_split(int dtype, int G, const void* Q, const void* K, const void* V,
                              int64_t rows_per_head, const int32_t* idx, int k, int batch,
                              int n_kv_heads, float qscale, float* part, int nch,

@@ -13,6 +13,7 @@
 // explicit fused multiply-adds.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stdint.h>
 
 #include "codebook_tables.h"
@@ -256,11 +257,11 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
         make_float4(x[4], x[5], x[6], x[7]);
   }
   __syncthreads();
-  // product table for the rerank: ptab[j][code] = fl((code & 8 ? -1 : 1) L[code & 7] yq_j)
+  // product table for the rerank: ptab[j][code] = fl(+-L[code & 7] yq_j), the
+  // sign bit (code & 8) negating the product exactly
   for (int e = tid; e < 2048; e += 1024) {
-    const int j = e >> 4, code = e & 15;
-    const float pr = c_levels[code & 7] * s_yq[j];
-    ptab_out[(int64_t)bh * 2048 + e] = (code & 8) ? -pr : pr;
+    const float pr = c_levels[e & 7] * s_yq[e >> 4];
+    ptab_out[(int64_t)bh * 2048 + e] = (e & 8) ? -pr : pr;
   }
   const int s = tid >> 6, l = tid & 63;
   float z[8];
@@ -316,62 +317,55 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
 // K3 vote scan: [TS] Coarse Candidate Generation: score_i = sum_b lut_b[id_{i,b}]
 // for i in [S, N).  The dominant HBM stream: 16 bytes of bucket ids per key,
 // read once, coalesced (256 threads x 16 B per step).  The 4 KB vote LUT
-// sits in LDS; one ds_read_u8 per subspace (each subspace's 256-byte row
-// spans 64 dwords, so a wave's lookups for one subspace conflict at most
-// 2-way).  Writes one score byte per key and a per-chunk histogram of the
-// scores (zeros counted by wave ballot, the rest by LDS atomics), stored
-// cumulatively: row[v] = #(score >= v) within the chunk.
-// Grid: (chunks, b*H_kv); chunk = KPT * 256 keys.
+// sits in LDS; one ds_read_u8 per subspace.  Writes one score byte per key
+// and a per-chunk histogram of the scores (zeros counted by wave ballot, the
+// rest by per-wave LDS atomics), stored cumulatively: row[v] = #(score >= v)
+// within the chunk.
+// Grid (chunks, b*H_kv); chunk = KPT * 256 keys.
 // ---------------------------------------------------------------------------
 template <int KPT>
-__global__ __launch_bounds__(256) void k_scan(const uint4* __restrict__ ids, int64_t cap, int64_t S,
-                                              int64_t E, const uint8_t* __restrict__ lut,
-                                              uint8_t* __restrict__ scores, int64_t Epad,
-                                              uint32_t* __restrict__ chist, int chunk_stride, int nbins) {
-  const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  __shared__ uint8_t s_lut[16 * 256];
-  __shared__ uint32_t s_hist[4][256];
-  // the key loads go out first; the LUT and histogram are set up meanwhile
+__device__ __forceinline__ void scan_chunk(const uint4 (&x)[KPT], int chunk, int64_t E,
+                                           const uint8_t* s_lut, uint32_t (*s_hist)[256],
+                                           uint8_t* __restrict__ dst, uint32_t* __restrict__ row,
+                                           int nbins, int rstride) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t p0 = (int64_t)chunk * (KPT * 256) + tid;
-  const uint4* src = ids + bh * cap + S;
-  uint8_t* dst = scores + bh * Epad;
-  uint4 x[KPT];
-#pragma unroll
-  for (int t = 0; t < KPT; ++t) {
-    const int64_t p = p0 + t * 256;
-    x[t] = (p < E) ? src[p] : make_uint4(0, 0, 0, 0);
-  }
-  reinterpret_cast<uint4*>(s_lut)[tid] = reinterpret_cast<const uint4*>(lut + (int64_t)bh * 4096)[tid];
-  for (int i = tid; i < 4 * 256; i += 256) (&s_hist[0][0])[i] = 0;
-  __syncthreads();
   uint32_t zeros = 0;
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
     const int64_t p = p0 + t * 256;
     const bool valid = p < E;
     const uint32_t w4[4] = {x[t].x, x[t].y, x[t].z, x[t].w};
-    uint32_t s = 0;
+    uint32_t sc = 0;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) s += s_lut[b * 256 + ((w4[b >> 2] >> ((b & 3) * 8)) & 0xFFu)];
-    const uint64_t zm = __ballot(valid && s == 0);
+    for (int b = 0; b < 16; ++b) sc += s_lut[b * 256 + ((w4[b >> 2] >> ((b & 3) * 8)) & 0xFFu)];
+    const uint64_t zm = __ballot(valid && sc == 0);
     zeros += (uint32_t)__popcll(zm);
     if (valid) {
-      dst[p] = (uint8_t)s;
-      if (s != 0) atomicAdd(&s_hist[wv][s], 1u);
+      dst[p] = (uint8_t)sc;
+      if (sc != 0) atomicAdd(&s_hist[wv][sc], 1u);
     }
   }
   if (lane == 0) s_hist[wv][0] = zeros;
   __syncthreads();
-  for (int v = tid; v < nbins; v += 256)
+  // sum the 4 wave histograms into row 0 and clear rows 1..3 for the next chunk
+  for (int v = tid; v < nbins; v += 256) {
     s_hist[0][v] = s_hist[0][v] + s_hist[1][v] + s_hist[2][v] + s_hist[3][v];
+    s_hist[1][v] = 0;
+    s_hist[2][v] = 0;
+    s_hist[3][v] = 0;
+  }
   __syncthreads();
   // chunk row = #(score >= v) for every v: suffix sums by wave 0, lane l
-  // owning bins 4 l .. 4 l + 3
+  // owning bins 4 l .. 4 l + 3 (rows rstride words apart; bins >= nbins are 0).
+  // Only wave 0 uses row 0 of s_hist, so it clears it for the next chunk.
   if (wv == 0) {
     uint32_t h[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) h[r] = (4 * lane + r < nbins) ? s_hist[0][4 * lane + r] : 0u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * lane + r < nbins) s_hist[0][4 * lane + r] = 0;
     const uint32_t loc = h[0] + h[1] + h[2] + h[3];
     uint32_t inc = loc;  // sum over lanes >= this one
 #pragma unroll
@@ -379,14 +373,42 @@ __global__ __launch_bounds__(256) void k_scan(const uint4* __restrict__ ids, int
       const uint32_t t = __shfl_down(inc, off);
       if (lane + off < 64) inc += t;
     }
-    uint32_t ge = inc - loc;
-    uint32_t* row = chist + ((int64_t)bh * chunk_stride + chunk) * nbins;
-#pragma unroll
-    for (int r = 3; r >= 0; --r) {
-      ge += h[r];
-      if (4 * lane + r < nbins) row[4 * lane + r] = ge;
-    }
+    uint32_t ge[4];
+    ge[3] = inc - loc + h[3];
+    ge[2] = ge[3] + h[2];
+    ge[1] = ge[2] + h[1];
+    ge[0] = ge[1] + h[0];
+    if (4 * lane < rstride) reinterpret_cast<uint4*>(row)[lane] = make_uint4(ge[0], ge[1], ge[2], ge[3]);
   }
+}
+
+template <int KPT>
+__global__ __launch_bounds__(256) void k_scan(const uint4* __restrict__ ids, int64_t cap, int64_t S,
+                                              int64_t E, const uint8_t* __restrict__ lut,
+                                              uint8_t* __restrict__ scores, int64_t Epad,
+                                              uint32_t* __restrict__ chist, int chunk_stride, int nbins,
+                                              int rstride) {
+  const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  __shared__ uint8_t s_lut[16 * 256];
+  __shared__ uint32_t s_hist[4][256];
+  // The LUT load goes out first: loads complete in issue order, so the LUT
+  // is written to LDS while the keys are still in flight.  The key loads are
+  // unconditional (index clamped; keys past E are not used), which keeps
+  // each wait down to the loads it needs.
+  const uint4 lutv = reinterpret_cast<const uint4*>(lut + (int64_t)bh * 4096)[tid];
+  const uint4* src = ids + bh * cap + S;
+  const int64_t p0 = (int64_t)chunk * (KPT * 256) + tid;
+  uint4 x[KPT];
+#pragma unroll
+  for (int t = 0; t < KPT; ++t) {
+    const int64_t p = p0 + t * 256;
+    x[t] = src[p < E ? p : E - 1];
+  }
+  reinterpret_cast<uint4*>(s_lut)[tid] = lutv;
+  for (int i = tid; i < 4 * 256; i += 256) (&s_hist[0][0])[i] = 0;
+  __syncthreads();
+  scan_chunk<KPT>(x, chunk, E, s_lut, s_hist, scores + bh * Epad,
+                  chist + ((int64_t)bh * chunk_stride + chunk) * rstride, nbins, rstride);
 }
 
 // ---------------------------------------------------------------------------
@@ -400,31 +422,42 @@ __global__ __launch_bounds__(256) void k_scan(const uint4* __restrict__ ids, int
 // One 1024-thread block per (b, h).  meta[bh] = (T, #gt, Q, C).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ chist, int chunk_stride,
-                                                 int nchunks, int nbins, int64_t C,
+                                                 int nchunks, int nbins, int rstride, int64_t C,
                                                  int32_t* __restrict__ meta, uint32_t* __restrict__ coff) {
   const int bh = blockIdx.x, tid = threadIdx.x;
-  __shared__ uint32_t s_tot[257];
+  __shared__ uint32_t s_tot[260];
   __shared__ int s_T;
   __shared__ uint2 s_w[16];
-  const uint32_t* hb = chist + (int64_t)bh * chunk_stride * nbins;
-  for (int v = tid; v < 257; v += 1024) s_tot[v] = 0;
-  __syncthreads();
-  {
-    // column sums over the chunks: flat, coalesced reads, 8 in flight per thread
-    const int nw = nchunks * nbins;
-    for (int w0 = 0; w0 < nw; w0 += 8 * 1024) {
-      uint32_t val[8];
+  const uint32_t* hb = chist + (int64_t)bh * chunk_stride * rstride;
+  for (int v = tid; v < 260; v += 1024) s_tot[v] = 0;
+  // column sums over the chunk rows: thread = (row r0, group g of 4 bins),
+  // 16-byte loads, 8 rows in flight per thread, summed in registers
+  const int ng = rstride >> 2, rpp = 1024 / ng;
+  const int g = tid % ng, r0 = tid / ng;
+  uint32_t acc[4] = {0u, 0u, 0u, 0u};
+  if (r0 < rpp) {
+    const uint4* h4 = reinterpret_cast<const uint4*>(hb);
+    for (int rb = r0; rb < nchunks; rb += 8 * rpp) {
+      uint4 v[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int w = w0 + r * 1024 + tid;
-        val[r] = (w < nw) ? hb[w] : 0u;
+      for (int u = 0; u < 8; ++u) {
+        const int row = rb + u * rpp;
+        v[u] = (row < nchunks) ? h4[(int64_t)row * ng + g] : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int w = w0 + r * 1024 + tid;
-        if (w < nw && val[r]) atomicAdd(&s_tot[w % nbins], val[r]);
+      for (int u = 0; u < 8; ++u) {
+        acc[0] += v[u].x;
+        acc[1] += v[u].y;
+        acc[2] += v[u].z;
+        acc[3] += v[u].w;
       }
     }
+  }
+  __syncthreads();
+  if (r0 < rpp) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (acc[i] && 4 * g + i < nbins) atomicAdd(&s_tot[4 * g + i], acc[i]);
   }
   __syncthreads();
   if (tid < nbins && (int64_t)s_tot[tid] >= C && (int64_t)s_tot[tid + 1] < C) {
@@ -442,7 +475,7 @@ __global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ ch
     const int c = c0 + tid;
     uint32_t gt = 0, eq = 0;
     if (c < nchunks) {
-      const uint32_t* hc = hb + (int64_t)c * nbins;
+      const uint32_t* hc = hb + (int64_t)c * rstride;
       gt = (T + 1 < nbins) ? hc[T + 1] : 0u;
       eq = hc[T] - gt;
     }
@@ -468,13 +501,13 @@ __global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ ch
 // chunks' candidates (see K4a), then [TS] Candidate Reranking (RSQ-IP)
 // "Estimation" for each: est = sum_b w_b <v_b, yq_b>, evaluated in fp32 as
 //   est = 0; for b: { p = 0; for j: p = p + fl(v_{b,j} yq_{b,j}); est = est + fl(w_b p) }
-// The products fl(v yq) for all 16 codes of each coordinate come from the
+// The products fl(v yq_j) for all 16 codes of each coordinate come from the
 // table K2 wrote (fl(-L yq) = -fl(L yq) exactly), staged in LDS, so each
-// coordinate costs one LDS read and one add in the stated order.  Reads the
-// candidate's 128-byte record (96 B used); writes (position, estimate) at the
-// candidate's rank in ascending-position order, and the block's estimate
-// range (order keys) for K6.  Grid (ceil(chunks / 2), b*H_kv): two chunks per
-// block keep every block resident in one round.
+// coordinate costs a nibble extract, one LDS read and one add in the stated
+// order.  Reads the candidate's 128-byte record (96 B
+// used); writes (position, estimate) at the candidate's rank in
+// ascending-position order, and the block's estimate range (order keys).
+// Grid (ceil(chunks / 2), b*H_kv), 256 threads.
 // ---------------------------------------------------------------------------
 template <int KPT>
 __device__ __forceinline__ void load_scores(const uint8_t* sp, uint8_t (&sc)[KPT]) {
@@ -497,7 +530,46 @@ __device__ __forceinline__ void load_scores(const uint8_t* sp, uint8_t (&sc)[KPT
   }
 }
 
-template <int KPT>
+// Block-wide exclusive scan of four uint32 values per thread (NT threads).
+template <int NT>
+__device__ __forceinline__ uint4 block_exscan4(uint4 v, uint4* s_warp, uint4& total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint4 inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t a = __shfl_up(inc.x, off), b = __shfl_up(inc.y, off);
+    const uint32_t c = __shfl_up(inc.z, off), d = __shfl_up(inc.w, off);
+    if (lane >= off) { inc.x += a; inc.y += b; inc.z += c; inc.w += d; }
+  }
+  if (lane == 63) s_warp[wv] = inc;
+  __syncthreads();
+  uint4 base = make_uint4(0, 0, 0, 0), tot = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint4 t = s_warp[w];
+    if (w < wv) { base.x += t.x; base.y += t.y; base.z += t.z; base.w += t.w; }
+    tot.x += t.x; tot.y += t.y; tot.z += t.z; tot.w += t.w;
+  }
+  __syncthreads();  // s_warp may be reused by the caller
+  total = tot;
+  return make_uint4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z,
+                    base.w + inc.w - v.w);
+}
+
+// value of lane S of this lane's group of 4 (DPP quad permutation, no LDS)
+template <int S>
+__device__ __forceinline__ float quad_lane(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x55 * S, 0xF, 0xF, false));
+}
+
+// LDS product table: subspace b's 128 entries ([j][code]) start at b * 132
+// floats, so the 4 lanes of a group (subspaces 4q + bb, q = 0..3) read
+// disjoint 16-bank ranges.
+constexpr int kPtabRow = 132;
+constexpr int kPtabLds = 16 * kPtabRow;
+
+template <int KPT, int CPB>
 __global__ __launch_bounds__(256) void k_compact_rerank(
     const uint8_t* __restrict__ scores, int64_t Epad, int64_t S, int64_t E,
     const int32_t* __restrict__ meta, const uint32_t* __restrict__ coff, int chunk_stride,
@@ -506,11 +578,11 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
     float* __restrict__ est, int64_t cstride, int64_t C, uint32_t* __restrict__ mm) {
   constexpr int CH = KPT * 256;
   const int bh = blockIdx.y, tid = threadIdx.x;
-  const int c0 = blockIdx.x * 2;
-  const int nc = (c0 + 1 < nchunks) ? 2 : 1;
-  __shared__ float s_P[128 * 16];
+  const int c0 = blockIdx.x * CPB;
+  const int nc = (CPB == 2 && c0 + 1 < nchunks) ? 2 : 1;
+  __shared__ float s_P[kPtabLds];
   __shared__ uint16_t s_list[2 * CH];
-  __shared__ uint2 s_w[4];
+  __shared__ uint4 s_w4[4];
   __shared__ uint32_t s_mm[8];
   // global reads first
   const int T = meta[bh * 4 + 0];
@@ -525,90 +597,116 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
     load_scores<KPT>(scores + bh * Epad + (int64_t)chunk * CH + tid * KPT, sc[h]);
   }
   {
-    const uint4* pt = reinterpret_cast<const uint4*>(ptab + (int64_t)bh * 2048);
-    reinterpret_cast<uint4*>(s_P)[tid] = pt[tid];
-    reinterpret_cast<uint4*>(s_P)[tid + 256] = pt[tid + 256];
+    // table [b][j][code] (2048 floats) -> LDS rows of kPtabRow floats per subspace
+    const float4* src = reinterpret_cast<const float4*>(ptab + (int64_t)bh * 2048);
+    const float4 v0 = src[tid], v1 = src[tid + 256];
+    reinterpret_cast<float4*>(s_P + (tid >> 5) * kPtabRow)[tid & 31] = v0;
+    reinterpret_cast<float4*>(s_P + ((tid + 256) >> 5) * kPtabRow)[tid & 31] = v1;
   }
-  uint32_t nsel[2];
+  // candidate counts of both chunks, one block scan
+  int64_t quota[2];
+  uint32_t ngt[2], neq[2];
+  int nval[2] = {0, 0};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    if (h >= nc) { nsel[h] = 0; continue; }  // uniform across the block
-    const int64_t pbase = (int64_t)(c0 + h) * CH + tid * KPT;
-    int64_t quota = Q - (int64_t)tieb_c[h];
-    if (quota < 0) quota = 0;
-    uint32_t ngt = 0, neq = 0;
+    quota[h] = Q - (int64_t)tieb_c[h];
+    if (quota[h] < 0) quota[h] = 0;
+    ngt[h] = 0;
+    neq[h] = 0;
+    if (h < nc) {
+      // keys of this thread below E: 0..KPT (one 64-bit compare per chunk)
+      const int64_t rem = E - ((int64_t)(c0 + h) * CH + tid * KPT);
+      nval[h] = rem <= 0 ? 0 : (rem >= KPT ? KPT : (int)rem);
 #pragma unroll
-    for (int t = 0; t < KPT; ++t) {
-      const bool valid = pbase + t < E;
-      ngt += (valid && sc[h][t] > T) ? 1u : 0u;
-      neq += (valid && sc[h][t] == T) ? 1u : 0u;
+      for (int t = 0; t < KPT; ++t) {
+        ngt[h] += (t < nval[h] && sc[h][t] > T) ? 1u : 0u;
+        neq[h] += (t < nval[h] && sc[h][t] == T) ? 1u : 0u;
+      }
     }
-    uint2 tot;
-    const uint2 ex = block_exscan2<256>(make_uint2(ngt, neq), s_w, tot);
-    uint32_t pos = (h ? nsel[0] : 0u) + ex.x + (uint32_t)((int64_t)ex.y < quota ? ex.y : quota);
-    uint32_t tie_seen = ex.y;
+  }
+  uint4 tot;
+  const uint4 ex = block_exscan4<256>(make_uint4(ngt[0], neq[0], ngt[1], neq[1]), s_w4, tot);
+  const uint32_t nsel0 = tot.x + (uint32_t)((int64_t)tot.y < quota[0] ? tot.y : quota[0]);
+  const uint32_t nsel1 = tot.z + (uint32_t)((int64_t)tot.w < quota[1] ? tot.w : quota[1]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h >= nc) continue;
+    const uint32_t exg = h ? ex.z : ex.x, exq = h ? ex.w : ex.y;
+    uint32_t pos = (h ? nsel0 : 0u) + exg + (uint32_t)((int64_t)exq < quota[h] ? exq : quota[h]);
+    uint32_t tie_seen = exq;
 #pragma unroll
     for (int t = 0; t < KPT; ++t) {
-      const bool valid = pbase + t < E;
       bool sel = false;
-      if (valid) {
+      if (t < nval[h]) {
         if (sc[h][t] > T) sel = true;
-        else if (sc[h][t] == T) { sel = (int64_t)tie_seen < quota; ++tie_seen; }
+        else if (sc[h][t] == T) { sel = (int64_t)tie_seen < quota[h]; ++tie_seen; }
       }
       if (sel) s_list[pos++] = (uint16_t)((h << 14) | (tid * KPT + t));
     }
-    nsel[h] = tot.x + (uint32_t)((int64_t)tot.y < quota ? tot.y : quota);
   }
   __syncthreads();
 
-  const uint32_t ntot = nsel[0] + nsel[1];
-  // 4 lanes per candidate: lane q of the group reads codes of subspaces
-  // 4q..4q+3 (16 B) and their w (8 B) from the candidate's 128-byte record,
-  // forms w_b p_b for them, and the running sum is handed from lane to lane
-  // so est accumulates b = 0, 1, ..., 15 in order.
+  const uint32_t ntot = nsel0 + nsel1;
+  // 4 lanes per candidate: lane q reads the codes of subspaces 4q..4q+3
+  // (16 B) and their w (8 B) from the candidate's 128-byte record and forms
+  // w_b p_b for them; DPP broadcasts give every lane all 16 terms, summed in
+  // b order.  Up to 4 candidates per group are fetched before any is used.
   const int q = tid & 3;
+  const uint32_t* rq = rec + (int64_t)bh * cap * 32;
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;  // order keys of this block's estimates
-  for (uint32_t j0 = 0; j0 < ntot; j0 += 64) {
-    const uint32_t j = j0 + (tid >> 2);
-    const bool has = j < ntot;
-    const uint32_t ent = has ? s_list[j] : 0u;
-    const int h = (int)(ent >> 14);
-    const int64_t i = S + (int64_t)(c0 + h) * CH + (ent & 0x3FFFu);
-    const uint32_t* rp = rec + (bh * cap + i) * 32;
-    uint4 cw = make_uint4(0, 0, 0, 0);
-    uint2 ww = make_uint2(0, 0);
-    if (has) {
-      cw = reinterpret_cast<const uint4*>(rp)[q];
-      ww = reinterpret_cast<const uint2*>(rp + 16)[q];
-    }
-    const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
-    float t[4];
+  for (uint32_t j0 = 0; j0 < ntot; j0 += 256) {
+    uint4 cw[4];
+    uint2 ww[4];
+    int64_t pi[4];
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int b = 4 * q + bb;
-      float p = 0.0f;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) p = p + s_P[(b * 8 + jj) * 16 + ((cws[bb] >> (4 * jj)) & 15u)];
-      const uint16_t hb = (uint16_t)(((bb < 2) ? ww.x : ww.y) >> ((bb & 1) * 16));
-      t[bb] = (float)__builtin_bit_cast(_Float16, hb) * p;
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t j = j0 + r * 64 + (tid >> 2);
+      const bool has = j < ntot;
+      const uint32_t ent = has ? s_list[j] : 0u;
+      const int h = (int)(ent >> 14);
+      pi[r] = S + (int64_t)(c0 + h) * CH + (ent & 0x3FFFu);
+      // unconditional loads (idle lanes read record 0), so each round's wait
+      // covers only the loads issued before it
+      const uint32_t* rp = rq + (has ? pi[r] : 0) * 32;
+      cw[r] = reinterpret_cast<const uint4*>(rp)[q];
+      ww[r] = reinterpret_cast<const uint2*>(rp + 16)[q];
     }
-    float e = 0.0f;
 #pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      if (q == step) e = (((e + t[0]) + t[1]) + t[2]) + t[3];
-      e = __shfl(e, (tid & 63 & ~3) + step);
-    }
-    if (has) {
-      if (q == 0) {
-        const uint32_t o = (h ? off_c[1] + (j - nsel[0]) : off_c[0] + j);
-        if ((int64_t)o < C) {  // always true when K4a and this kernel agree
-          cand[bh * cstride + o] = (int32_t)i;
-          est[bh * cstride + o] = e;
-        }
+    for (int r = 0; r < 4; ++r) {
+      if (j0 + r * 64 >= ntot) break;  // uniform across the block
+      const uint32_t j = j0 + r * 64 + (tid >> 2);
+      const uint32_t cws[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+      float t[4];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const float* pb = s_P + (4 * q + bb) * kPtabRow;
+        float p = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) p = p + pb[jj * 16 + ((cws[bb] >> (4 * jj)) & 15u)];
+        const uint16_t hb = (uint16_t)(((bb < 2) ? ww[r].x : ww[r].y) >> ((bb & 1) * 16));
+        t[bb] = (float)__builtin_bit_cast(_Float16, hb) * p;
       }
-      const uint32_t ok = order_key(e);
-      kmn = min(kmn, ok);
-      kmx = max(kmx, ok);
+      float e = 0.0f;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) e = e + quad_lane<0>(t[bb]);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) e = e + quad_lane<1>(t[bb]);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) e = e + quad_lane<2>(t[bb]);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) e = e + quad_lane<3>(t[bb]);
+      if (j < ntot) {
+        if (q == 0) {
+          const uint32_t o = (j >= nsel0) ? off_c[1] + (j - nsel0) : off_c[0] + j;
+          if ((int64_t)o < C) {  // always true when K4a and this kernel agree
+            cand[bh * cstride + o] = (int32_t)pi[r];
+            est[bh * cstride + o] = e;
+          }
+        }
+        const uint32_t ok = order_key(e);
+        kmn = min(kmn, ok);
+        kmx = max(kmx, ok);
+      }
     }
   }
   // this block's estimate range (order keys; no candidates: max key 0 < min)
@@ -658,6 +756,10 @@ __device__ __forceinline__ void range_scale(uint32_t kmin, uint32_t kmax, float&
 __device__ __forceinline__ uint32_t est_bin(float f, float fmin, float scale) {
   return (uint32_t)fminf((f - fmin) * scale, 2047.0f);
 }
+// one 64-bit key per member: larger means earlier in (est desc, position asc)
+__device__ __forceinline__ uint64_t member_key(uint32_t okey, uint32_t pos) {
+  return ((uint64_t)okey << 32) | (uint64_t)(~pos);
+}
 
 // Whole-(b, h) exact selection by an 11 + 11 + 10-bit radix select of the
 // order keys, for 1024 threads; writes sinks, positions and estimates.
@@ -674,6 +776,7 @@ __device__ void topk_radix_block(const float* __restrict__ e, const int32_t* __r
     const int sh = shifts[pass], nb = 1 << widths[pass];
     for (int i = tid; i < nb; i += 1024) s_hist[i] = 0;
     __syncthreads();
+#pragma nounroll
     for (int c = tid; c < C; c += 1024) {
       const uint32_t o = order_key(e[c]);
       if ((o & pmask) == prefix) atomicAdd(&s_hist[(o >> sh) & (nb - 1)], 1u);
@@ -702,6 +805,7 @@ __device__ void topk_radix_block(const float* __restrict__ e, const int32_t* __r
   const int c0 = tid * per;
   const int c1 = (c0 + per < C) ? c0 + per : C;
   uint32_t ngt = 0, neq = 0;
+#pragma nounroll
   for (int c = c0; c < c1; ++c) {
     const uint32_t o = order_key(e[c]);
     ngt += o > thr;
@@ -711,6 +815,7 @@ __device__ void topk_radix_block(const float* __restrict__ e, const int32_t* __r
   const uint2 ex = block_exscan2<1024>(make_uint2(ngt, neq), s_w, tot);
   uint32_t pos = ex.x + (ex.y < remaining ? ex.y : remaining);
   uint32_t tie_seen = ex.y;
+#pragma nounroll
   for (int c = c0; c < c1; ++c) {
     const float ev = e[c];
     const uint32_t o = order_key(ev);
@@ -733,6 +838,12 @@ __global__ __launch_bounds__(1024) void k_topk_hist(
   __shared__ uint32_t s_hist[2048];
   __shared__ uint2 s_w[16];
   __shared__ uint32_t s_r[32];
+  // this block's candidates first (independent of the range), 4 at a time
+  // at an index clamped into the row of cstride (a multiple of 64); entries
+  // past C are not used
+  const int c0 = p * TK_SL + tid * 4;
+  const float4 fv = *reinterpret_cast<const float4*>(e + min(c0, (int)cstride - 4));
+  const float f[4] = {fv.x, fv.y, fv.z, fv.w};
   // this (b, h)'s estimate range from the per-chunk ranges
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   const uint32_t* mb = mmc + (int64_t)bh * chunk_stride * 2;
@@ -755,15 +866,6 @@ __global__ __launch_bounds__(1024) void k_topk_hist(
   if (p == 0 && tid == 0) { range[2 * bh] = kmin; range[2 * bh + 1] = kmax; }
   float fmin, scale;
   range_scale(kmin, kmax, fmin, scale);
-  const int c0 = p * TK_SL + tid * 4;
-  float f[4];
-  if (c0 + 3 < C) {
-    const float4 t = *reinterpret_cast<const float4*>(e + c0);
-    f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w;
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) f[r] = (c0 + r < C) ? e[c0 + r] : 0.0f;
-  }
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     if (c0 + r < C) atomicAdd(&s_hist[est_bin(f[r], fmin, scale)], 1u);
@@ -800,8 +902,7 @@ __global__ __launch_bounds__(1024) void k_topk_select(
   const int32_t* cd = cand + bh * cstride;
   int32_t* oi = out_idx + (int64_t)bh * k;
   __shared__ uint32_t s_hist[2049];
-  __shared__ uint32_t s_mk[TK_MAXMEM];
-  __shared__ uint32_t s_mc[TK_MAXMEM];
+  __shared__ uint64_t s_mem[TK_MAXMEM];
   __shared__ uint32_t s_pref[1024];
   __shared__ uint32_t s_start[1024];
   __shared__ uint32_t s_bits[TK_SL / 32];
@@ -809,20 +910,11 @@ __global__ __launch_bounds__(1024) void k_topk_select(
   __shared__ uint32_t s_sel[4];
   // this block's candidates: loads go out first
   const int c0 = p * TK_SL + tid * 4;
-  float f[4];
-  int32_t ci[4];
-  if (c0 + 3 < C) {
-    const float4 t = *reinterpret_cast<const float4*>(e + c0);
-    const int4 u = *reinterpret_cast<const int4*>(cd + c0);
-    f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w;
-    ci[0] = u.x; ci[1] = u.y; ci[2] = u.z; ci[3] = u.w;
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      f[r] = (c0 + r < C) ? e[c0 + r] : 0.0f;
-      ci[r] = (c0 + r < C) ? cd[c0 + r] : 0;
-    }
-  }
+  const int cl = min(c0, (int)cstride - 4);  // in the row; entries past C unused
+  const float4 fv = *reinterpret_cast<const float4*>(e + cl);
+  const int4 cv = *reinterpret_cast<const int4*>(cd + cl);
+  const float f[4] = {fv.x, fv.y, fv.z, fv.w};
+  const int32_t ci[4] = {cv.x, cv.y, cv.z, cv.w};
   // resolve (every block of this (b, h) does it, identically): the bin b1
   // holding rank k' and the kept members of b1
   const uint32_t* rb = rows + (int64_t)bh * P * 2048;
@@ -886,18 +978,16 @@ __global__ __launch_bounds__(1024) void k_topk_select(
       if (s_pref[mid] <= j) lo = mid; else hi = mid - 1;
     }
     const uint2 pr = sorted[((int64_t)bh * P + lo) * TK_SL + s_start[lo] + (j - s_pref[lo])];
-    s_mk[j] = pr.x;
-    s_mc[j] = pr.y;
+    s_mem[j] = member_key(pr.x, pr.y);
   }
   __syncthreads();
   // rank the members by (est desc, position asc); keep the first `remaining`
   for (uint32_t j = tid; j < M; j += 1024) {
-    const uint32_t kj = s_mk[j], cj = s_mc[j];
+    const uint64_t mj = s_mem[j];
+    const uint32_t cj = ~(uint32_t)mj;
     uint32_t rank = 0;
-    for (uint32_t q = 0; q < M; ++q) {
-      const uint32_t kq = s_mk[q], cq = s_mc[q];
-      rank += (kq > kj || (kq == kj && cq < cj)) ? 1u : 0u;
-    }
+#pragma unroll 8
+    for (uint32_t q = 0; q < M; ++q) rank += (s_mem[q] > mj) ? 1u : 0u;
     if (rank < remaining) {
       const uint32_t qb = cj / TK_SL;
       if (qb < (uint32_t)p) atomicAdd(&s_sel[3], 1u);
@@ -936,6 +1026,333 @@ __global__ __launch_bounds__(1024) void k_topk_select(
       oi[S + pos] = ci[r];
       if (out_est) out_est[(int64_t)bh * kprime + pos] = f[r];
       ++pos;
+    }
+  }
+}
+
+// k_topk_select for P <= MAXP slices: every global read the resolve needs
+// goes out at once (this block's candidates, the range, and the rows of
+// bins 2t, 2t+1 of every slice, kept in registers), so b1's per-slice
+// counts come from the registers of the threads owning b1 and b1 + 1, and
+// only the gather of b1's members waits on a second round of loads.
+template <int MAXP>
+__global__ __launch_bounds__(1024) void k_topk_select_few(
+    const float* __restrict__ est, const int32_t* __restrict__ cand, int64_t cstride, int C,
+    int kprime, int S, int k, int P, const uint32_t* __restrict__ range,
+    const uint32_t* __restrict__ rows, const uint2* __restrict__ sorted,
+    int32_t* __restrict__ tkmeta, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
+  const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const float* e = est + bh * cstride;
+  const int32_t* cd = cand + bh * cstride;
+  int32_t* oi = out_idx + (int64_t)bh * k;
+  __shared__ uint32_t s_hist[2049];
+  __shared__ uint64_t s_mem[TK_MAXMEM];
+  __shared__ uint32_t s_cnt[MAXP], s_start[MAXP], s_pref[MAXP + 1];
+  __shared__ uint32_t s_bits[TK_SL / 32];
+  __shared__ uint2 s_w[16];
+  __shared__ uint32_t s_sel[4];
+  // All loads are unconditional (one wait covers them all): rows past P
+  // re-read row P - 1 and are masked; this block's candidates are read 4 at
+  // a time at an index clamped into the row of cstride (a multiple of 64).
+  const uint32_t* rb = rows + (int64_t)bh * P * 2048;
+  uint2 rv[MAXP];
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q)
+    rv[q] = reinterpret_cast<const uint2*>(rb + (int64_t)(q < P ? q : P - 1) * 2048)[tid];
+  const int c0 = p * TK_SL + tid * 4;
+  const int cl = min(c0, (int)cstride - 4);
+  const float4 fv = *reinterpret_cast<const float4*>(e + cl);
+  const int4 cv = *reinterpret_cast<const int4*>(cd + cl);
+  const float f[4] = {fv.x, fv.y, fv.z, fv.w};
+  const int32_t ci[4] = {cv.x, cv.y, cv.z, cv.w};
+  const uint32_t kmin = range[2 * bh], kmax = range[2 * bh + 1];
+  uint32_t a0 = 0, a1 = 0;
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q) {
+    if (q < P) { a0 += rv[q].x; a1 += rv[q].y; }
+  }
+  s_hist[2 * tid] = a0;
+  s_hist[2 * tid + 1] = a1;
+  if (tid == 0) { s_hist[2048] = 0; s_sel[3] = 0; }
+  if (tid < TK_SL / 32) s_bits[tid] = 0;
+  __syncthreads();
+  for (int b = tid; b < 2048; b += 1024)
+    if (s_hist[b] >= (uint32_t)kprime && s_hist[b + 1] < (uint32_t)kprime) s_sel[0] = b;
+  __syncthreads();
+  const uint32_t b1 = s_sel[0];
+  const uint32_t above_tot = s_hist[b1 + 1];
+  const uint32_t M = s_hist[b1] - above_tot;
+  const uint32_t remaining = (uint32_t)kprime - above_tot;
+  if (M > (uint32_t)TK_MAXMEM) {
+    if (p == 0) {
+      __syncthreads();  // s_hist is reused below
+      topk_radix_block(e, cd, C, kprime, S, oi,
+                       out_est ? out_est + (int64_t)bh * kprime : nullptr, s_hist, s_w, s_sel);
+      if (tid == 0) {
+        tkmeta[bh * 4 + 0] = (int32_t)b1;
+        tkmeta[bh * 4 + 1] = (int32_t)remaining;
+        tkmeta[bh * 4 + 2] = 1;
+        tkmeta[bh * 4 + 3] = (int32_t)M;
+      }
+    }
+    return;
+  }
+  // per slice q: #(bin >= b1) and #(bin > b1), from the owners' registers
+  // (separate loops for the even and odd bin keep rv[] in registers)
+  if (tid == (int)(b1 >> 1)) {
+    if (b1 & 1u) {
+#pragma unroll
+      for (int q = 0; q < MAXP; ++q)
+        if (q < P) s_cnt[q] = rv[q].y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < MAXP; ++q)
+        if (q < P) s_cnt[q] = rv[q].x;
+    }
+  }
+  if (b1 + 1 < 2048u) {
+    if (tid == (int)((b1 + 1) >> 1)) {
+      if ((b1 + 1) & 1u) {
+#pragma unroll
+        for (int q = 0; q < MAXP; ++q)
+          if (q < P) s_start[q] = rv[q].y;
+      } else {
+#pragma unroll
+        for (int q = 0; q < MAXP; ++q)
+          if (q < P) s_start[q] = rv[q].x;
+      }
+    }
+  } else if (tid < P) {
+    s_start[tid] = 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t acc = 0, before = 0;
+    s_pref[0] = 0;
+    for (int q = 0; q < P; ++q) {
+      acc += s_cnt[q] - s_start[q];
+      s_pref[q + 1] = acc;
+      if (q < p) before += s_start[q];
+    }
+    s_sel[2] = before;
+  }
+  __syncthreads();
+  const uint32_t above_before = s_sel[2];
+  // b1's members: slice q holds them contiguously in its sorted array from
+  // #(bin > b1) on
+  for (uint32_t j = tid; j < M; j += 1024) {
+    int q = 0;
+    while (q + 1 < P && s_pref[q + 1] <= j) ++q;
+    const uint2 pr = sorted[((int64_t)bh * P + q) * TK_SL + s_start[q] + (j - s_pref[q])];
+    s_mem[j] = member_key(pr.x, pr.y);
+  }
+  __syncthreads();
+  // rank the members by (est desc, position asc); keep the first `remaining`
+  for (uint32_t j = tid; j < M; j += 1024) {
+    const uint64_t mj = s_mem[j];
+    const uint32_t cj = ~(uint32_t)mj;
+    uint32_t rank = 0;
+#pragma unroll 8
+    for (uint32_t q = 0; q < M; ++q) rank += (s_mem[q] > mj) ? 1u : 0u;
+    if (rank < remaining) {
+      const uint32_t qb = cj / TK_SL;
+      if (qb < (uint32_t)p) atomicAdd(&s_sel[3], 1u);
+      else if (qb == (uint32_t)p) atomicOr(&s_bits[(cj % TK_SL) >> 5], 1u << (cj & 31));
+    }
+  }
+  __syncthreads();
+  if (p == 0) {
+    for (int t = tid; t < S; t += 1024) oi[t] = t;
+    if (tid == 0) {
+      tkmeta[bh * 4 + 0] = (int32_t)b1;
+      tkmeta[bh * 4 + 1] = (int32_t)remaining;
+      tkmeta[bh * 4 + 2] = 0;
+      tkmeta[bh * 4 + 3] = (int32_t)M;
+    }
+  }
+  // ordered compaction of this block's selection at its offset
+  float fmin, scale;
+  range_scale(kmin, kmax, fmin, scale);
+  uint32_t selm = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int c = c0 + r;
+    if (c < C) {
+      const uint32_t bn = est_bin(f[r], fmin, scale);
+      if (bn > b1 || (bn == b1 && ((s_bits[(c % TK_SL) >> 5] >> (c & 31)) & 1u)))
+        selm |= 1u << r;
+    }
+  }
+  uint2 tot;
+  const uint2 ex = block_exscan2<1024>(make_uint2((uint32_t)__popc(selm), 0), s_w, tot);
+  uint32_t pos = above_before + s_sel[3] + ex.x;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (((selm >> r) & 1u) && pos < (uint32_t)kprime) {  // bound holds by construction
+      oi[S + pos] = ci[r];
+      if (out_est) out_est[(int64_t)bh * kprime + pos] = f[r];
+      ++pos;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K6, single kernel for C <= TK_SL * MAXS candidates per (b, h).  Every
+// block loads all C estimates of its (b, h) (at most 256 KB, L2-resident)
+// and resolves the selection by itself -- the same result in every block:
+// range = min/max of the estimates, linear 2048-bin histogram (same binning
+// as above), cumulative counts, the bin b1 holding rank k', exact ranking of
+// b1's members by (est desc, position asc).  Then block p writes the
+// selected candidates of its slice [p TK_SL, (p + 1) TK_SL) in position
+// order at offset S + #(selected before the slice).  A bin with more than
+// TK_MAXMEM members goes to the whole-(b, h) radix select in block 0.
+// ---------------------------------------------------------------------------
+template <int MAXS>
+__global__ __launch_bounds__(1024) void k_topk_fused(
+    const float* __restrict__ est, const int32_t* __restrict__ cand, int64_t cstride, int C,
+    int kprime, int S, int k, int32_t* __restrict__ tkmeta, int32_t* __restrict__ out_idx,
+    float* __restrict__ out_est) {
+  const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const float* e = est + bh * cstride;
+  const int32_t* cd = cand + bh * cstride;
+  int32_t* oi = out_idx + (int64_t)bh * k;
+  __shared__ uint32_t s_hist[2049];
+  __shared__ uint64_t s_mem[TK_MAXMEM];
+  __shared__ uint32_t s_bits[MAXS * TK_SL / 32];
+  __shared__ uint2 s_w[16];
+  __shared__ uint32_t s_r[32];
+  __shared__ uint32_t s_sel[4];
+  // all estimates: thread t holds candidates sl TK_SL + 4 t .. + 3 of every slice sl
+  // (unconditional loads, 4 at a time at an index clamped into the row of
+  // cstride, a multiple of 64; entries past C are not used)
+  float f[MAXS][4];
+#pragma unroll
+  for (int sl = 0; sl < MAXS; ++sl) {
+    const int c0 = sl * TK_SL + tid * 4;
+    const float4 t = *reinterpret_cast<const float4*>(e + min(c0, (int)cstride - 4));
+    f[sl][0] = t.x; f[sl][1] = t.y; f[sl][2] = t.z; f[sl][3] = t.w;
+  }
+  const int cp = p * TK_SL + tid * 4;
+  const int4 cv = *reinterpret_cast<const int4*>(cd + min(cp, (int)cstride - 4));
+  const int32_t ci[4] = {cv.x, cv.y, cv.z, cv.w};
+  for (int i = tid; i < 2049; i += 1024) s_hist[i] = 0;
+  for (int i = tid; i < MAXS * TK_SL / 32; i += 1024) s_bits[i] = 0;
+  if (tid < 4) s_sel[tid] = 0;
+  // range of the estimates (order keys)
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int sl = 0; sl < MAXS; ++sl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (sl * TK_SL + tid * 4 + r < C) {
+        const uint32_t o = order_key(f[sl][r]);
+        kmin = min(kmin, o);
+        kmax = max(kmax, o);
+      }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  if ((tid & 63) == 0) { s_r[tid >> 6] = kmin; s_r[16 + (tid >> 6)] = kmax; }
+  __syncthreads();
+  kmin = s_r[0];
+  kmax = s_r[16];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) { kmin = min(kmin, s_r[w]); kmax = max(kmax, s_r[16 + w]); }
+  float fmin, scale;
+  range_scale(kmin, kmax, fmin, scale);
+#pragma unroll
+  for (int sl = 0; sl < MAXS; ++sl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (sl * TK_SL + tid * 4 + r < C) atomicAdd(&s_hist[est_bin(f[sl][r], fmin, scale)], 1u);
+  __syncthreads();
+  {
+    // cumulative #(bin >= b); thread t owns bins 2047 - 2t and 2046 - 2t
+    const uint32_t hh = s_hist[2047 - 2 * tid], hl = s_hist[2046 - 2 * tid];
+    uint2 tot;
+    const uint2 ex = block_exscan2<1024>(make_uint2(hh + hl, 0), s_w, tot);
+    s_hist[2047 - 2 * tid] = ex.x + hh;
+    s_hist[2046 - 2 * tid] = ex.x + hh + hl;
+  }
+  __syncthreads();
+  for (int b = tid; b < 2048; b += 1024)
+    if (s_hist[b] >= (uint32_t)kprime && s_hist[b + 1] < (uint32_t)kprime) s_sel[0] = b;
+  __syncthreads();
+  const uint32_t b1 = s_sel[0];
+  const uint32_t above_tot = s_hist[b1 + 1];
+  const uint32_t M = s_hist[b1] - above_tot;
+  const uint32_t remaining = (uint32_t)kprime - above_tot;
+  if (M > (uint32_t)TK_MAXMEM) {
+    if (p == 0) {
+      __syncthreads();  // s_hist is reused below
+      topk_radix_block(e, cd, C, kprime, S, oi,
+                       out_est ? out_est + (int64_t)bh * kprime : nullptr, s_hist, s_w, s_sel);
+      if (tid == 0) {
+        tkmeta[bh * 4 + 0] = (int32_t)b1;
+        tkmeta[bh * 4 + 1] = (int32_t)remaining;
+        tkmeta[bh * 4 + 2] = 1;
+        tkmeta[bh * 4 + 3] = (int32_t)M;
+      }
+    }
+    return;
+  }
+  // b1's members, then their exact ranks; kept members are marked in s_bits
+#pragma unroll
+  for (int sl = 0; sl < MAXS; ++sl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = sl * TK_SL + tid * 4 + r;
+      if (c < C && est_bin(f[sl][r], fmin, scale) == b1) {
+        const uint32_t slot = atomicAdd(&s_sel[2], 1u);
+        s_mem[slot] = member_key(order_key(f[sl][r]), (uint32_t)c);
+      }
+    }
+  __syncthreads();
+  for (uint32_t j = tid; j < M; j += 1024) {
+    const uint64_t mj = s_mem[j];
+    const uint32_t cj = ~(uint32_t)mj;
+    uint32_t rank = 0;
+#pragma unroll 8
+    for (uint32_t q = 0; q < M; ++q) rank += (s_mem[q] > mj) ? 1u : 0u;
+    if (rank < remaining) atomicOr(&s_bits[cj >> 5], 1u << (cj & 31));
+  }
+  __syncthreads();
+  // selected flags: count those of the slices before p, keep this slice's
+  uint32_t before = 0, selm = 0;
+  float fo[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int sl = 0; sl < MAXS; ++sl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = sl * TK_SL + tid * 4 + r;
+      if (c < C && sl <= p) {
+        const uint32_t bn = est_bin(f[sl][r], fmin, scale);
+        const bool sel = bn > b1 || (bn == b1 && ((s_bits[c >> 5] >> (c & 31)) & 1u));
+        if (sl < p) before += sel ? 1u : 0u;
+        else if (sel) selm |= 1u << r;
+      }
+      if (sl == p) fo[r] = f[sl][r];
+    }
+  uint2 tot;
+  const uint2 ex = block_exscan2<1024>(make_uint2((uint32_t)__popc(selm), before), s_w, tot);
+  uint32_t pos = tot.y + ex.x;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (((selm >> r) & 1u) && pos < (uint32_t)kprime) {  // bound holds by construction
+      oi[S + pos] = ci[r];
+      if (out_est) out_est[(int64_t)bh * kprime + pos] = fo[r];
+      ++pos;
+    }
+  }
+  if (p == 0) {
+    for (int t = tid; t < S; t += 1024) oi[t] = t;
+    if (tid == 0) {
+      tkmeta[bh * 4 + 0] = (int32_t)b1;
+      tkmeta[bh * 4 + 1] = (int32_t)remaining;
+      tkmeta[bh * 4 + 2] = 0;
+      tkmeta[bh * 4 + 3] = (int32_t)M;
     }
   }
 }
@@ -1027,59 +1444,72 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, con
       o = __builtin_fmaf(f, s_o[s][g][j], o);
       l = __builtin_fmaf(f, s_l[s][g], l);
     }
-    float* pp = part + (((int64_t)(b * Hq + h * G + g)) * nch + chunk) * 130;
+    float* pp = part + (((int64_t)(b * Hq + h * G + g)) * nch + chunk) * kPartStride;
     pp[j] = o;
     if (j == 0) { pp[128] = M; pp[129] = l; }
   }
 }
 
 // K8 log-sum-exp merge of the split-K partials -> output row per query head.
-// The block stages its (m, l) pairs in LDS first (one coalesced pass), so the
-// per-element loop reads LDS, not dependent global loads.
+// One block per (b, query head).  Partials are staged in LDS 64 chunks at a
+// time (one round of 16-byte loads); threads 0..127 then combine them for
+// their output element, rescaling by the running maximum across tiles.
 template <typename T>
-__global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part, int nch,
+__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part, int nch,
                                                     T* __restrict__ out) {
-  const int bq = blockIdx.x, j = threadIdx.x;
-  const float* pp = part + (int64_t)bq * nch * 130;
-  __shared__ float s_f[2048];
-  __shared__ float s_l[2048];
-  __shared__ float s_red[2];
-  float o = 0.0f, l = 0.0f;
-  // running maximum over tiles of up to 2048 chunks
-  float M = -INFINITY;
-  for (int t0 = 0; t0 < nch; t0 += 2048) {
-    const int nt = min(2048, nch - t0);
-    for (int c = j; c < nt; c += 128) {
-      s_f[c] = pp[(int64_t)(t0 + c) * 130 + 128];
-      s_l[c] = pp[(int64_t)(t0 + c) * 130 + 129];
-    }
-    __syncthreads();
-    float tm = -INFINITY;
-    for (int c = j; c < nt; c += 128) tm = fmaxf(tm, s_f[c]);
+  constexpr int R4 = kPartStride / 4;  // float4 per partial record
+  constexpr int TILE = 64;
+  constexpr int NLD = (TILE * R4 + 255) / 256;
+  const int bq = blockIdx.x, tid = threadIdx.x;
+  const float* pp = part + (int64_t)bq * nch * kPartStride;
+  __shared__ float4 s_p4[TILE * R4];
+  const float* s_p = reinterpret_cast<const float*>(s_p4);
+  float o = 0.0f, l = 0.0f, M = -INFINITY;
+  for (int t0 = 0; t0 < nch; t0 += TILE) {
+    const int nt = min(TILE, nch - t0);
+    const int n4 = nt * R4;
+    const float4* src = reinterpret_cast<const float4*>(pp + (int64_t)t0 * kPartStride);
+    float4 v[NLD];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) tm = fmaxf(tm, __shfl_xor(tm, off));
-    if ((j & 63) == 0) s_red[j >> 6] = tm;
-    __syncthreads();
-    const float Mn = fmaxf(M, fmaxf(s_red[0], s_red[1]));
-    const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
-    o *= r;
-    l *= r;
-    M = Mn;
-    for (int c = 0; c < nt; ++c) {
-      const float f = exp2f(s_f[c] - M);
-      o = __builtin_fmaf(f, pp[(int64_t)(t0 + c) * 130 + j], o);
-      l = __builtin_fmaf(f, s_l[c], l);
+    for (int u = 0; u < NLD; ++u) {
+      const int i = tid + 256 * u;
+      v[u] = (i < n4) ? src[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    __syncthreads();  // the previous tile has been consumed
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int i = tid + 256 * u;
+      if (i < n4) s_p4[i] = v[u];
     }
     __syncthreads();
+    if (tid < 128) {
+      float tm = -INFINITY;
+      for (int c = 0; c < nt; ++c) tm = fmaxf(tm, s_p[c * kPartStride + 128]);
+      const float Mn = fmaxf(M, tm);
+      if (Mn != -INFINITY) {
+        const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+        o *= r;
+        l *= r;
+        M = Mn;
+        for (int c = 0; c < nt; ++c) {
+          const float mc = s_p[c * kPartStride + 128];
+          const float f = (mc == -INFINITY) ? 0.0f : exp2f(mc - M);
+          o = __builtin_fmaf(f, s_p[c * kPartStride + tid], o);
+          l = __builtin_fmaf(f, s_p[c * kPartStride + 129], l);
+        }
+      }
+    }
   }
-  const float r = o / l;
-  if constexpr (sizeof(T) == 2) {
-    // fp32 -> bf16, round to nearest even
-    uint32_t u = __float_as_uint(r);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    out[(int64_t)bq * 128 + j] = (T)(u >> 16);
-  } else {
-    out[(int64_t)bq * 128 + j] = r;
+  if (tid < 128) {
+    const float r = o / l;
+    if constexpr (sizeof(T) == 2) {
+      // fp32 -> bf16, round to nearest even
+      uint32_t u = __float_as_uint(r);
+      u += 0x7FFFu + ((u >> 16) & 1u);
+      out[(int64_t)bq * 128 + tid] = (T)(u >> 16);
+    } else {
+      out[(int64_t)bq * 128 + tid] = r;
+    }
   }
 }
 
@@ -1123,7 +1553,7 @@ hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
 
 hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t cap, int64_t S,
                        int64_t E, const uint8_t* lut, uint8_t* scores, int64_t Epad,
-                       uint32_t* chist, int chunk_stride, int nbins, hipStream_t st,
+                       uint32_t* chist, int chunk_stride, int nbins, int rstride, hipStream_t st,
                        const EvPair& ev) {
   const dim3 grid(nchunks, BH);
   const uint4* id4 = (const uint4*)ids;
@@ -1131,7 +1561,7 @@ hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t
 #define PKV_SCAN(K)                                                                          \
   case K:                                                                                    \
     return launch(k_scan<K>, grid, dim3(256), st, ev, id4, cap, S, E, lut, scores, Epad,     \
-                  chist, chunk_stride, nbins);
+                  chist, chunk_stride, nbins, rstride);
     PKV_SCAN(1) PKV_SCAN(2) PKV_SCAN(4) PKV_SCAN(8) PKV_SCAN(16)
 #undef PKV_SCAN
     default: return hipErrorInvalidValue;
@@ -1139,10 +1569,10 @@ hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t
 }
 
 hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nchunks, int nbins,
-                         int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st,
+                         int rstride, int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st,
                          const EvPair& ev) {
-  return launch(k_thresh, dim3(BH), dim3(1024), st, ev, chist, chunk_stride, nchunks, nbins, C,
-                meta, coff);
+  return launch(k_thresh, dim3(BH), dim3(1024), st, ev, chist, chunk_stride, nchunks, nbins,
+                rstride, C, meta, coff);
 }
 
 hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* scores,
@@ -1151,12 +1581,13 @@ hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* sc
                                  const uint32_t* rec, int64_t cap, int32_t* cand, float* est,
                                  int64_t cstride, int64_t C, uint32_t* mm, hipStream_t st,
                                  const EvPair& ev) {
-  const dim3 grid((nchunks + 1) / 2, BH);
+  const dim3 grid((nchunks + kCompactChunks - 1) / kCompactChunks, BH);
   switch (kpt) {
 #define PKV_CR(K)                                                                            \
   case K:                                                                                    \
-    return launch(k_compact_rerank<K>, grid, dim3(256), st, ev, scores, Epad, S, E, meta,    \
-                  coff, chunk_stride, nchunks, ptab, rec, cap, cand, est, cstride, C, mm);
+    return launch(k_compact_rerank<K, kCompactChunks>, grid, dim3(256), st, ev, scores, Epad, \
+                  S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, cand, est, cstride, \
+                  C, mm);
     PKV_CR(1) PKV_CR(2) PKV_CR(4) PKV_CR(8) PKV_CR(16)
 #undef PKV_CR
     default: return hipErrorInvalidValue;
@@ -1169,9 +1600,23 @@ hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cs
                        uint2* sorted, int32_t* out_idx, float* out_est, hipStream_t st,
                        const EvPair& ev_hist, const EvPair& ev_select) {
   const dim3 grid(P, BH);
+  if (P <= kTopkFusedSlices) {
+    // one slice: the whole top-k in one kernel
+    hipError_t e = launch(k_topk_fused<1>, grid, dim3(1024), st, ev_hist, est, cand, cstride, C,
+                          kprime, S, k, tkmeta, out_idx, out_est);
+    if (e != hipSuccess || !ev_select.start) return e;
+    // the second stage does not run: its events are recorded back to back
+    e = hipEventRecord(ev_select.start, st);
+    if (e != hipSuccess) return e;
+    return hipEventRecord(ev_select.stop, st);
+  }
   hipError_t e = launch(k_topk_hist, grid, dim3(1024), st, ev_hist, est, cstride, C, P, mmc,
                         chunk_stride, nchunks, rows, range, sorted);
   if (e != hipSuccess) return e;
+  if (P <= kTopkFewSlices)
+    return launch(k_topk_select_few<kTopkFewSlices>, grid, dim3(1024), st, ev_select, est, cand,
+                  cstride, C, kprime, S, k, P, (const uint32_t*)range, (const uint32_t*)rows,
+                  (const uint2*)sorted, tkmeta, out_idx, out_est);
   return launch(k_topk_select, grid, dim3(1024), st, ev_select, est, cand, cstride, C, kprime, S,
                 k, P, (const uint32_t*)range, (const uint32_t*)rows, (const uint2*)sorted, tkmeta,
                 out_idx, out_est);
@@ -1207,9 +1652,9 @@ hipError_t launch_attn_split(int dtype, int G, const void* Q, const void* K, con
 hipError_t launch_attn_merge(int dtype, const float* part, int nch, int rows, void* out,
                              hipStream_t st, const EvPair& ev) {
   if (dtype == 0)
-    return launch(k_attn_merge<uint16_t>, dim3(rows), dim3(128), st, ev, part, nch,
+    return launch(k_attn_merge<uint16_t>, dim3(rows), dim3(256), st, ev, part, nch,
                   (uint16_t*)out);
-  return launch(k_attn_merge<float>, dim3(rows), dim3(128), st, ev, part, nch, (float*)out);
+  return launch(k_attn_merge<float>, dim3(rows), dim3(256), st, ev, part, nch, (float*)out);
 }
 
 void codebook_m8(float* L, float* tau) {

@@ -64,7 +64,7 @@ def test_sizes(pk):
     assert pk.pariskv_index_bytes(c) == 8 * (1 << 20) * 144
     ws = pk.pariskv_retrieve_workspace_bytes(c, 4096)
     assert 8 * (1 << 20) < ws < 64 * (1 << 20)
-    assert pk.pariskv_attn_workspace_bytes(1, 32, 4096, 128) == 32 * 64 * 130 * 4
+    assert pk.pariskv_attn_workspace_bytes(1, 32, 4096, 128) == 32 * 64 * 132 * 4
 
 
 @pytest.mark.parametrize("field,value,rc", [
@@ -136,5 +136,5 @@ def test_status_strings(pk):
         assert pk.pariskv_status_string(rc) != "unknown status"
     assert [pk.pariskv_stage_name(s) for s in range(6)] == [
         "query_prep", "vote_scan", "threshold", "compact_rerank",
-        "topk_histogram", "topk_select"]
+        "topk", "topk_second_pass"]
     assert pk.pariskv_stage_name(6) is None
