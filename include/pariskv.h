@@ -65,7 +65,8 @@ extern "C" {
  *   n_sink       S: keys [0, S) are always selected and are not scored.
  *   batch, n_kv_heads, n_q_heads   n_q_heads % n_kv_heads == 0; the
  *                G = n_q_heads / n_kv_heads query heads of a KV head share
- *                one retrieval whose query is their mean.
+ *                one retrieval whose query is their mean (this build:
+ *                G in {1, 2, 4, 8}).  batch * n_kv_heads <= 65535.
  *   key_dtype    PARISKV_DTYPE_BF16 or _FP32, the dtype of K and Q.
  *   capacity     maximum keys per (batch, KV head) the index can hold.
  */

@@ -63,8 +63,11 @@ int32_t check_cfg(const pariskv_config* c) {
   if (c->capacity < 1 || c->capacity > 0x7FFFFFFFll || c->n_sink >= c->capacity)
     return PARISKV_ERR_INVALID_ARG;
   if ((int64_t)c->batch * c->n_kv_heads > 65535) return PARISKV_ERR_UNSUPPORTED;
-  // kernels of this build: d = 128 split into 16 subspaces of 8
+  // kernels of this build: d = 128 split into 16 subspaces of 8, and 1, 2, 4
+  // or 8 query heads per KV head
   if (d != 128 || m != 8) return PARISKV_ERR_UNSUPPORTED;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PARISKV_ERR_UNSUPPORTED;
   return PARISKV_OK;
 }
 
@@ -216,7 +219,7 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_compact_rerank(kpt, nch, BH, scores, L.Epad, S, E, meta, coff,
                                  (int)L.nchunks_max, ptab, ix->rec, c->capacity, cand, est,
-                                 L.cstride, C, mmc, st, ev(3));
+                                 L.cstride, C, mmc, L.nbins, st, ev(3));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_topk(BH, est, cand, L.cstride, (int)C, (int)kp, (int)S, k, P, mmc,
                        (int)L.nchunks_max, nch, range, rows, tkmeta, sorted, out_idx, out_est, st,

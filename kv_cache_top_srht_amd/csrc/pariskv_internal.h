@@ -31,6 +31,8 @@ struct AppendJob {
 constexpr int kMaxFusedAppend = 48;
 // scan chunks per compact + rerank block (1 or 2)
 constexpr int kCompactChunks = 2;
+// threads of a vote-scan block (256 or 512; chunks of 4+ keys per 256 threads)
+constexpr int kScanThreads = 512;
 
 // Optional timing events stamped by a kernel's own dispatch (null: none).
 struct EvPair {
@@ -56,8 +58,8 @@ hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* sc
                                  int64_t Epad, int64_t S, int64_t E, const int32_t* meta,
                                  const uint32_t* coff, int chunk_stride, const float* ptab,
                                  const uint32_t* rec, int64_t cap, int32_t* cand, float* est,
-                                 int64_t cstride, int64_t C, uint32_t* mm, hipStream_t st,
-                                 const EvPair& ev);
+                                 int64_t cstride, int64_t C, uint32_t* mm, int nbins,
+                                 hipStream_t st, const EvPair& ev);
 hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cstride, int C,
                        int kprime, int S, int k, int P, const uint32_t* mmc, int chunk_stride,
                        int nchunks, uint32_t* range, uint32_t* rows, int32_t* tkmeta,

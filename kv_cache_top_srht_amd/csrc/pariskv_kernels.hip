@@ -211,14 +211,42 @@ __device__ __forceinline__ uint2 block_exscan2(uint2 v, uint2* s_warp, uint2& to
 // get tier weights in the vote LUT, all other centroids 0.
 // One 1024-thread block per (b, h): wave s handles subspace s, lane l scores
 // centroids 4 l .. 4 l + 3 and keeps them in order; rho rounds of a wave
-// arg-max (6 xor-shuffle steps) pick the winners.
+// maximum over 64-bit (score, centroid) keys pick the winners.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool better(float va, int pa, float vb, int pb) {
-  return va > vb || (va == vb && pa < pb);
+// Centroid p of a subspace with score sc as one 64-bit key: larger key means
+// earlier in (sc desc, p asc); -0 and +0 tie.
+__device__ __forceinline__ uint64_t centroid_key(float sc, int p) {
+  return ((uint64_t)order_key(sc) << 32) | (uint64_t)(255 - p);
 }
 
-template <typename T>
-__global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_kv_heads, int G,
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the 64 lanes, received by every lane: in each row of 16 lanes
+// DPP quad swaps (lane ^ 1, lane ^ 2), the half-row mirror and the row
+// mirror; then lane ^ 16 and lane ^ 32 across rows.
+__device__ __forceinline__ uint64_t wave_max64(uint64_t k) {
+  k = max64(k, dpp64<0xB1>(k));   // quad_perm [1, 0, 3, 2]
+  k = max64(k, dpp64<0x4E>(k));   // quad_perm [2, 3, 0, 1]
+  k = max64(k, dpp64<0x141>(k));  // row_half_mirror
+  k = max64(k, dpp64<0x140>(k));  // row_mirror
+  k = max64(k, shfl_xor64(k, 16));
+  k = max64(k, shfl_xor64(k, 32));
+  return k;
+}
+
+template <typename T, int G>
+__global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_kv_heads,
                                                 float invG, SignMask sg, float c, int rho, Tiers tw,
                                                 uint8_t* __restrict__ lut_out, float* __restrict__ yq_out,
                                                 float* __restrict__ ptab_out, AppendJob app) {
@@ -237,15 +265,18 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
   }
   if (tid < 16) {
     const int sub = tid;
-    float x[8];
+    // all G query rows are loaded at once, then summed in head order
+    float xg[G][8];
     const T* q0 = Q + ((int64_t)(b * Hq + h * G) << 7) + sub * 8;
-    load8(q0, x);
-    for (int g = 1; g < G; ++g) {
-      float t[8];
-      load8(q0 + ((int64_t)g << 7), t);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = x[j] + t[j];
-    }
+    for (int g = 0; g < G; ++g) load8(q0 + ((int64_t)g << 7), xg[g]);
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = xg[0][j];
+#pragma unroll
+    for (int g = 1; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = x[j] + xg[g][j];
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = x[j] * invG;
     srht16(x, sign_byte_of(sg, sub), sub, c);
@@ -267,46 +298,37 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
   float z[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) z[j] = s_yq[s * 8 + j];
-  float bv[4];
-  int bp[4];
+  uint64_t key[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int p = l * 4 + q;
     float acc = (p & 1) ? -z[0] : z[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) acc = acc + (((p >> j) & 1) ? -z[j] : z[j]);
-    bv[q] = acc;
-    bp[q] = p;
+    key[q] = centroid_key(acc, p);
   }
-  // sort the lane's 4 in (sc desc, p asc) order
+  // the lane's 4 in descending key order
 #pragma unroll
   for (int i = 0; i < 3; ++i)
 #pragma unroll
     for (int j = 0; j < 3 - i; ++j)
-      if (better(bv[j + 1], bp[j + 1], bv[j], bp[j])) {
-        const float tv = bv[j]; bv[j] = bv[j + 1]; bv[j + 1] = tv;
-        const int tp = bp[j]; bp[j] = bp[j + 1]; bp[j + 1] = tp;
-      }
+      if (key[j + 1] > key[j]) { const uint64_t t = key[j]; key[j] = key[j + 1]; key[j + 1] = t; }
+  // rho rounds: the wave's best remaining centroid gets tier weight r; its
+  // owner lane drops it (an exhausted lane offers key 0, below every centroid)
   uint32_t lv[4] = {0, 0, 0, 0};
   for (int r = 0; r < rho; ++r) {
-    float wv = bv[0];
-    int wp = bp[0];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float ov = __shfl_xor(wv, off);
-      const int op = __shfl_xor(wp, off);
-      if (better(ov, op, wv, wp)) { wv = ov; wp = op; }
-    }
+    const uint64_t W = wave_max64(key[0]);
+    const int wp = 255 - (int)(uint32_t)(W & 0xFFu);
     if ((wp >> 2) == l) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if ((wp & 3) == q) lv[q] = (uint32_t)tw.w[r];
     }
-    if (bp[0] == wp) {  // the owner lane drops its head
-      bv[0] = bv[1]; bp[0] = bp[1];
-      bv[1] = bv[2]; bp[1] = bp[2];
-      bv[2] = bv[3]; bp[2] = bp[3];
-      bv[3] = -INFINITY; bp[3] = 0x7FFFFFFF;
+    if (key[0] == W) {
+      key[0] = key[1];
+      key[1] = key[2];
+      key[2] = key[3];
+      key[3] = 0;
     }
   }
   reinterpret_cast<uint32_t*>(lut_out + ((int64_t)bh * 16 + s) * 256)[l] =
@@ -323,17 +345,18 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
 // within the chunk.
 // Grid (chunks, b*H_kv); chunk = KPT * 256 keys.
 // ---------------------------------------------------------------------------
-template <int KPT>
+template <int KPT, int NT>
 __device__ __forceinline__ void scan_chunk(const uint4 (&x)[KPT], int chunk, int64_t E,
                                            const uint8_t* s_lut, uint32_t (*s_hist)[256],
                                            uint8_t* __restrict__ dst, uint32_t* __restrict__ row,
                                            int nbins, int rstride) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t p0 = (int64_t)chunk * (KPT * 256) + tid;
+  const int64_t p0 = (int64_t)chunk * (KPT * NT) + tid;
   uint32_t zeros = 0;
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
-    const int64_t p = p0 + t * 256;
+    const int64_t p = p0 + t * NT;
     const bool valid = p < E;
     const uint32_t w4[4] = {x[t].x, x[t].y, x[t].z, x[t].w};
     uint32_t sc = 0;
@@ -348,24 +371,20 @@ __device__ __forceinline__ void scan_chunk(const uint4 (&x)[KPT], int chunk, int
   }
   if (lane == 0) s_hist[wv][0] = zeros;
   __syncthreads();
-  // sum the 4 wave histograms into row 0 and clear rows 1..3 for the next chunk
-  for (int v = tid; v < nbins; v += 256) {
-    s_hist[0][v] = s_hist[0][v] + s_hist[1][v] + s_hist[2][v] + s_hist[3][v];
-    s_hist[1][v] = 0;
-    s_hist[2][v] = 0;
-    s_hist[3][v] = 0;
+  // sum the wave histograms into row 0
+  for (int v = tid; v < nbins; v += NT) {
+    uint32_t a = s_hist[0][v];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) a += s_hist[w][v];
+    s_hist[0][v] = a;
   }
   __syncthreads();
   // chunk row = #(score >= v) for every v: suffix sums by wave 0, lane l
-  // owning bins 4 l .. 4 l + 3 (rows rstride words apart; bins >= nbins are 0).
-  // Only wave 0 uses row 0 of s_hist, so it clears it for the next chunk.
+  // owning bins 4 l .. 4 l + 3 (rows rstride words apart; bins >= nbins are 0)
   if (wv == 0) {
     uint32_t h[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) h[r] = (4 * lane + r < nbins) ? s_hist[0][4 * lane + r] : 0u;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (4 * lane + r < nbins) s_hist[0][4 * lane + r] = 0;
     const uint32_t loc = h[0] + h[1] + h[2] + h[3];
     uint32_t inc = loc;  // sum over lanes >= this one
 #pragma unroll
@@ -382,33 +401,36 @@ __device__ __forceinline__ void scan_chunk(const uint4 (&x)[KPT], int chunk, int
   }
 }
 
-template <int KPT>
-__global__ __launch_bounds__(256) void k_scan(const uint4* __restrict__ ids, int64_t cap, int64_t S,
-                                              int64_t E, const uint8_t* __restrict__ lut,
-                                              uint8_t* __restrict__ scores, int64_t Epad,
-                                              uint32_t* __restrict__ chist, int chunk_stride, int nbins,
-                                              int rstride) {
+// one chunk of KPT * NT keys per block
+template <int KPT, int NT>
+__global__ __launch_bounds__(NT) void k_scan(const uint4* __restrict__ ids, int64_t cap, int64_t S,
+                                             int64_t E, const uint8_t* __restrict__ lut,
+                                             uint8_t* __restrict__ scores, int64_t Epad,
+                                             uint32_t* __restrict__ chist, int chunk_stride, int nbins,
+                                             int rstride) {
+  constexpr int NW = NT / 64;
   const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   __shared__ uint8_t s_lut[16 * 256];
-  __shared__ uint32_t s_hist[4][256];
+  __shared__ uint32_t s_hist[NW][256];
   // The LUT load goes out first: loads complete in issue order, so the LUT
   // is written to LDS while the keys are still in flight.  The key loads are
   // unconditional (index clamped; keys past E are not used), which keeps
   // each wait down to the loads it needs.
-  const uint4 lutv = reinterpret_cast<const uint4*>(lut + (int64_t)bh * 4096)[tid];
+  uint4 lutv = make_uint4(0, 0, 0, 0);
+  if (tid < 256) lutv = reinterpret_cast<const uint4*>(lut + (int64_t)bh * 4096)[tid];
   const uint4* src = ids + bh * cap + S;
-  const int64_t p0 = (int64_t)chunk * (KPT * 256) + tid;
+  const int64_t p0 = (int64_t)chunk * (KPT * NT) + tid;
   uint4 x[KPT];
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
-    const int64_t p = p0 + t * 256;
+    const int64_t p = p0 + t * NT;
     x[t] = src[p < E ? p : E - 1];
   }
-  reinterpret_cast<uint4*>(s_lut)[tid] = lutv;
-  for (int i = tid; i < 4 * 256; i += 256) (&s_hist[0][0])[i] = 0;
+  if (tid < 256) reinterpret_cast<uint4*>(s_lut)[tid] = lutv;
+  for (int i = tid; i < NW * 256; i += NT) (&s_hist[0][0])[i] = 0;
   __syncthreads();
-  scan_chunk<KPT>(x, chunk, E, s_lut, s_hist, scores + bh * Epad,
-                  chist + ((int64_t)bh * chunk_stride + chunk) * rstride, nbins, rstride);
+  scan_chunk<KPT, NT>(x, chunk, E, s_lut, s_hist, scores + bh * Epad,
+                      chist + ((int64_t)bh * chunk_stride + chunk) * rstride, nbins, rstride);
 }
 
 // ---------------------------------------------------------------------------
@@ -557,6 +579,84 @@ __device__ __forceinline__ uint4 block_exscan4(uint4 v, uint4* s_warp, uint4& to
                     base.w + inc.w - v.w);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
+// 4 and 8 within each row of 16 lanes, then the last lane of row 0 (2) added
+// to row 1 (3) and the last lane of row 1 added to rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// Block-wide exclusive scan of two uint32 values per thread (NT threads),
+// each the packed pair (lo 16 bits, hi 16 bits) of counts whose block total
+// stays below 65536.
+template <int NT>
+__device__ __forceinline__ uint2 block_exscan_packed(uint2 v, uint2* s_warp, uint2& total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t ix = wave_incl_scan(v.x), iy = wave_incl_scan(v.y);
+  if (lane == 63) s_warp[wv] = make_uint2(ix, iy);
+  __syncthreads();
+  uint2 base = make_uint2(0, 0), tot = make_uint2(0, 0);
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint2 t = s_warp[w];
+    if (w < wv) { base.x += t.x; base.y += t.y; }
+    tot.x += t.x; tot.y += t.y;
+  }
+  total = tot;
+  return make_uint2(base.x + ix - v.x, base.y + iy - v.y);
+}
+
+// the lowest r set bits of m
+__device__ __forceinline__ uint32_t lowest_bits(uint32_t m, uint32_t r) {
+  uint32_t out = 0;
+  for (uint32_t i = 0; i < r && m; ++i) {
+    const uint32_t low = m & (0u - m);
+    out |= low;
+    m ^= low;
+  }
+  return out;
+}
+
+// key masks of one chunk's KPT scores of this thread: bit t of gtm / eqm is
+// set when key t (t < nval) has score > T / == T.  For 8 keys with every
+// score below 128 the bytes are compared four at a time (SWAR: adding
+// 0x7F - T (0x80 - T) to each byte sets its top bit exactly when the byte is
+// > T (>= T), with no carry out of a byte).
+template <int KPT>
+__device__ __forceinline__ void score_masks(const uint8_t (&sc)[KPT], const uint2 raw, int T,
+                                            int nval, bool swar, uint32_t& gtm, uint32_t& eqm) {
+  gtm = 0;
+  eqm = 0;
+  if constexpr (KPT == 8) {
+    if (swar) {
+      const uint32_t ag = (uint32_t)(0x7F - T) * 0x01010101u, ae = (uint32_t)(0x80 - T) * 0x01010101u;
+      const uint32_t g0 = (raw.x + ag) & 0x80808080u, g1 = (raw.y + ag) & 0x80808080u;
+      const uint32_t e0 = ((raw.x + ae) & 0x80808080u) ^ g0, e1 = ((raw.y + ae) & 0x80808080u) ^ g1;
+      // gather the top bits of the 4 bytes into a nibble (bit i from byte i)
+      gtm = (((g0 >> 7) * 0x10204080u) >> 28) | ((((g1 >> 7) * 0x10204080u) >> 28) << 4);
+      eqm = (((e0 >> 7) * 0x10204080u) >> 28) | ((((e1 >> 7) * 0x10204080u) >> 28) << 4);
+      const uint32_t vm = (nval >= 8) ? 0xFFu : ((1u << nval) - 1u);
+      gtm &= vm;
+      eqm &= vm;
+      return;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < KPT; ++t) {
+    if (t < nval) {
+      gtm |= (sc[t] > T) ? (1u << t) : 0u;
+      eqm |= (sc[t] == T) ? (1u << t) : 0u;
+    }
+  }
+}
+
 // value of lane S of this lane's group of 4 (DPP quad permutation, no LDS)
 template <int S>
 __device__ __forceinline__ float quad_lane(float v) {
@@ -575,26 +675,34 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
     const int32_t* __restrict__ meta, const uint32_t* __restrict__ coff, int chunk_stride,
     int nchunks, const float* __restrict__ ptab, const uint32_t* __restrict__ rec,
     int64_t cap, int32_t* __restrict__ cand,
-    float* __restrict__ est, int64_t cstride, int64_t C, uint32_t* __restrict__ mm) {
+    float* __restrict__ est, int64_t cstride, int64_t C, uint32_t* __restrict__ mm, int swar) {
   constexpr int CH = KPT * 256;
   const int bh = blockIdx.y, tid = threadIdx.x;
   const int c0 = blockIdx.x * CPB;
   const int nc = (CPB == 2 && c0 + 1 < nchunks) ? 2 : 1;
   __shared__ float s_P[kPtabLds];
   __shared__ uint16_t s_list[2 * CH];
-  __shared__ uint4 s_w4[4];
+  __shared__ uint2 s_w2[4];
   __shared__ uint32_t s_mm[8];
   // global reads first
   const int T = meta[bh * 4 + 0];
   const int64_t Q = meta[bh * 4 + 2];
   uint32_t off_c[2], tieb_c[2];
   uint8_t sc[2][KPT];
+  uint2 raw[2] = {make_uint2(0, 0), make_uint2(0, 0)};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int chunk = c0 + (h < nc ? h : 0);
     off_c[h] = coff[((int64_t)bh * chunk_stride + chunk) * 2 + 0];
     tieb_c[h] = coff[((int64_t)bh * chunk_stride + chunk) * 2 + 1];
-    load_scores<KPT>(scores + bh * Epad + (int64_t)chunk * CH + tid * KPT, sc[h]);
+    const uint8_t* sp = scores + bh * Epad + (int64_t)chunk * CH + tid * KPT;
+    if constexpr (KPT == 8) {
+      raw[h] = *reinterpret_cast<const uint2*>(sp);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sc[h][t] = (uint8_t)(((t < 4) ? raw[h].x : raw[h].y) >> ((t & 3) * 8));
+    } else {
+      load_scores<KPT>(sp, sc[h]);
+    }
   }
   {
     // table [b][j][code] (2048 floats) -> LDS rows of kPtabRow floats per subspace
@@ -603,45 +711,45 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
     reinterpret_cast<float4*>(s_P + (tid >> 5) * kPtabRow)[tid & 31] = v0;
     reinterpret_cast<float4*>(s_P + ((tid + 256) >> 5) * kPtabRow)[tid & 31] = v1;
   }
-  // candidate counts of both chunks, one block scan
+  // candidate masks and counts of both chunks, one block scan
   int64_t quota[2];
-  uint32_t ngt[2], neq[2];
-  int nval[2] = {0, 0};
+  uint32_t gtm[2], eqm[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     quota[h] = Q - (int64_t)tieb_c[h];
     if (quota[h] < 0) quota[h] = 0;
-    ngt[h] = 0;
-    neq[h] = 0;
+    gtm[h] = 0;
+    eqm[h] = 0;
     if (h < nc) {
       // keys of this thread below E: 0..KPT (one 64-bit compare per chunk)
       const int64_t rem = E - ((int64_t)(c0 + h) * CH + tid * KPT);
-      nval[h] = rem <= 0 ? 0 : (rem >= KPT ? KPT : (int)rem);
-#pragma unroll
-      for (int t = 0; t < KPT; ++t) {
-        ngt[h] += (t < nval[h] && sc[h][t] > T) ? 1u : 0u;
-        neq[h] += (t < nval[h] && sc[h][t] == T) ? 1u : 0u;
-      }
+      const int nval = rem <= 0 ? 0 : (rem >= KPT ? KPT : (int)rem);
+      score_masks<KPT>(sc[h], raw[h], T, nval, swar != 0, gtm[h], eqm[h]);
     }
   }
-  uint4 tot;
-  const uint4 ex = block_exscan4<256>(make_uint4(ngt[0], neq[0], ngt[1], neq[1]), s_w4, tot);
-  const uint32_t nsel0 = tot.x + (uint32_t)((int64_t)tot.y < quota[0] ? tot.y : quota[0]);
-  const uint32_t nsel1 = tot.z + (uint32_t)((int64_t)tot.w < quota[1] ? tot.w : quota[1]);
+  // counts packed two per word: (gt, eq) of chunk 0 and of chunk 1
+  uint2 tot;
+  const uint2 ex = block_exscan_packed<256>(
+      make_uint2((uint32_t)__popc(gtm[0]) | ((uint32_t)__popc(eqm[0]) << 16),
+                 (uint32_t)__popc(gtm[1]) | ((uint32_t)__popc(eqm[1]) << 16)),
+      s_w2, tot);
+  const uint32_t tg0 = tot.x & 0xFFFFu, tq0 = tot.x >> 16, tg1 = tot.y & 0xFFFFu, tq1 = tot.y >> 16;
+  const uint32_t nsel0 = tg0 + (uint32_t)((int64_t)tq0 < quota[0] ? tq0 : quota[0]);
+  const uint32_t nsel1 = tg1 + (uint32_t)((int64_t)tq1 < quota[1] ? tq1 : quota[1]);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if (h >= nc) continue;
-    const uint32_t exg = h ? ex.z : ex.x, exq = h ? ex.w : ex.y;
+    const uint32_t exw = h ? ex.y : ex.x;
+    const uint32_t exg = exw & 0xFFFFu, exq = exw >> 16;
+    // ties of this thread inside the quota: the lowest r of its tie keys
+    const int64_t left = quota[h] - (int64_t)exq;
+    const uint32_t r = left <= 0 ? 0u : (uint32_t)(left < 32 ? left : 32);
+    uint32_t sel = gtm[h] | lowest_bits(eqm[h], r);
     uint32_t pos = (h ? nsel0 : 0u) + exg + (uint32_t)((int64_t)exq < quota[h] ? exq : quota[h]);
-    uint32_t tie_seen = exq;
-#pragma unroll
-    for (int t = 0; t < KPT; ++t) {
-      bool sel = false;
-      if (t < nval[h]) {
-        if (sc[h][t] > T) sel = true;
-        else if (sc[h][t] == T) { sel = (int64_t)tie_seen < quota[h]; ++tie_seen; }
-      }
-      if (sel) s_list[pos++] = (uint16_t)((h << 14) | (tid * KPT + t));
+    while (sel) {
+      const int t = __builtin_ctz(sel);
+      s_list[pos++] = (uint16_t)((h << 14) | (tid * KPT + t));
+      sel &= sel - 1u;
     }
   }
   __syncthreads();
@@ -1544,26 +1652,49 @@ hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
                         float* yq, float* ptab, const AppendJob& app, hipStream_t st,
                         const EvPair& ev) {
   const float invG = 1.0f / (float)G;
-  if (dtype == 0)
-    return launch(k_qprep<uint16_t>, dim3(BH), dim3(1024), st, ev, (const uint16_t*)Q,
-                  n_kv_heads, G, invG, sg, c, rho, tw, lut, yq, ptab, app);
-  return launch(k_qprep<float>, dim3(BH), dim3(1024), st, ev, (const float*)Q, n_kv_heads, G,
-                invG, sg, c, rho, tw, lut, yq, ptab, app);
+#define PKV_QP(T, GG)                                                                        \
+  return launch(k_qprep<T, GG>, dim3(BH), dim3(1024), st, ev, (const T*)Q, n_kv_heads, invG, \
+                sg, c, rho, tw, lut, yq, ptab, app)
+  if (dtype == 0) {
+    switch (G) {
+      case 1: PKV_QP(uint16_t, 1);
+      case 2: PKV_QP(uint16_t, 2);
+      case 4: PKV_QP(uint16_t, 4);
+      case 8: PKV_QP(uint16_t, 8);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (G) {
+    case 1: PKV_QP(float, 1);
+    case 2: PKV_QP(float, 2);
+    case 4: PKV_QP(float, 4);
+    case 8: PKV_QP(float, 8);
+    default: return hipErrorInvalidValue;
+  }
+#undef PKV_QP
 }
 
 hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t cap, int64_t S,
                        int64_t E, const uint8_t* lut, uint8_t* scores, int64_t Epad,
                        uint32_t* chist, int chunk_stride, int nbins, int rstride, hipStream_t st,
                        const EvPair& ev) {
+  // a chunk is kpt * 256 keys; the scan covers it with kScanThreads threads
   const dim3 grid(nchunks, BH);
   const uint4* id4 = (const uint4*)ids;
+  constexpr int NT = kScanThreads;
   switch (kpt) {
 #define PKV_SCAN(K)                                                                          \
   case K:                                                                                    \
-    return launch(k_scan<K>, grid, dim3(256), st, ev, id4, cap, S, E, lut, scores, Epad,     \
-                  chist, chunk_stride, nbins, rstride);
-    PKV_SCAN(1) PKV_SCAN(2) PKV_SCAN(4) PKV_SCAN(8) PKV_SCAN(16)
+    return launch(k_scan<(K * 256) / NT, NT>, grid, dim3(NT), st, ev, id4, cap, S, E, lut,   \
+                  scores, Epad, chist, chunk_stride, nbins, rstride);
+    PKV_SCAN(4) PKV_SCAN(8) PKV_SCAN(16)
 #undef PKV_SCAN
+    case 1:
+      return launch(k_scan<1, 256>, grid, dim3(256), st, ev, id4, cap, S, E, lut, scores, Epad,
+                    chist, chunk_stride, nbins, rstride);
+    case 2:
+      return launch(k_scan<2, 256>, grid, dim3(256), st, ev, id4, cap, S, E, lut, scores, Epad,
+                    chist, chunk_stride, nbins, rstride);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1579,15 +1710,16 @@ hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* sc
                                  int64_t Epad, int64_t S, int64_t E, const int32_t* meta,
                                  const uint32_t* coff, int chunk_stride, const float* ptab,
                                  const uint32_t* rec, int64_t cap, int32_t* cand, float* est,
-                                 int64_t cstride, int64_t C, uint32_t* mm, hipStream_t st,
-                                 const EvPair& ev) {
+                                 int64_t cstride, int64_t C, uint32_t* mm, int nbins,
+                                 hipStream_t st, const EvPair& ev) {
+  const int swar = nbins <= 128 ? 1 : 0;  // every score below 128
   const dim3 grid((nchunks + kCompactChunks - 1) / kCompactChunks, BH);
   switch (kpt) {
 #define PKV_CR(K)                                                                            \
   case K:                                                                                    \
     return launch(k_compact_rerank<K, kCompactChunks>, grid, dim3(256), st, ev, scores, Epad, \
                   S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, cand, est, cstride, \
-                  C, mm);
+                  C, mm, swar);
     PKV_CR(1) PKV_CR(2) PKV_CR(4) PKV_CR(8) PKV_CR(16)
 #undef PKV_CR
     default: return hipErrorInvalidValue;
