@@ -177,30 +177,41 @@ __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ K, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// Block-wide exclusive scan of a pair of uint32 values (NT threads).
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
+// 4 and 8 within each row of 16 lanes, then the last lane of row 0 (2) added
+// to row 1 (3) and the last lane of row 1 added to rows 2 and 3.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide exclusive scan of a pair of uint32 values (NT threads): DPP
+// scans within each wave, wave totals through LDS.
 // ---------------------------------------------------------------------------
 template <int NT>
 __device__ __forceinline__ uint2 block_exscan2(uint2 v, uint2* s_warp, uint2& total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint2 inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t a = __shfl_up(inc.x, off), b = __shfl_up(inc.y, off);
-    if (lane >= off) { inc.x += a; inc.y += b; }
-  }
-  if (lane == 63) s_warp[wv] = inc;
+  const uint32_t ix = wave_incl_scan(v.x), iy = wave_incl_scan(v.y);
+  if (lane == 63) s_warp[wv] = make_uint2(ix, iy);
   __syncthreads();
   uint2 base = make_uint2(0, 0), tot = make_uint2(0, 0);
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    uint2 t = s_warp[w];
+    const uint2 t = s_warp[w];
     if (w < wv) { base.x += t.x; base.y += t.y; }
     tot.x += t.x; tot.y += t.y;
   }
   __syncthreads();  // s_warp may be reused by the caller
   total = tot;
-  return make_uint2(base.x + inc.x - v.x, base.y + inc.y - v.y);
+  return make_uint2(base.x + ix - v.x, base.y + iy - v.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -550,46 +561,6 @@ __device__ __forceinline__ void load_scores(const uint8_t* sp, uint8_t (&sc)[KPT
 #pragma unroll
     for (int t = 0; t < KPT; ++t) sc[t] = sp[t];
   }
-}
-
-// Block-wide exclusive scan of four uint32 values per thread (NT threads).
-template <int NT>
-__device__ __forceinline__ uint4 block_exscan4(uint4 v, uint4* s_warp, uint4& total) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint4 inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t a = __shfl_up(inc.x, off), b = __shfl_up(inc.y, off);
-    const uint32_t c = __shfl_up(inc.z, off), d = __shfl_up(inc.w, off);
-    if (lane >= off) { inc.x += a; inc.y += b; inc.z += c; inc.w += d; }
-  }
-  if (lane == 63) s_warp[wv] = inc;
-  __syncthreads();
-  uint4 base = make_uint4(0, 0, 0, 0), tot = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint4 t = s_warp[w];
-    if (w < wv) { base.x += t.x; base.y += t.y; base.z += t.z; base.w += t.w; }
-    tot.x += t.x; tot.y += t.y; tot.z += t.z; tot.w += t.w;
-  }
-  __syncthreads();  // s_warp may be reused by the caller
-  total = tot;
-  return make_uint4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z,
-                    base.w + inc.w - v.w);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
-// 4 and 8 within each row of 16 lanes, then the last lane of row 0 (2) added
-// to row 1 (3) and the last lane of row 1 added to rows 2 and 3.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return x;
 }
 
 // Block-wide exclusive scan of two uint32 values per thread (NT threads),
@@ -1234,15 +1205,15 @@ __global__ __launch_bounds__(1024) void k_topk_select_few(
     s_start[tid] = 0;
   }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t acc = 0, before = 0;
-    s_pref[0] = 0;
-    for (int q = 0; q < P; ++q) {
-      acc += s_cnt[q] - s_start[q];
-      s_pref[q + 1] = acc;
-      if (q < p) before += s_start[q];
-    }
-    s_sel[2] = before;
+  if (tid < 64) {
+    // wave 0: prefix of the per-slice member counts, and #(bin > b1) in the
+    // slices before p
+    const uint32_t nq = (tid < P) ? s_cnt[tid] - s_start[tid] : 0u;
+    const uint32_t sb = (tid < P && tid < p) ? s_start[tid] : 0u;
+    const uint32_t inc = wave_incl_scan(nq), sbs = wave_incl_scan(sb);
+    if (tid < P) s_pref[tid + 1] = inc;
+    if (tid == 0) s_pref[0] = 0;
+    if (tid == 63) s_sel[2] = sbs;
   }
   __syncthreads();
   const uint32_t above_before = s_sel[2];
