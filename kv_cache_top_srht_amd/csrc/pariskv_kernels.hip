@@ -1441,10 +1441,32 @@ __global__ __launch_bounds__(1024) void k_topk_fused(
 // Innovations 1: only the selected rows are fetched).  Block = 64 selected
 // rows of one (b, h); 16 lanes per row (16 B of K and of V per lane), 16 row
 // slots x 4 rows.  The G query heads of the KV head are held in registers
-// (pre-multiplied by scale * log2 e), logits reduced across the 16 lanes,
-// softmax statistics combined across slots in LDS; writes per query head a
-// partial (o[128], m, l) in the log2 domain.
+// (pre-multiplied by scale * log2 e), logits summed across the 16 lanes of a
+// row with DPP, softmax statistics per slot; the 16 slots are combined in
+// LDS (wave 0, one row of 16 lanes per query head, forms each slot's factor
+// and the total denominator once).  Writes per query head a partial
+// (o[128], m, l) in the log2 domain.
 // ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum / maximum over the 16 lanes of a row, received by all of them
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dppf<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dppf<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dppf<0x141>(v);  // row_half_mirror
+  v += dppf<0x140>(v);  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  v = fmaxf(v, dppf<0x140>(v));
+  return v;
+}
+
 template <typename T, int G>
 __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, const T* __restrict__ K,
                                                     const T* __restrict__ V, int64_t rows_per_head,
@@ -1455,9 +1477,19 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, con
   const int b = bh / n_kv_heads, h = bh - b * n_kv_heads;
   const int Hq = n_kv_heads * G;
   const int slot = tid >> 4, sub = tid & 15;
-  __shared__ float s_m[16][G], s_l[16][G];
+  __shared__ float s_m[16][G], s_l[16][G], s_f[16][G];
+  __shared__ float s_M[G], s_L[G];
   __shared__ float s_o[16][G][128];
 
+  const int32_t* ib = idx + (int64_t)bh * k;
+  int64_t row[4];
+  bool valid[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = chunk * 64 + slot + 16 * it;
+    valid[it] = r < k;
+    row[it] = (int64_t)ib[valid[it] ? r : k - 1];  // unconditional load, row unused when invalid
+  }
   float q[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -1465,30 +1497,24 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, con
 #pragma unroll
     for (int j = 0; j < 8; ++j) q[g][j] *= qscale;
   }
-  const int32_t* ib = idx + (int64_t)bh * k;
   const T* Kb = K + ((int64_t)bh * rows_per_head << 7) + sub * 8;
   const T* Vb = V + ((int64_t)bh * rows_per_head << 7) + sub * 8;
   float kx[4][8], vx[4][8];
-  bool valid[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int r = chunk * 64 + slot + 16 * it;
-    valid[it] = r < k;
-    const int64_t row = valid[it] ? (int64_t)ib[r] : 0;
-    load8(Kb + (row << 7), kx[it]);
-    load8(Vb + (row << 7), vx[it]);
+    load8(Kb + (row[it] << 7), kx[it]);
+    load8(Vb + (row[it] << 7), vx[it]);
   }
   float lg[4][G];
 #pragma unroll
   for (int it = 0; it < 4; ++it)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float s = 0.0f;
+      float sdot = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s = __builtin_fmaf(q[g][j], kx[it][j], s);
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, 16);
-      lg[it][g] = valid[it] ? s : -INFINITY;
+      for (int j = 0; j < 8; ++j) sdot = __builtin_fmaf(q[g][j], kx[it][j], sdot);
+      sdot = row_sum16(sdot);
+      lg[it][g] = valid[it] ? sdot : -INFINITY;
     }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -1499,33 +1525,37 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, con
     if (m != -INFINITY) {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const float p = exp2f(lg[it][g] - m);
-        l += p;
+        const float pw = exp2f(lg[it][g] - m);
+        l += pw;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = __builtin_fmaf(p, vx[it][j], o[j]);
+        for (int j = 0; j < 8; ++j) o[j] = __builtin_fmaf(pw, vx[it][j], o[j]);
       }
     }
     if (sub == 0) { s_m[slot][g] = m; s_l[slot][g] = l; }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s_o[slot][g][sub * 8 + j] = o[j];
+    reinterpret_cast<float4*>(&s_o[slot][g][sub * 8])[0] = make_float4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<float4*>(&s_o[slot][g][sub * 8])[1] = make_float4(o[4], o[5], o[6], o[7]);
+  }
+  __syncthreads();
+  if (tid < 16 * G) {
+    // row g of 16 lanes, lane s: slot s's factor exp2(m_s - M) and the sum of
+    // the scaled denominators (some slot of the chunk has a valid row)
+    const int g = tid >> 4, sl = tid & 15;
+    const float ms = s_m[sl][g];
+    const float M = row_max16(ms);
+    const float f = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
+    const float lt = row_sum16(f * s_l[sl][g]);
+    s_f[sl][g] = f;
+    if (sl == 0) { s_M[g] = M; s_L[g] = lt; }
   }
   __syncthreads();
   for (int e = tid; e < G * 128; e += 256) {
     const int g = e >> 7, j = e & 127;
-    float M = -INFINITY;
+    float o = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) M = fmaxf(M, s_m[s][g]);
-    float o = 0.0f, l = 0.0f;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const float ms = s_m[s][g];
-      const float f = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
-      o = __builtin_fmaf(f, s_o[s][g][j], o);
-      l = __builtin_fmaf(f, s_l[s][g], l);
-    }
+    for (int sl = 0; sl < 16; ++sl) o = __builtin_fmaf(s_f[sl][g], s_o[sl][g][j], o);
     float* pp = part + (((int64_t)(b * Hq + h * G + g)) * nch + chunk) * kPartStride;
     pp[j] = o;
-    if (j == 0) { pp[128] = M; pp[129] = l; }
+    if (j == 0) { pp[128] = s_M[g]; pp[129] = s_L[g]; }
   }
 }
 
