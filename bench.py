@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--drift-steps", type=int, default=0,
                     help="decode steps of the drift run (default: the workload's)")
     ap.add_argument("--drift-every", type=int, default=1024)
+    ap.add_argument("--uva", choices=["none", "v", "kv"], default="none",
+                    help="keep V (v) or K and V (kv) of every layer in pinned host "
+                         "memory, read by the kernels over the host link")
     return ap.parse_args()
 
 
@@ -116,6 +119,13 @@ def main():
         lay = synth.make_layer(w.scaled(N=cap), dev, layer=l)
         cfg = pk.config_for(w, capacity=cap)
         L = pk.Layer(cfg, lay["signs"], lay["K"], w.N, k=w.k, device=dev)
+        if args.uva != "none":
+            # full-precision rows in pinned host memory, mapped into the GPU's
+            # address space; the device copies are dropped
+            for name in (("V",) if args.uva == "v" else ("K", "V")):
+                hst = torch.empty(lay[name].shape, dtype=lay[name].dtype, pin_memory=True)
+                hst.copy_(lay[name])
+                lay[name] = hst
         layers.append((L, lay))
         torch.cuda.synchronize()
     idx = torch.empty(BH, w.k, dtype=torch.int32, device=dev)
@@ -229,6 +239,8 @@ def main():
             "candidate_fraction": "%d/%d" % (w.cand_num, w.cand_den),
             "candidates_per_head": C, "layers_in_rotation": Lr,
             "parallelism": "single GPU", "launch": mode,
+            "kv_placement": {"none": "HBM", "v": "V in pinned host memory",
+                             "kv": "K and V in pinned host memory"}[args.uva],
         },
         "roofline": {
             "kernel": "vote_scan",
@@ -284,7 +296,7 @@ def main():
     result["recall"] = recall_at_k(pk, torch, np, w, layers[0], idx, cap)
     result["stream_copy"] = stream_copy(torch)
     result["roofline"]["frac_of_stream_copy"] = achieved / result["stream_copy"]["gbps"]
-    if not args.no_dense:
+    if not args.no_dense and args.uva == "none":
         result["dense_attention"] = dense_attention(pk, torch, w, layers[0],
                                                     cap, scale, dt_code)
         result["dense_attention"]["speedup_of_step"] = \
@@ -303,7 +315,7 @@ def exact_topk_rows(torch, w, lay, n):
     for b in range(w.batch):
         for h in range(w.n_kv_heads):
             qs = lay["Q"][b, h * G:(h + 1) * G].float().sum(0)
-            sc = torch.mv(lay["K"][b, h, S:n].float(), qs)
+            sc = torch.mv(lay["K"][b, h, S:n].to(qs.device).float(), qs)
             out.append(torch.topk(sc, kp).indices + S)
     return out
 

@@ -127,7 +127,8 @@ PARISKV_API int32_t pariskv_attn_workspace_bytes(int32_t batch,
  * of every (b, h), asynchronously on `stream`.
  *   srht_signs   host array of head_dim int8 values, each +1 or -1: the
  *                random diagonal D of the rotation c * H * diag(D).  Copied.
- *   K            device, key_dtype, element (b, h, i, j) at
+ *   K            device-accessible (HBM, or mapped pinned host memory read
+ *                over the host link), key_dtype, element (b, h, i, j) at
  *                K[((b * n_kv_heads + h) * k_rows_per_head + i) * d + j].
  *   k_rows_per_head   row stride between consecutive (b, h), >= n_keys.
  * Errors: INVALID_ARG (null pointer, signs not +-1, stride < n_keys),
@@ -143,7 +144,8 @@ PARISKV_API int32_t pariskv_build_index(const pariskv_config *cfg,
 /* Encodes n_new keys per (b, h) and appends them at positions [N, N+n_new)
  * where N is the current size; the host-side size is updated at once, so
  * later calls know N without a device synchronisation.
- *   K_new        device, element (b, h, r, j) at
+ *   K_new        device-accessible (HBM or mapped pinned host memory),
+ *                element (b, h, r, j) at
  *                K_new[((b * n_kv_heads + h) * new_rows_per_head + r) * d + j]
  *                for r < n_new (a pointer into the KV cache at row N with
  *                new_rows_per_head = the cache's rows per head works).
