@@ -146,6 +146,42 @@ def test_ties_duplicates_and_zero_keys(orc):
     L.close()
 
 
+@pytest.mark.parametrize("N,den,k,copies", [
+    (60000, 5, 2048, 8000),     # 3 top-k slices, threshold bin of 8000 equal keys
+    (150000, 2, 4096, 0),       # 75000 candidates: 19 slices, generic select
+    (150000, 2, 4096, 8000),    # 19 slices and the radix select of a tied bin
+])
+def test_topk_paths(orc, N, den, k, copies):
+    """The top-k's other paths: more than 16 slices of 4096 candidates, and a
+    threshold bin holding more than 4096 members (identical keys tie exactly
+    on score and estimate; the lower positions win)."""
+    w = W("topk paths", 1, 1, 4, 128, N, "bf16", cand_num=1, cand_den=den, k=k,
+          seed=33)
+    case("top-k paths N=%d f=1/%d k=%d copies=%d" % (N, den, k, copies))
+    lay = synth.make_layer(w, "cuda")
+    K = lay["K"]
+    if copies:
+        # keys along the group's mean query, scaled up: the top centroid in
+        # every subspace (maximal vote score) and the largest estimates
+        qbar = lay["Q"][0, 0:4].float().mean(0) * 4
+        K[0, 0, 1000:1000 + copies] = qbar.to(K.dtype)
+    cfg = pk.config_for(w)
+    L = pk.Layer(cfg, lay["signs"], K, w.N, k=w.k)
+    idx = torch.empty(1, w.k, dtype=torch.int32, device="cuda")
+    est = torch.empty(1, w.kprime, dtype=torch.float32, device="cuda")
+    L.retrieve(lay["Q"], idx, est)
+    torch.cuda.synchronize()
+    Kh, Qh = host_f32(K), host_f32(lay["Q"])
+    enc = oracle_encode_heads(orc, w, Kh, lay["signs"], [0])
+    ref = oracle_retrieve_heads(orc, w, Qh, enc, lay["signs"], [0])
+    gi = gpu_intermediates(L, 1)
+    assert_retrieval_equal(w, gi, idx.cpu().numpy(), est.cpu().numpy(), ref[0], 0)
+    if copies:
+        # the tied copies fill the top-k in position order
+        assert np.array_equal(idx.cpu().numpy()[0], np.arange(1000, 1000 + w.k))
+    L.close()
+
+
 def test_deterministic_repeat():
     w = SMALL["batched_kpt2"]
     case("determinism")
