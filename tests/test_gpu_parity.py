@@ -32,6 +32,16 @@ SMALL = {
                               k=700, seed=16),
     "batched_kpt2": W("64 heads, 20K keys", 8, 8, 32, 128, 20000, "bf16",
                       k=256, sinks=16, seed=17),
+    # other query-side parameters: scores up to 128 and 240 (the compaction's
+    # byte-wise compare path needs scores below 128), rho = 1 and 2
+    "rho8_tiers8": W("rho 8, tiers 8..1", 1, 2, 8, 128, 30000, "bf16", rho=8,
+                     tiers=(8, 7, 6, 5, 4, 3, 2, 1), k=512, seed=18),
+    "wide_tiers": W("rho 4, tiers 15/10/5/1", 1, 2, 8, 128, 30000, "bf16",
+                    tiers=(15, 10, 5, 1), cand_num=1, cand_den=10, k=512, seed=19),
+    "rho2": W("rho 2, tiers 2/1", 2, 2, 8, 128, 20000, "bf16", rho=2, tiers=(2, 1),
+              k=300, seed=20),
+    "rho1": W("rho 1", 1, 4, 4, 128, 20000, "bf16", rho=1, tiers=(1,),
+              cand_num=1, cand_den=10, k=300, seed=21),
 }
 
 
