@@ -57,6 +57,12 @@ def parse():
     ap.add_argument("--drift-steps", type=int, default=0,
                     help="decode steps of the drift run (default: the workload's)")
     ap.add_argument("--drift-every", type=int, default=1024)
+    ap.add_argument("--rho", type=int, default=0,
+                    help="centroids kept per subspace (default: the workload's); "
+                         "tiers become rho, rho-1, ..., 1 unless --tiers is given")
+    ap.add_argument("--tiers", default="", help="comma-separated tier weights")
+    ap.add_argument("--cand-frac", default="",
+                    help="candidate fraction as num/den (default: the workload's)")
     ap.add_argument("--uva", choices=["none", "v", "kv"], default="none",
                     help="keep V (v) or K and V (kv) of every layer in pinned host "
                          "memory, read by the kernels over the host link")
@@ -107,6 +113,14 @@ def main():
         return
     dev = "cuda"
     w = synth.WORKLOADS[args.workload]
+    if args.rho:
+        w = w.scaled(rho=args.rho, tiers=tuple(range(args.rho, 0, -1)))
+    if args.tiers:
+        t = tuple(int(x) for x in args.tiers.split(","))
+        w = w.scaled(rho=len(t), tiers=t)
+    if args.cand_frac:
+        num, den = (int(x) for x in args.cand_frac.split("/"))
+        w = w.scaled(cand_num=num, cand_den=den)
     K_steps, W_steps, Lr = args.steps, args.warmup, max(1, args.layers)
     per_layer = math.ceil((K_steps + W_steps + args.profile_steps) / Lr) + 1
     cap = w.N + per_layer + max(0, args.warm_steps) + 1
