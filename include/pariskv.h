@@ -86,6 +86,7 @@ typedef struct pariskv_config {
 } pariskv_config;
 
 typedef struct pariskv_index pariskv_index;   /* opaque host-side handle */
+typedef struct pariskv_window pariskv_window; /* opaque host-side handle */
 
 /* Number of stages that pariskv_retrieve_topk_profiled brackets. */
 #define PARISKV_RETRIEVE_STAGES 6
@@ -248,6 +249,74 @@ PARISKV_API int32_t pariskv_sparse_attn_profiled(
     const int32_t *idx, int32_t k, int32_t batch, int32_t n_q_heads,
     int32_t n_kv_heads, int32_t head_dim, int32_t dtype, float scale,
     void *out, void *ws, size_t ws_bytes, void *stream, void **events);
+
+/* ---------------------------------------------------------------------- */
+/* Sliding window.                                                         */
+/* [TS] System-Level Innovations 2: four regions per (b, h) -- Sink (first */
+/* S tokens), Retrieval (indexed; rows may live in host memory), Local     */
+/* (the L most recent tokens before the buffer) and an Update Buffer of up */
+/* to U new tokens.  When the buffer fills, the U oldest Local tokens move */
+/* to Retrieval (rows copied to the far store, keys encoded into the       */
+/* index) and the buffer becomes part of Local.  Attention covers the      */
+/* sinks, the retrieved top-k and every Local and buffer token.  Host-side */
+/* bookkeeping; the caller owns every buffer.                              */
+/* ---------------------------------------------------------------------- */
+
+/* Creates a window over `index`, whose keys [0, S + R) are the sinks and the
+ * retrieval region (R = index size - S).  Positions: sinks [0, S), retrieval
+ * [S, S + R), then the L local tokens [S + R, S + R + L); the buffer is empty.
+ *   K_near, V_near  device [b][h][S + L + U][d] (key_dtype): rows [0, S) hold
+ *                   the sinks; position p >= S + R lives at row
+ *                   S + (p - S) % (L + U).  The caller fills the sinks and
+ *                   the L local rows before the first call.
+ *   K_far, V_far    device-accessible (HBM or mapped pinned host memory)
+ *                   [b][h][far_rows_per_head][d]: position p of the
+ *                   retrieval region at row p.  far_rows_per_head >= the
+ *                   index capacity.
+ *   n_local L, n_update U   U >= 1, L >= U, L a multiple of U.
+ * The window keeps the pointers; they must outlive it.
+ * Errors: INVALID_ARG, NOMEM. */
+PARISKV_API int32_t pariskv_window_create(pariskv_index *index,
+                                          int64_t n_local, int64_t n_update,
+                                          void *K_near, void *V_near,
+                                          void *K_far, void *V_far,
+                                          int64_t far_rows_per_head,
+                                          pariskv_window **out);
+
+/* Appends one token per (b, h) (rows K_new/V_new[(b * n_kv_heads + h) *
+ * new_rows_per_head], device-accessible) to the update buffer; when that
+ * fills the buffer, moves the U oldest local tokens to the retrieval region
+ * (far-store copies and an index encode, asynchronous on `stream`).
+ * Errors: INVALID_ARG, CAPACITY (the index cannot take U more keys), HIP. */
+PARISKV_API int32_t pariskv_window_append(pariskv_window *w, const void *K_new,
+                                          const void *V_new,
+                                          int64_t new_rows_per_head,
+                                          void *stream);
+
+/* Current tokens per (b, h), retrieval-region size R, and the attended
+ * tail L + u (local plus buffer).  Any pointer may be NULL. */
+PARISKV_API int32_t pariskv_window_state(const pariskv_window *w,
+                                         int64_t *n_tokens,
+                                         int64_t *n_retrieval,
+                                         int64_t *n_tail);
+
+/* Bytes of the workspace pariskv_window_attn needs for k listed rows. */
+PARISKV_API int32_t pariskv_window_attn_workspace_bytes(const pariskv_window *w,
+                                                        int32_t k,
+                                                        size_t *bytes);
+
+/* Attention of every query head over the k positions idx (the output of
+ * pariskv_retrieve_topk on the window's index: sinks then retrieved, read
+ * from the near store below S and from the far store above) and the tail
+ * [S + R, S + R + L + u) read from the near store's ring.  Q, out, idx as for
+ * pariskv_sparse_attn; dtype = the index's key_dtype.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+PARISKV_API int32_t pariskv_window_attn(const pariskv_window *w, const void *Q,
+                                        const int32_t *idx, int32_t k,
+                                        float scale, void *out, void *ws,
+                                        size_t ws_bytes, void *stream);
+
+PARISKV_API void pariskv_window_destroy(pariskv_window *w);
 
 /* ---------------------------------------------------------------------- */
 /* Introspection for parity tests (synchronous; not for the hot path).     */

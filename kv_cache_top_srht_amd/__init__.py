@@ -84,6 +84,13 @@ def lib():
             "pariskv_codebook": (i32, [i32, P, P]),
             "pariskv_rot_scale": (C.c_float, [i32]),
             "pariskv_status_string": (C.c_char_p, [i32]),
+            "pariskv_window_create": (i32, [P, i64, i64, P, P, P, P, i64, C.POINTER(P)]),
+            "pariskv_window_append": (i32, [P, P, P, i64, P]),
+            "pariskv_window_state": (i32, [P, C.POINTER(i64), C.POINTER(i64),
+                                           C.POINTER(i64)]),
+            "pariskv_window_attn_workspace_bytes": (i32, [P, i32, C.POINTER(sz)]),
+            "pariskv_window_attn": (i32, [P, P, P, i32, C.c_float, P, P, sz, P]),
+            "pariskv_window_destroy": (None, [P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -208,6 +215,42 @@ def pariskv_retrieve_topk_profiled(handle, Q, k, out_idx, out_est, ws, events,
     _check(lib().pariskv_retrieve_topk_profiled(
         handle, _ptr(Q), int(k), _ptr(out_idx), _ptr(out_est), _ptr(ws),
         _nbytes(ws), _stream(stream), _events(events)))
+
+
+def pariskv_window_create(index_handle, n_local, n_update, K_near, V_near, K_far,
+                          V_far, far_rows_per_head):
+    h = C.c_void_p()
+    _check(lib().pariskv_window_create(index_handle, int(n_local), int(n_update),
+                                       _ptr(K_near), _ptr(V_near), _ptr(K_far),
+                                       _ptr(V_far), int(far_rows_per_head), C.byref(h)))
+    return h
+
+
+def pariskv_window_append(w, K_new, V_new, new_rows_per_head, stream=None):
+    _check(lib().pariskv_window_append(w, _ptr(K_new), _ptr(V_new),
+                                       int(new_rows_per_head), _stream(stream)))
+
+
+def pariskv_window_state(w):
+    """(tokens per (b, h), retrieval-region size R, attended tail L + u)."""
+    a, b, c = C.c_int64(), C.c_int64(), C.c_int64()
+    _check(lib().pariskv_window_state(w, C.byref(a), C.byref(b), C.byref(c)))
+    return a.value, b.value, c.value
+
+
+def pariskv_window_attn_workspace_bytes(w, k) -> int:
+    n = C.c_size_t()
+    _check(lib().pariskv_window_attn_workspace_bytes(w, int(k), C.byref(n)))
+    return n.value
+
+
+def pariskv_window_attn(w, Q, idx, k, scale, out, ws, stream=None):
+    _check(lib().pariskv_window_attn(w, _ptr(Q), _ptr(idx), int(k), C.c_float(scale),
+                                     _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def pariskv_window_destroy(w):
+    lib().pariskv_window_destroy(w)
 
 
 def pariskv_stage_name(s: int):

@@ -23,6 +23,20 @@ struct pariskv_index {
   hipStream_t pending_stream;
 };
 
+// Four-region window over one index (sinks, retrieval, local, update buffer).
+struct pariskv_window {
+  pariskv_index* ix;
+  int64_t S, L, U, ring;  // ring = L + U slots after the S sink rows of the near store
+  uint8_t* Kn;            // near store [BH][S + ring][d]
+  uint8_t* Vn;
+  uint8_t* Kf;            // far store [BH][far_rows][d]
+  uint8_t* Vf;
+  int64_t far_rows;
+  int64_t R;              // keys in the retrieval region [S, S + R): the index holds S + R
+  int64_t u;              // tokens in the update buffer
+  size_t rb;              // bytes per row
+};
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -228,12 +242,13 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   return PARISKV_OK;
 }
 
-int32_t attn_impl(const void* Q, const void* K, const void* V, int64_t rows_per_head,
-                  const int32_t* idx, int32_t k, int32_t batch, int32_t n_q_heads,
-                  int32_t n_kv_heads, int32_t head_dim, int32_t dtype, float scale, void* out,
-                  void* ws, size_t ws_bytes, void* stream, void** events) {
-  if (!Q || !K || !V || !idx || !out || !ws) return PARISKV_ERR_INVALID_ARG;
-  if (k < 1 || batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || rows_per_head < 1)
+// Split-K attention over k listed rows plus rs.tail_n tail rows.
+int32_t attn_core(const void* Q, const pkv::AttnRows& rs, const int32_t* idx, int32_t k,
+                  int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                  int32_t dtype, float scale, void* out, void* ws, size_t ws_bytes, void* stream,
+                  void** events) {
+  if (!Q || !rs.K || !rs.V || !idx || !out || !ws) return PARISKV_ERR_INVALID_ARG;
+  if (k < 1 || batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || rs.rows < 1 || rs.tail_n < 0)
     return PARISKV_ERR_INVALID_ARG;
   if (n_q_heads % n_kv_heads) return PARISKV_ERR_INVALID_ARG;
   if (dtype != PARISKV_DTYPE_BF16 && dtype != PARISKV_DTYPE_FP32) return PARISKV_ERR_INVALID_ARG;
@@ -241,11 +256,13 @@ int32_t attn_impl(const void* Q, const void* K, const void* V, int64_t rows_per_
   const int G = n_q_heads / n_kv_heads;
   if (head_dim != 128 || (G != 1 && G != 2 && G != 4 && G != 8)) return PARISKV_ERR_UNSUPPORTED;
   if ((int64_t)batch * n_kv_heads > 65535) return PARISKV_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)k + rs.tail_n;
+  if (rows > 0x7FFFFFFFll) return PARISKV_ERR_INVALID_ARG;
   size_t need = 0;
-  pariskv_attn_workspace_bytes(batch, n_q_heads, k, head_dim, &need);
+  pariskv_attn_workspace_bytes(batch, n_q_heads, (int32_t)rows, head_dim, &need);
   if (ws_bytes < need) return PARISKV_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  const int nch = (int)ceil_div(k, 64);
+  const int nch = (int)ceil_div(rows, 64);
   const float qscale = scale * 1.4426950408889634f;
   pkv::EvPair e0, e1;
   if (events) {
@@ -255,12 +272,27 @@ int32_t attn_impl(const void* Q, const void* K, const void* V, int64_t rows_per_
     e1.stop = (hipEvent_t)events[3];
   }
   (void)hipGetLastError();
-  hipError_t e = pkv::launch_attn_split(dtype, G, Q, K, V, rows_per_head, idx, k, batch,
-                                        n_kv_heads, qscale, (float*)ws, nch, st, e0);
+  hipError_t e = pkv::launch_attn_split(dtype, G, Q, rs, idx, k, batch, n_kv_heads, qscale,
+                                        (float*)ws, nch, st, e0);
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_attn_merge(dtype, (const float*)ws, nch, batch * n_q_heads, out, st, e1);
   if (e != hipSuccess) return hip_status(e);
   return PARISKV_OK;
+}
+
+int32_t attn_impl(const void* Q, const void* K, const void* V, int64_t rows_per_head,
+                  const int32_t* idx, int32_t k, int32_t batch, int32_t n_q_heads,
+                  int32_t n_kv_heads, int32_t head_dim, int32_t dtype, float scale, void* out,
+                  void* ws, size_t ws_bytes, void* stream, void** events) {
+  pkv::AttnRows rs;
+  rs.K = K;
+  rs.V = V;
+  rs.rows = rows_per_head;
+  rs.K_near = K;  // unused: no near rows, no tail
+  rs.V_near = V;
+  rs.near_rows = rows_per_head;
+  return attn_core(Q, rs, idx, k, batch, n_q_heads, n_kv_heads, head_dim, dtype, scale, out, ws,
+                   ws_bytes, stream, events);
 }
 
 }  // namespace
@@ -478,6 +510,115 @@ int32_t pariskv_debug_intermediate(const pariskv_index* ix, int32_t k, const voi
     default: return PARISKV_ERR_INVALID_ARG;
   }
 }
+
+int32_t pariskv_window_create(pariskv_index* ix, int64_t n_local, int64_t n_update, void* K_near,
+                              void* V_near, void* K_far, void* V_far, int64_t far_rows_per_head,
+                              pariskv_window** out) {
+  if (out) *out = nullptr;
+  if (!ix || !out || !K_near || !V_near || !K_far || !V_far) return PARISKV_ERR_INVALID_ARG;
+  const int64_t S = ix->cfg.n_sink;
+  if (n_update < 1 || n_local < n_update || n_local % n_update) return PARISKV_ERR_INVALID_ARG;
+  if (ix->n < S || far_rows_per_head < ix->cfg.capacity) return PARISKV_ERR_INVALID_ARG;
+  if (n_local + n_update > 0x7FFFFFFFll) return PARISKV_ERR_INVALID_ARG;
+  pariskv_window* w = new (std::nothrow) pariskv_window;
+  if (!w) return PARISKV_ERR_NOMEM;
+  w->ix = ix;
+  w->S = S;
+  w->L = n_local;
+  w->U = n_update;
+  w->ring = n_local + n_update;
+  w->Kn = (uint8_t*)K_near;
+  w->Vn = (uint8_t*)V_near;
+  w->Kf = (uint8_t*)K_far;
+  w->Vf = (uint8_t*)V_far;
+  w->far_rows = far_rows_per_head;
+  w->R = ix->n - S;
+  w->u = 0;
+  w->rb = (size_t)ix->cfg.head_dim * (ix->cfg.key_dtype == PARISKV_DTYPE_BF16 ? 2 : 4);
+  *out = w;
+  return PARISKV_OK;
+}
+
+int32_t pariskv_window_append(pariskv_window* w, const void* K_new, const void* V_new,
+                              int64_t new_rows_per_head, void* stream) {
+  if (!w || !K_new || !V_new || new_rows_per_head < 1) return PARISKV_ERR_INVALID_ARG;
+  pariskv_index* ix = w->ix;
+  if (w->u + 1 == w->U && ix->n + w->U > ix->cfg.capacity) return PARISKV_ERR_CAPACITY;
+  const int64_t BH = (int64_t)ix->cfg.batch * ix->cfg.n_kv_heads;
+  const size_t rb = w->rb, near_pitch = (size_t)(w->S + w->ring) * rb;
+  hipStream_t st = (hipStream_t)stream;
+  // the new token's row goes to its ring slot in the near store
+  const int64_t p = w->S + w->R + w->L + w->u;
+  const int64_t slot = w->S + (p - w->S) % w->ring;
+  (void)hipGetLastError();
+  hipError_t e = hipMemcpy2DAsync(w->Kn + slot * rb, near_pitch, K_new, new_rows_per_head * rb, rb,
+                                  BH, hipMemcpyDefault, st);
+  if (e == hipSuccess)
+    e = hipMemcpy2DAsync(w->Vn + slot * rb, near_pitch, V_new, new_rows_per_head * rb, rb, BH,
+                         hipMemcpyDefault, st);
+  if (e != hipSuccess) return PARISKV_ERR_HIP;
+  if (++w->u < w->U) return PARISKV_OK;
+  // update buffer full: the U oldest local tokens [S + R, S + R + U) move to the
+  // retrieval region.  Their ring slots are contiguous (R and ring are
+  // multiples of U); their rows are copied to the far store and their keys
+  // encoded into the index now (the next token reuses the first slot).
+  const int64_t pos0 = w->S + w->R, slot0 = w->S + w->R % w->ring;
+  const size_t far_pitch = (size_t)w->far_rows * rb;
+  e = hipMemcpy2DAsync(w->Kf + pos0 * rb, far_pitch, w->Kn + slot0 * rb, near_pitch, w->U * rb,
+                       BH, hipMemcpyDefault, st);
+  if (e == hipSuccess)
+    e = hipMemcpy2DAsync(w->Vf + pos0 * rb, far_pitch, w->Vn + slot0 * rb, near_pitch,
+                         w->U * rb, BH, hipMemcpyDefault, st);
+  if (e != hipSuccess) return PARISKV_ERR_HIP;
+  if (int32_t rc = flush_pending(ix)) return rc;
+  e = pkv::launch_encode(ix->cfg.key_dtype, w->Kn + slot0 * rb, w->S + w->ring, ix->n, w->U,
+                         (int)BH, ix->cfg.capacity, ix->ids, ix->rec, ix->signs, ix->rot_c, st,
+                         pkv::EvPair{});
+  if (e != hipSuccess) return PARISKV_ERR_HIP;
+  ix->n += w->U;
+  ix->last = st;
+  w->R += w->U;
+  w->u = 0;
+  return PARISKV_OK;
+}
+
+int32_t pariskv_window_state(const pariskv_window* w, int64_t* n_tokens, int64_t* n_retrieval,
+                             int64_t* n_tail) {
+  if (!w) return PARISKV_ERR_INVALID_ARG;
+  if (n_tokens) *n_tokens = w->S + w->R + w->L + w->u;
+  if (n_retrieval) *n_retrieval = w->R;
+  if (n_tail) *n_tail = w->L + w->u;
+  return PARISKV_OK;
+}
+
+int32_t pariskv_window_attn_workspace_bytes(const pariskv_window* w, int32_t k, size_t* bytes) {
+  if (!w || !bytes || k < 1) return PARISKV_ERR_INVALID_ARG;
+  const pariskv_config* c = &w->ix->cfg;
+  const int64_t rows = (int64_t)k + w->L + w->U;
+  if (rows > 0x7FFFFFFFll) return PARISKV_ERR_INVALID_ARG;
+  return pariskv_attn_workspace_bytes(c->batch, c->n_q_heads, (int32_t)rows, c->head_dim, bytes);
+}
+
+int32_t pariskv_window_attn(const pariskv_window* w, const void* Q, const int32_t* idx, int32_t k,
+                            float scale, void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!w) return PARISKV_ERR_INVALID_ARG;
+  const pariskv_config* c = &w->ix->cfg;
+  pkv::AttnRows rs;
+  rs.K = w->Kf;
+  rs.V = w->Vf;
+  rs.rows = w->far_rows;
+  rs.K_near = w->Kn;
+  rs.V_near = w->Vn;
+  rs.near_rows = w->S + w->ring;
+  rs.n_near_head = w->S;
+  rs.ring = w->ring;
+  rs.tail_lo = w->S + w->R;
+  rs.tail_n = (int)(w->L + w->u);
+  return attn_core(Q, rs, idx, k, c->batch, c->n_q_heads, c->n_kv_heads, c->head_dim,
+                   c->key_dtype, scale, out, ws, ws_bytes, stream, nullptr);
+}
+
+void pariskv_window_destroy(pariskv_window* w) { delete w; }
 
 int32_t pariskv_codebook(int32_t m, float* L, float* tau) {
   if (!L || !tau) return PARISKV_ERR_INVALID_ARG;

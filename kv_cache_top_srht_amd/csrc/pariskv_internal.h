@@ -74,11 +74,26 @@ constexpr int kTopkFusedSlices = 1;
 constexpr int kTopkFewSlices = 16;
 // split-K attention partial per (query head, chunk): o[128], m, l, 2 unused
 constexpr int kPartStride = 132;
-hipError_t launch_attn_split(int dtype, int G, const void* Q, const void* K, const void* V,
-                             int64_t rows_per_head, const int32_t* idx, int k, int batch,
-                             int n_kv_heads, float qscale, float* part, int nch,
-                             hipStream_t st,
-                         const EvPair& ev);
+// Where attention rows come from.  Listed positions p (from idx) are read
+// from the near store when p < n_near_head, else from the far store; the
+// tail_n rows after the list are positions tail_lo + t, read from the near
+// store's ring at n_near_head + (p - n_near_head) % ring.  Plain sparse
+// attention: far store only (n_near_head = 0, tail_n = 0).
+struct AttnRows {
+  const void* K = nullptr;       // far store [b][h][rows][d]
+  const void* V = nullptr;
+  int64_t rows = 0;
+  const void* K_near = nullptr;  // near store [b][h][near_rows][d]
+  const void* V_near = nullptr;
+  int64_t near_rows = 0;
+  int64_t n_near_head = 0;       // positions [0, n_near_head) live in the near store
+  int64_t ring = 1;
+  int64_t tail_lo = 0;
+  int tail_n = 0;
+};
+hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs,
+                             const int32_t* idx, int k, int batch, int n_kv_heads, float qscale,
+                             float* part, int nch, hipStream_t st, const EvPair& ev);
 hipError_t launch_attn_merge(int dtype, const float* part, int nch, int rows, void* out,
                              hipStream_t st,
                          const EvPair& ev);

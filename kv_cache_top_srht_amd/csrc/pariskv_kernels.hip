@@ -1468,8 +1468,7 @@ __device__ __forceinline__ float row_max16(float v) {
 }
 
 template <typename T, int G>
-__global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, const T* __restrict__ K,
-                                                    const T* __restrict__ V, int64_t rows_per_head,
+__global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, AttnRows rs,
                                                     const int32_t* __restrict__ idx, int k,
                                                     int n_kv_heads, float qscale,
                                                     float* __restrict__ part, int nch) {
@@ -1481,14 +1480,28 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, con
   __shared__ float s_M[G], s_L[G];
   __shared__ float s_o[16][G][128];
 
+  // rows r < k are the positions idx[r] (positions below n_near_head in the
+  // near store, the rest in the far store); rows k .. k + tail_n - 1 are the
+  // positions tail_lo + (r - k), in the near store's ring
+  const int n_rows = k + rs.tail_n;
   const int32_t* ib = idx + (int64_t)bh * k;
   int64_t row[4];
-  bool valid[4];
+  bool valid[4], near[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int r = chunk * 64 + slot + 16 * it;
-    valid[it] = r < k;
-    row[it] = (int64_t)ib[valid[it] ? r : k - 1];  // unconditional load, row unused when invalid
+    valid[it] = r < n_rows;
+    const bool listed = r < k;
+    const int64_t p = listed ? (int64_t)ib[r < k ? r : k - 1]  // unconditional load
+                             : rs.tail_lo + (r - k);
+    if (listed) {
+      near[it] = p < rs.n_near_head;
+      row[it] = p;
+    } else {
+      near[it] = true;
+      row[it] = rs.n_near_head + (p - rs.n_near_head) % rs.ring;
+    }
+    if (!valid[it]) { near[it] = false; row[it] = 0; }
   }
   float q[G][8];
 #pragma unroll
@@ -1497,13 +1510,15 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, con
 #pragma unroll
     for (int j = 0; j < 8; ++j) q[g][j] *= qscale;
   }
-  const T* Kb = K + ((int64_t)bh * rows_per_head << 7) + sub * 8;
-  const T* Vb = V + ((int64_t)bh * rows_per_head << 7) + sub * 8;
+  const T* Kf = (const T*)rs.K + ((int64_t)bh * rs.rows << 7) + sub * 8;
+  const T* Vf = (const T*)rs.V + ((int64_t)bh * rs.rows << 7) + sub * 8;
+  const T* Kn = (const T*)rs.K_near + ((int64_t)bh * rs.near_rows << 7) + sub * 8;
+  const T* Vn = (const T*)rs.V_near + ((int64_t)bh * rs.near_rows << 7) + sub * 8;
   float kx[4][8], vx[4][8];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    load8(Kb + (row[it] << 7), kx[it]);
-    load8(Vb + (row[it] << 7), vx[it]);
+    load8((near[it] ? Kn : Kf) + (row[it] << 7), kx[it]);
+    load8((near[it] ? Vn : Vf) + (row[it] << 7), vx[it]);
   }
   float lg[4][G];
 #pragma unroll
@@ -1755,14 +1770,13 @@ hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cs
                 out_idx, out_est);
 }
 
-hipError_t launch_attn_split(int dtype, int G, const void* Q, const void* K, const void* V,
-                             int64_t rows_per_head, const int32_t* idx, int k, int batch,
-                             int n_kv_heads, float qscale, float* part, int nch, hipStream_t st,
-                             const EvPair& ev) {
+hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs,
+                             const int32_t* idx, int k, int batch, int n_kv_heads, float qscale,
+                             float* part, int nch, hipStream_t st, const EvPair& ev) {
   const dim3 grid(nch, batch * n_kv_heads);
 #define PKV_AS(T, GG)                                                                         \
-  return launch(k_attn_split<T, GG>, grid, dim3(256), st, ev, (const T*)Q, (const T*)K,     \
-                (const T*)V, rows_per_head, idx, k, n_kv_heads, qscale, part, nch)
+  return launch(k_attn_split<T, GG>, grid, dim3(256), st, ev, (const T*)Q, rs, idx, k,      \
+                n_kv_heads, qscale, part, nch)
   if (dtype == 0) {
     switch (G) {
       case 1: PKV_AS(uint16_t, 1);
