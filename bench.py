@@ -63,6 +63,10 @@ def parse():
     ap.add_argument("--tiers", default="", help="comma-separated tier weights")
     ap.add_argument("--cand-frac", default="",
                     help="candidate fraction as num/den (default: the workload's)")
+    ap.add_argument("--window", default="",
+                    help="L,U: sliding-window regions with L local tokens and an "
+                         "update buffer of U; the far store is HBM, or pinned host "
+                         "memory with --uva kv")
     ap.add_argument("--uva", choices=["none", "v", "kv"], default="none",
                     help="keep V (v) or K and V (kv) of every layer in pinned host "
                          "memory, read by the kernels over the host link")
@@ -128,12 +132,42 @@ def main():
     print("[bench] workload=%s layers=%d cap=%d steps=%d warmup=%d" %
           (args.workload, Lr, cap, K_steps, W_steps), file=sys.stderr, flush=True)
 
+    win_L = win_U = 0
+    if args.window:
+        win_L, win_U = (int(x) for x in args.window.split(","))
+        if args.uva == "v":
+            sys.exit("--window keeps K and V together: use --uva kv or none")
     layers = []
     for l in range(Lr):
         lay = synth.make_layer(w.scaled(N=cap), dev, layer=l)
         cfg = pk.config_for(w, capacity=cap)
-        L = pk.Layer(cfg, lay["signs"], lay["K"], w.N, k=w.k, device=dev)
-        if args.uva != "none":
+        L = pk.Layer(cfg, lay["signs"], lay["K"], w.N - win_L, k=w.k, device=dev)
+        if args.window:
+            # near store: sinks, then the ring of local + buffer rows; far store:
+            # the layer's own K/V (positions at their rows), moved to pinned
+            # host memory with --uva kv
+            S, ring = w.sinks, win_L + win_U
+            shp = (w.batch, w.n_kv_heads, S + ring, w.d)
+            Kn = torch.zeros(shp, dtype=lay["K"].dtype, device=dev)
+            Vn = torch.zeros_like(Kn)
+            Kn[:, :, :S], Vn[:, :, :S] = lay["K"][:, :, :S], lay["V"][:, :, :S]
+            pos = torch.arange(w.N - win_L, w.N, device=dev)
+            slots = S + (pos - S) % ring
+            Kn[:, :, slots] = lay["K"][:, :, pos]
+            Vn[:, :, slots] = lay["V"][:, :, pos]
+            lay["Kn"], lay["Vn"] = Kn, Vn
+            if args.uva == "kv":
+                for name in ("K", "V"):
+                    hst = torch.empty(lay[name].shape, dtype=lay[name].dtype,
+                                      pin_memory=True)
+                    hst.copy_(lay[name])
+                    lay[name] = hst
+            lay["win"] = pk.pariskv_window_create(L.handle, win_L, win_U, Kn, Vn,
+                                                  lay["K"], lay["V"], cap)
+            lay["win_ws"] = torch.empty(
+                pk.pariskv_window_attn_workspace_bytes(lay["win"], w.k),
+                dtype=torch.uint8, device=dev)
+        if args.uva != "none" and not args.window:
             # full-precision rows in pinned host memory, mapped into the GPU's
             # address space; the device copies are dropped
             for name in (("V",) if args.uva == "v" else ("K", "V")):
@@ -150,6 +184,21 @@ def main():
 
     def step(t, ev=None):
         L, lay = layers[t % Lr]
+        if args.window:
+            n = pk.pariskv_window_state(lay["win"])[0]
+            pk.pariskv_window_append(lay["win"], lay["K"][:, :, n:], lay["V"][:, :, n:],
+                                     cap)
+            E_of.append(L.size - w.sinks)
+            if ev is None:
+                L.retrieve(lay["Q"], idx)
+                pk.pariskv_window_attn(lay["win"], lay["Q"], idx, w.k, scale, out,
+                                       lay["win_ws"])
+            else:
+                pk.pariskv_retrieve_topk_profiled(L.handle, lay["Q"], w.k, idx, None,
+                                                  L.ws, ev[0:12])
+                pk.pariskv_window_attn_profiled(lay["win"], lay["Q"], idx, w.k, scale,
+                                                out, lay["win_ws"], ev[12:16])
+            return
         n = L.size
         L.append(lay["K"][:, :, n:], 1, rows_per_head=cap)
         E_of.append(L.size - w.sinks)
@@ -255,6 +304,9 @@ def main():
             "parallelism": "single GPU", "launch": mode,
             "kv_placement": {"none": "HBM", "v": "V in pinned host memory",
                              "kv": "K and V in pinned host memory"}[args.uva],
+            "window": ({"sinks": w.sinks, "local": win_L, "update_buffer": win_U,
+                        "far_store": "pinned host memory" if args.uva == "kv" else "HBM"}
+                       if args.window else None),
         },
         "roofline": {
             "kernel": "vote_scan",
@@ -310,7 +362,7 @@ def main():
     result["recall"] = recall_at_k(pk, torch, np, w, layers[0], idx, cap)
     result["stream_copy"] = stream_copy(torch)
     result["roofline"]["frac_of_stream_copy"] = achieved / result["stream_copy"]["gbps"]
-    if not args.no_dense and args.uva == "none":
+    if not args.no_dense and args.uva == "none" and not args.window:
         result["dense_attention"] = dense_attention(pk, torch, w, layers[0],
                                                     cap, scale, dt_code)
         result["dense_attention"]["speedup_of_step"] = \

@@ -316,6 +316,16 @@ PARISKV_API int32_t pariskv_window_attn(const pariskv_window *w, const void *Q,
                                         float scale, void *out, void *ws,
                                         size_t ws_bytes, void *stream);
 
+/* Same as pariskv_window_attn, and times its two kernels: events holds 4
+ * caller-created hipEvent_t, stamped as by pariskv_sparse_attn_profiled.
+ * Not for use under stream capture. */
+PARISKV_API int32_t pariskv_window_attn_profiled(const pariskv_window *w,
+                                                 const void *Q,
+                                                 const int32_t *idx, int32_t k,
+                                                 float scale, void *out,
+                                                 void *ws, size_t ws_bytes,
+                                                 void *stream, void **events);
+
 PARISKV_API void pariskv_window_destroy(pariskv_window *w);
 
 /* ---------------------------------------------------------------------- */

@@ -90,6 +90,8 @@ def lib():
                                            C.POINTER(i64)]),
             "pariskv_window_attn_workspace_bytes": (i32, [P, i32, C.POINTER(sz)]),
             "pariskv_window_attn": (i32, [P, P, P, i32, C.c_float, P, P, sz, P]),
+            "pariskv_window_attn_profiled": (i32, [P, P, P, i32, C.c_float, P, P, sz, P,
+                                                   C.POINTER(P)]),
             "pariskv_window_destroy": (None, [P]),
         }
         for name, (res, args) in sig.items():
@@ -247,6 +249,13 @@ def pariskv_window_attn_workspace_bytes(w, k) -> int:
 def pariskv_window_attn(w, Q, idx, k, scale, out, ws, stream=None):
     _check(lib().pariskv_window_attn(w, _ptr(Q), _ptr(idx), int(k), C.c_float(scale),
                                      _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def pariskv_window_attn_profiled(w, Q, idx, k, scale, out, ws, events, stream=None):
+    _check(lib().pariskv_window_attn_profiled(w, _ptr(Q), _ptr(idx), int(k),
+                                              C.c_float(scale), _ptr(out), _ptr(ws),
+                                              _nbytes(ws), _stream(stream),
+                                              _events(events)))
 
 
 def pariskv_window_destroy(w):

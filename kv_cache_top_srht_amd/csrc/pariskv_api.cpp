@@ -599,8 +599,9 @@ int32_t pariskv_window_attn_workspace_bytes(const pariskv_window* w, int32_t k, 
   return pariskv_attn_workspace_bytes(c->batch, c->n_q_heads, (int32_t)rows, c->head_dim, bytes);
 }
 
-int32_t pariskv_window_attn(const pariskv_window* w, const void* Q, const int32_t* idx, int32_t k,
-                            float scale, void* out, void* ws, size_t ws_bytes, void* stream) {
+static int32_t window_attn_impl(const pariskv_window* w, const void* Q, const int32_t* idx, int32_t k,
+                         float scale, void* out, void* ws, size_t ws_bytes, void* stream,
+                         void** events) {
   if (!w) return PARISKV_ERR_INVALID_ARG;
   const pariskv_config* c = &w->ix->cfg;
   pkv::AttnRows rs;
@@ -615,7 +616,21 @@ int32_t pariskv_window_attn(const pariskv_window* w, const void* Q, const int32_
   rs.tail_lo = w->S + w->R;
   rs.tail_n = (int)(w->L + w->u);
   return attn_core(Q, rs, idx, k, c->batch, c->n_q_heads, c->n_kv_heads, c->head_dim,
-                   c->key_dtype, scale, out, ws, ws_bytes, stream, nullptr);
+                   c->key_dtype, scale, out, ws, ws_bytes, stream, events);
+}
+
+int32_t pariskv_window_attn(const pariskv_window* w, const void* Q, const int32_t* idx, int32_t k,
+                            float scale, void* out, void* ws, size_t ws_bytes, void* stream) {
+  return window_attn_impl(w, Q, idx, k, scale, out, ws, ws_bytes, stream, nullptr);
+}
+
+int32_t pariskv_window_attn_profiled(const pariskv_window* w, const void* Q, const int32_t* idx,
+                                     int32_t k, float scale, void* out, void* ws,
+                                     size_t ws_bytes, void* stream, void** events) {
+  if (!events) return PARISKV_ERR_INVALID_ARG;
+  for (int s = 0; s < 4; ++s)
+    if (!events[s]) return PARISKV_ERR_INVALID_ARG;
+  return window_attn_impl(w, Q, idx, k, scale, out, ws, ws_bytes, stream, events);
 }
 
 void pariskv_window_destroy(pariskv_window* w) { delete w; }
