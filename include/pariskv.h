@@ -69,6 +69,11 @@ extern "C" {
  *                G in {1, 2, 4, 8}).  batch * n_kv_heads <= 65535.
  *   key_dtype    PARISKV_DTYPE_BF16 or _FP32, the dtype of K and Q.
  *   capacity     maximum keys per (batch, KV head) the index can hold.
+ *   per_query_head  0: one retrieval per (batch, KV head) with the group's
+ *                mean query (the default).  1: unshared retrieval, one per
+ *                (batch, query head) with that head's own query, over its KV
+ *                head's index; out_idx / out_est then hold n_q_heads rows per
+ *                batch entry.  batch * n_q_heads <= 65535.
  */
 typedef struct pariskv_config {
     int32_t head_dim;
@@ -83,6 +88,7 @@ typedef struct pariskv_config {
     int32_t n_q_heads;
     int32_t key_dtype;
     int64_t capacity;
+    int32_t per_query_head;
 } pariskv_config;
 
 typedef struct pariskv_index pariskv_index;   /* opaque host-side handle */
@@ -249,6 +255,16 @@ PARISKV_API int32_t pariskv_sparse_attn_profiled(
     const int32_t *idx, int32_t k, int32_t batch, int32_t n_q_heads,
     int32_t n_kv_heads, int32_t head_dim, int32_t dtype, float scale,
     void *out, void *ws, size_t ws_bytes, void *stream, void **events);
+
+/* Attention with an index list per query head (idx [batch][n_q_heads][k],
+ * e.g. from a per_query_head retrieval): query head q attends to its own k
+ * rows of KV head q / G.  Other arguments and errors as pariskv_sparse_attn;
+ * the workspace is pariskv_attn_workspace_bytes(batch, n_q_heads, k, d). */
+PARISKV_API int32_t pariskv_sparse_attn_per_query_head(
+    const void *Q, const void *K, const void *V, int64_t kv_rows_per_head,
+    const int32_t *idx, int32_t k, int32_t batch, int32_t n_q_heads,
+    int32_t n_kv_heads, int32_t head_dim, int32_t dtype, float scale,
+    void *out, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Sliding window.                                                         */

@@ -44,6 +44,7 @@ class pariskv_config(C.Structure):
         ("n_q_heads", C.c_int32),
         ("key_dtype", C.c_int32),
         ("capacity", C.c_int64),
+        ("per_query_head", C.c_int32),
     ]
 
 
@@ -84,6 +85,9 @@ def lib():
             "pariskv_codebook": (i32, [i32, P, P]),
             "pariskv_rot_scale": (C.c_float, [i32]),
             "pariskv_status_string": (C.c_char_p, [i32]),
+            "pariskv_sparse_attn_per_query_head": (i32, [P, P, P, i64, P, i32, i32, i32,
+                                                         i32, i32, i32, C.c_float, P, P,
+                                                         sz, P]),
             "pariskv_window_create": (i32, [P, i64, i64, P, P, P, P, i64, C.POINTER(P)]),
             "pariskv_window_append": (i32, [P, P, P, i64, P]),
             "pariskv_window_state": (i32, [P, C.POINTER(i64), C.POINTER(i64),
@@ -138,7 +142,8 @@ def _events(events):
 
 def make_config(*, head_dim=128, n_subspaces=16, rho=4, tiers=(4, 3, 2, 1),
                 cand_num=1, cand_den=20, n_sink=0, batch=1, n_kv_heads=8,
-                n_q_heads=32, key_dtype=PARISKV_DTYPE_BF16, capacity):
+                n_q_heads=32, key_dtype=PARISKV_DTYPE_BF16, capacity,
+                per_query_head=False):
     c = pariskv_config()
     c.head_dim, c.n_subspaces, c.rho = head_dim, n_subspaces, rho
     for i in range(8):
@@ -146,6 +151,7 @@ def make_config(*, head_dim=128, n_subspaces=16, rho=4, tiers=(4, 3, 2, 1),
     c.cand_num, c.cand_den, c.n_sink = cand_num, cand_den, n_sink
     c.batch, c.n_kv_heads, c.n_q_heads = batch, n_kv_heads, n_q_heads
     c.key_dtype, c.capacity = key_dtype, int(capacity)
+    c.per_query_head = 1 if per_query_head else 0
     return c
 
 
@@ -157,7 +163,8 @@ def config_for(w, capacity=None):
                        n_q_heads=w.n_q_heads,
                        key_dtype=PARISKV_DTYPE_BF16 if w.dtype == "bf16"
                        else PARISKV_DTYPE_FP32,
-                       capacity=capacity or w.N)
+                       capacity=capacity or w.N,
+                       per_query_head=getattr(w, "per_query_head", False))
 
 
 # ------------------------------------------------------------ C entry points
@@ -217,6 +224,15 @@ def pariskv_retrieve_topk_profiled(handle, Q, k, out_idx, out_est, ws, events,
     _check(lib().pariskv_retrieve_topk_profiled(
         handle, _ptr(Q), int(k), _ptr(out_idx), _ptr(out_est), _ptr(ws),
         _nbytes(ws), _stream(stream), _events(events)))
+
+
+def pariskv_sparse_attn_per_query_head(Q, K, V, kv_rows_per_head, idx, k, batch,
+                                       n_q_heads, n_kv_heads, head_dim, dtype, scale, out,
+                                       ws, stream=None):
+    _check(lib().pariskv_sparse_attn_per_query_head(
+        _ptr(Q), _ptr(K), _ptr(V), int(kv_rows_per_head), _ptr(idx), int(k), int(batch),
+        int(n_q_heads), int(n_kv_heads), int(head_dim), int(dtype), C.c_float(scale),
+        _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def pariskv_window_create(index_handle, n_local, n_update, K_near, V_near, K_far,
@@ -343,7 +359,8 @@ class Layer:
         import torch
         self.cfg = cfg
         self.k = int(k)
-        self.BH = cfg.batch * cfg.n_kv_heads
+        # retrieval units: (b, KV head), or (b, query head) when unshared
+        self.BH = cfg.batch * (cfg.n_q_heads if cfg.per_query_head else cfg.n_kv_heads)
         self.index_buf = torch.empty(pariskv_index_bytes(cfg), dtype=torch.uint8,
                                      device=device)
         self.ws = torch.empty(pariskv_retrieve_workspace_bytes(cfg, self.k),
@@ -370,10 +387,10 @@ class Layer:
 
     def attend(self, Q, K, V, idx, out, scale=None, stream=None):
         c = self.cfg
-        pariskv_sparse_attn(Q, K, V, K.shape[2], idx, self.k, c.batch,
-                            c.n_q_heads, c.n_kv_heads, c.head_dim, c.key_dtype,
-                            scale if scale is not None else c.head_dim ** -0.5,
-                            out, self.attn_ws, stream)
+        fn = pariskv_sparse_attn_per_query_head if c.per_query_head else pariskv_sparse_attn
+        fn(Q, K, V, K.shape[2], idx, self.k, c.batch, c.n_q_heads, c.n_kv_heads,
+           c.head_dim, c.key_dtype, scale if scale is not None else c.head_dim ** -0.5,
+           out, self.attn_ws, stream)
 
     def close(self):
         if self.handle:

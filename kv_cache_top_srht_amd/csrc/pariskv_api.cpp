@@ -44,6 +44,14 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// retrieval units: one per (b, KV head), or per (b, query head) when unshared
+int64_t units_of(const pariskv_config* c) {
+  return (int64_t)c->batch * (c->per_query_head ? c->n_q_heads : c->n_kv_heads);
+}
+int unit_div_of(const pariskv_config* c) {
+  return c->per_query_head ? c->n_q_heads / c->n_kv_heads : 1;
+}
+
 int64_t cand_count(int64_t E, int64_t kprime, int64_t num, int64_t den) {
   int64_t c = (E * num + den - 1) / den;
   if (c < kprime) c = kprime;
@@ -76,7 +84,9 @@ int32_t check_cfg(const pariskv_config* c) {
     return PARISKV_ERR_INVALID_ARG;
   if (c->capacity < 1 || c->capacity > 0x7FFFFFFFll || c->n_sink >= c->capacity)
     return PARISKV_ERR_INVALID_ARG;
+  if (c->per_query_head != 0 && c->per_query_head != 1) return PARISKV_ERR_INVALID_ARG;
   if ((int64_t)c->batch * c->n_kv_heads > 65535) return PARISKV_ERR_UNSUPPORTED;
+  if (units_of(c) > 65535) return PARISKV_ERR_UNSUPPORTED;
   // kernels of this build: d = 128 split into 16 subspaces of 8, and 1, 2, 4
   // or 8 query heads per KV head
   if (d != 128 || m != 8) return PARISKV_ERR_UNSUPPORTED;
@@ -106,7 +116,7 @@ struct WsLayout {
 };
 
 WsLayout ws_layout(const pariskv_config* c, int64_t k) {
-  const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
+  const int64_t BH = units_of(c);  // workspace rows: one per retrieval unit
   const int64_t Emax = c->capacity - c->n_sink;
   int64_t kp = k - c->n_sink;
   if (kp > Emax) kp = Emax;
@@ -185,8 +195,11 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
       return rc;
     }
   }
-  const int BH = c->batch * c->n_kv_heads;
-  const int G = c->n_q_heads / c->n_kv_heads;
+  const int BH = (int)units_of(c);  // retrieval units
+  const int udiv = unit_div_of(c);
+  // a unit's query: the mean of its G query heads, or its own head when unshared
+  const int G = c->per_query_head ? 1 : c->n_q_heads / c->n_kv_heads;
+  const int units_per_batch = c->per_query_head ? c->n_q_heads : c->n_kv_heads;
   const int64_t E = N - S, kp = k - S;
   const int64_t C = cand_count(E, kp, c->cand_num, c->cand_den);
   if (C > 1024ll * pkv::kTopkSlice) return PARISKV_ERR_UNSUPPORTED;  // > 4M candidates per head
@@ -222,18 +235,18 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   };
   (void)hipGetLastError();  // launches below report only their own errors
   hipError_t e;
-  e = pkv::launch_qprep(c->key_dtype, Q, BH, c->n_kv_heads, G, ix->signs, ix->rot_c, c->rho, tw,
-                        lut, yq, ptab, app, st, ev(0));
+  e = pkv::launch_qprep(c->key_dtype, Q, BH, units_per_batch, G, ix->signs, ix->rot_c, c->rho, tw,
+                        lut, yq, ptab, app, udiv, st, ev(0));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_scan(kpt, nch, BH, ix->ids, c->capacity, S, E, lut, scores, L.Epad, chist,
-                       (int)L.nchunks_max, L.nbins, L.rstride, st, ev(1));
+                       (int)L.nchunks_max, L.nbins, L.rstride, udiv, st, ev(1));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, L.rstride, C, meta, coff,
                          st, ev(2));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_compact_rerank(kpt, nch, BH, scores, L.Epad, S, E, meta, coff,
                                  (int)L.nchunks_max, ptab, ix->rec, c->capacity, cand, est,
-                                 L.cstride, C, mmc, L.nbins, st, ev(3));
+                                 L.cstride, C, mmc, L.nbins, udiv, st, ev(3));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_topk(BH, est, cand, L.cstride, (int)C, (int)kp, (int)S, k, P, mmc,
                        (int)L.nchunks_max, nch, range, rows, tkmeta, sorted, out_idx, out_est, st,
@@ -422,6 +435,26 @@ int32_t pariskv_retrieve_topk_profiled(const pariskv_index* ix, const void* Q, i
   return retrieve_impl(ix, Q, k, out_idx, out_est, ws, ws_bytes, stream, events);
 }
 
+int32_t pariskv_sparse_attn_per_query_head(const void* Q, const void* K, const void* V,
+                                           int64_t kv_rows_per_head, const int32_t* idx,
+                                           int32_t k, int32_t batch, int32_t n_q_heads,
+                                           int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                                           float scale, void* out, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  if (n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads) return PARISKV_ERR_INVALID_ARG;
+  pkv::AttnRows rs;
+  rs.K = K;
+  rs.V = V;
+  rs.rows = kv_rows_per_head;
+  rs.K_near = K;
+  rs.V_near = V;
+  rs.near_rows = kv_rows_per_head;
+  rs.unit_div = n_q_heads / n_kv_heads;  // query head q reads KV head q / G
+  // each query head is its own attention unit with one query row
+  return attn_core(Q, rs, idx, k, batch, n_q_heads, n_q_heads, head_dim, dtype, scale, out, ws,
+                   ws_bytes, stream, nullptr);
+}
+
 const char* pariskv_stage_name(int32_t s) {
   static const char* names[PARISKV_RETRIEVE_STAGES] = {
       "query_prep", "vote_scan", "threshold", "compact_rerank", "topk", "topk_second_pass"};
@@ -489,7 +522,7 @@ int32_t pariskv_debug_intermediate(const pariskv_index* ix, int32_t k, const voi
   if (!ws || !host_dst) return PARISKV_ERR_INVALID_ARG;
   const WsLayout L = ws_layout(&ix->cfg, k);
   if (ws_bytes < L.total) return PARISKV_ERR_WORKSPACE;
-  const int64_t BH = (int64_t)ix->cfg.batch * ix->cfg.n_kv_heads;
+  const int64_t BH = units_of(&ix->cfg);  // one row per retrieval unit
   const uint8_t* base = (const uint8_t*)ws;
   if (hipDeviceSynchronize() != hipSuccess) return PARISKV_ERR_HIP;
   auto rows = [&](size_t off, int64_t stride, int64_t len, int64_t elem) -> int32_t {

@@ -45,12 +45,12 @@ hipError_t launch_encode(int dtype, const void* K, int64_t rows_per_head, int64_
                          float c, hipStream_t st, const EvPair& ev);
 hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
                         const SignMask& sg, float c, int rho, const Tiers& tw, uint8_t* lut,
-                        float* yq, float* ptab, const AppendJob& app, hipStream_t st,
-                        const EvPair& ev);
+                        float* yq, float* ptab, const AppendJob& app, int unit_div,
+                        hipStream_t st, const EvPair& ev);
 hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t cap, int64_t S,
                        int64_t E, const uint8_t* lut, uint8_t* scores, int64_t Epad,
                        uint32_t* chist, int chunk_stride, int nbins, int rstride,
-                       hipStream_t st, const EvPair& ev);
+                       int unit_div, hipStream_t st, const EvPair& ev);
 hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nchunks, int nbins,
                          int rstride, int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st,
                          const EvPair& ev);
@@ -59,7 +59,7 @@ hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* sc
                                  const uint32_t* coff, int chunk_stride, const float* ptab,
                                  const uint32_t* rec, int64_t cap, int32_t* cand, float* est,
                                  int64_t cstride, int64_t C, uint32_t* mm, int nbins,
-                                 hipStream_t st, const EvPair& ev);
+                                 int unit_div, hipStream_t st, const EvPair& ev);
 hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cstride, int C,
                        int kprime, int S, int k, int P, const uint32_t* mmc, int chunk_stride,
                        int nchunks, uint32_t* range, uint32_t* rows, int32_t* tkmeta,
@@ -90,6 +90,7 @@ struct AttnRows {
   int64_t ring = 1;
   int64_t tail_lo = 0;
   int tail_n = 0;
+  int unit_div = 1;              // attention units (blocks.y) per KV head of K and V
 };
 hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs,
                              const int32_t* idx, int k, int batch, int n_kv_heads, float qscale,

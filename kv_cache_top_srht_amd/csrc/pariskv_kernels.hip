@@ -260,7 +260,11 @@ template <typename T, int G>
 __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_kv_heads,
                                                 float invG, SignMask sg, float c, int rho, Tiers tw,
                                                 uint8_t* __restrict__ lut_out, float* __restrict__ yq_out,
-                                                float* __restrict__ ptab_out, AppendJob app) {
+                                                float* __restrict__ ptab_out, AppendJob app,
+                                                int unit_div) {
+  // one block per retrieval unit: a (b, KV head), or a (b, query head) with
+  // unit_div = G units per KV head (then G = 1 here and n_kv_heads counts
+  // units per batch entry)
   const int bh = blockIdx.x;
   const int b = bh / n_kv_heads, h = bh - b * n_kv_heads;
   const int Hq = n_kv_heads * G;
@@ -268,11 +272,11 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
   __shared__ float s_yq[128];
   // keys appended since the last retrieval are encoded here (threads 256+,
   // 16 per key), so the vote scan that follows sees them
-  if (app.n > 0 && tid >= 256) {
+  if (app.n > 0 && tid >= 256 && bh % unit_div == 0) {
     const int r = (tid - 256) >> 4;
     if (r < app.n)
-      encode_key((const T*)app.K, app.rows_per_head, bh, r, app.lo + r, app.cap, app.ids,
-                 app.rec, sg, c, tid & 15);
+      encode_key((const T*)app.K, app.rows_per_head, bh / unit_div, r, app.lo + r, app.cap,
+                 app.ids, app.rec, sg, c, tid & 15);
   }
   if (tid < 16) {
     const int sub = tid;
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(NT) void k_scan(const uint4* __restrict__ ids, int6
                                              int64_t E, const uint8_t* __restrict__ lut,
                                              uint8_t* __restrict__ scores, int64_t Epad,
                                              uint32_t* __restrict__ chist, int chunk_stride, int nbins,
-                                             int rstride) {
+                                             int rstride, int unit_div) {
   constexpr int NW = NT / 64;
   const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   __shared__ uint8_t s_lut[16 * 256];
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(NT) void k_scan(const uint4* __restrict__ ids, int6
   // each wait down to the loads it needs.
   uint4 lutv = make_uint4(0, 0, 0, 0);
   if (tid < 256) lutv = reinterpret_cast<const uint4*>(lut + (int64_t)bh * 4096)[tid];
-  const uint4* src = ids + bh * cap + S;
+  const uint4* src = ids + (int64_t)(bh / unit_div) * cap + S;  // the unit's KV head
   const int64_t p0 = (int64_t)chunk * (KPT * NT) + tid;
   uint4 x[KPT];
 #pragma unroll
@@ -646,7 +650,8 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
     const int32_t* __restrict__ meta, const uint32_t* __restrict__ coff, int chunk_stride,
     int nchunks, const float* __restrict__ ptab, const uint32_t* __restrict__ rec,
     int64_t cap, int32_t* __restrict__ cand,
-    float* __restrict__ est, int64_t cstride, int64_t C, uint32_t* __restrict__ mm, int swar) {
+    float* __restrict__ est, int64_t cstride, int64_t C, uint32_t* __restrict__ mm, int swar,
+    int unit_div) {
   constexpr int CH = KPT * 256;
   const int bh = blockIdx.y, tid = threadIdx.x;
   const int c0 = blockIdx.x * CPB;
@@ -731,7 +736,7 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
   // w_b p_b for them; DPP broadcasts give every lane all 16 terms, summed in
   // b order.  Up to 4 candidates per group are fetched before any is used.
   const int q = tid & 3;
-  const uint32_t* rq = rec + (int64_t)bh * cap * 32;
+  const uint32_t* rq = rec + (int64_t)(bh / unit_div) * cap * 32;  // the unit's KV head
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;  // order keys of this block's estimates
   for (uint32_t j0 = 0; j0 < ntot; j0 += 256) {
     uint4 cw[4];
@@ -1510,10 +1515,11 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
 #pragma unroll
     for (int j = 0; j < 8; ++j) q[g][j] *= qscale;
   }
-  const T* Kf = (const T*)rs.K + ((int64_t)bh * rs.rows << 7) + sub * 8;
-  const T* Vf = (const T*)rs.V + ((int64_t)bh * rs.rows << 7) + sub * 8;
-  const T* Kn = (const T*)rs.K_near + ((int64_t)bh * rs.near_rows << 7) + sub * 8;
-  const T* Vn = (const T*)rs.V_near + ((int64_t)bh * rs.near_rows << 7) + sub * 8;
+  const int64_t kvh = bh / rs.unit_div;  // the KV head whose rows this block reads
+  const T* Kf = (const T*)rs.K + ((int64_t)kvh * rs.rows << 7) + sub * 8;
+  const T* Vf = (const T*)rs.V + ((int64_t)kvh * rs.rows << 7) + sub * 8;
+  const T* Kn = (const T*)rs.K_near + ((int64_t)kvh * rs.near_rows << 7) + sub * 8;
+  const T* Vn = (const T*)rs.V_near + ((int64_t)kvh * rs.near_rows << 7) + sub * 8;
   float kx[4][8], vx[4][8];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
@@ -1665,12 +1671,12 @@ hipError_t launch_encode(int dtype, const void* K, int64_t rows_per_head, int64_
 
 hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
                         const SignMask& sg, float c, int rho, const Tiers& tw, uint8_t* lut,
-                        float* yq, float* ptab, const AppendJob& app, hipStream_t st,
-                        const EvPair& ev) {
+                        float* yq, float* ptab, const AppendJob& app, int unit_div,
+                        hipStream_t st, const EvPair& ev) {
   const float invG = 1.0f / (float)G;
 #define PKV_QP(T, GG)                                                                        \
   return launch(k_qprep<T, GG>, dim3(BH), dim3(1024), st, ev, (const T*)Q, n_kv_heads, invG, \
-                sg, c, rho, tw, lut, yq, ptab, app)
+                sg, c, rho, tw, lut, yq, ptab, app, unit_div)
   if (dtype == 0) {
     switch (G) {
       case 1: PKV_QP(uint16_t, 1);
@@ -1692,8 +1698,8 @@ hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
 
 hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t cap, int64_t S,
                        int64_t E, const uint8_t* lut, uint8_t* scores, int64_t Epad,
-                       uint32_t* chist, int chunk_stride, int nbins, int rstride, hipStream_t st,
-                       const EvPair& ev) {
+                       uint32_t* chist, int chunk_stride, int nbins, int rstride, int unit_div,
+                       hipStream_t st, const EvPair& ev) {
   // a chunk is kpt * 256 keys; the scan covers it with kScanThreads threads
   const dim3 grid(nchunks, BH);
   const uint4* id4 = (const uint4*)ids;
@@ -1702,15 +1708,15 @@ hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t
 #define PKV_SCAN(K)                                                                          \
   case K:                                                                                    \
     return launch(k_scan<(K * 256) / NT, NT>, grid, dim3(NT), st, ev, id4, cap, S, E, lut,   \
-                  scores, Epad, chist, chunk_stride, nbins, rstride);
+                  scores, Epad, chist, chunk_stride, nbins, rstride, unit_div);
     PKV_SCAN(4) PKV_SCAN(8) PKV_SCAN(16)
 #undef PKV_SCAN
     case 1:
       return launch(k_scan<1, 256>, grid, dim3(256), st, ev, id4, cap, S, E, lut, scores, Epad,
-                    chist, chunk_stride, nbins, rstride);
+                    chist, chunk_stride, nbins, rstride, unit_div);
     case 2:
       return launch(k_scan<2, 256>, grid, dim3(256), st, ev, id4, cap, S, E, lut, scores, Epad,
-                    chist, chunk_stride, nbins, rstride);
+                    chist, chunk_stride, nbins, rstride, unit_div);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1727,7 +1733,7 @@ hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* sc
                                  const uint32_t* coff, int chunk_stride, const float* ptab,
                                  const uint32_t* rec, int64_t cap, int32_t* cand, float* est,
                                  int64_t cstride, int64_t C, uint32_t* mm, int nbins,
-                                 hipStream_t st, const EvPair& ev) {
+                                 int unit_div, hipStream_t st, const EvPair& ev) {
   const int swar = nbins <= 128 ? 1 : 0;  // every score below 128
   const dim3 grid((nchunks + kCompactChunks - 1) / kCompactChunks, BH);
   switch (kpt) {
@@ -1735,7 +1741,7 @@ hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* sc
   case K:                                                                                    \
     return launch(k_compact_rerank<K, kCompactChunks>, grid, dim3(256), st, ev, scores, Epad, \
                   S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, cand, est, cstride, \
-                  C, mm, swar);
+                  C, mm, swar, unit_div);
     PKV_CR(1) PKV_CR(2) PKV_CR(4) PKV_CR(8) PKV_CR(16)
 #undef PKV_CR
     default: return hipErrorInvalidValue;

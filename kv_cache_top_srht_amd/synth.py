@@ -51,6 +51,7 @@ class Workload:
     decode_steps: int = 0  # drift workload: keys appended one per step
     drift_channels: int = 16
     drift_sigma: float = 1.5
+    per_query_head: bool = False  # unshared retrieval: one per query head
 
     @property
     def m(self) -> int:

@@ -72,7 +72,7 @@ def test_sizes(pk):
     ("n_subspaces", 7, -1), ("rho", 0, -1), ("rho", 9, -1),
     ("cand_num", 0, -1), ("cand_den", 0, -1), ("n_q_heads", 30, -1),
     ("key_dtype", 5, -1), ("capacity", 0, -1), ("n_sink", -1, -1),
-    ("n_q_heads", 24, -2), ("n_q_heads", 128, -2),
+    ("n_q_heads", 24, -2), ("n_q_heads", 128, -2), ("per_query_head", 2, -1),
 ])
 def test_config_validation(pk, field, value, rc):
     c = pk.make_config(capacity=4096)
