@@ -67,6 +67,9 @@ def parse():
                     help="L,U: sliding-window regions with L local tokens and an "
                          "update buffer of U; the far store is HBM, or pinned host "
                          "memory with --uva kv")
+    ap.add_argument("--per-query-head", action="store_true",
+                    help="unshared retrieval: every query head selects its own "
+                         "top-k with its own query over its KV head's index")
     ap.add_argument("--uva", choices=["none", "v", "kv"], default="none",
                     help="keep V (v) or K and V (kv) of every layer in pinned host "
                          "memory, read by the kernels over the host link")
@@ -125,10 +128,16 @@ def main():
     if args.cand_frac:
         num, den = (int(x) for x in args.cand_frac.split("/"))
         w = w.scaled(cand_num=num, cand_den=den)
+    if args.per_query_head:
+        if args.window:
+            sys.exit("--per-query-head runs without --window")
+        w = w.scaled(per_query_head=True)
     K_steps, W_steps, Lr = args.steps, args.warmup, max(1, args.layers)
     per_layer = math.ceil((K_steps + W_steps + args.profile_steps) / Lr) + 1
     cap = w.N + per_layer + max(0, args.warm_steps) + 1
-    BH = w.batch * w.n_kv_heads
+    # retrieval units: one per (batch, KV head), or per (batch, query head)
+    # in the unshared mode
+    U = w.batch * (w.n_q_heads if w.per_query_head else w.n_kv_heads)
     print("[bench] workload=%s layers=%d cap=%d steps=%d warmup=%d" %
           (args.workload, Lr, cap, K_steps, W_steps), file=sys.stderr, flush=True)
 
@@ -176,7 +185,7 @@ def main():
                 lay[name] = hst
         layers.append((L, lay))
         torch.cuda.synchronize()
-    idx = torch.empty(BH, w.k, dtype=torch.int32, device=dev)
+    idx = torch.empty(U, w.k, dtype=torch.int32, device=dev)
     out = torch.empty_like(layers[0][1]["Q"])
     scale = w.d ** -0.5
     dt_code = pk.PARISKV_DTYPE_BF16 if w.dtype == "bf16" else pk.PARISKV_DTYPE_FP32
@@ -210,10 +219,10 @@ def main():
             # the 2 attention kernels, stamped by the dispatches themselves
             pk.pariskv_retrieve_topk_profiled(L.handle, lay["Q"], w.k, idx, None,
                                               L.ws, ev[0:12])
-            pk.pariskv_sparse_attn_profiled(lay["Q"], lay["K"], lay["V"], cap, idx,
-                                            w.k, w.batch, w.n_q_heads,
-                                            w.n_kv_heads, w.d, dt_code, scale, out,
-                                            L.attn_ws, ev[12:16])
+            attn = (pk.pariskv_sparse_attn_per_query_head_profiled if w.per_query_head
+                    else pk.pariskv_sparse_attn_profiled)
+            attn(lay["Q"], lay["K"], lay["V"], cap, idx, w.k, w.batch, w.n_q_heads,
+                 w.n_kv_heads, w.d, dt_code, scale, out, L.attn_ws, ev[12:16])
 
     for t in range(W_steps):
         step(t)
@@ -263,20 +272,21 @@ def main():
                         for t in range(P)]) * 1e3
     E_of[:] = E_timed
     E = np.array(E_of, dtype=np.float64)
-    keys_scanned = float(E.sum() * BH)
+    keys_scanned = float(E.sum() * U)
     value = keys_scanned / wall
     us_per_step = wall / K_steps * 1e6
 
-    scan_bytes = 16.0 * E_prof.mean() * BH
+    scan_bytes = 16.0 * E_prof.mean() * U
     scan_us = float(kern[:, 1].mean())
     achieved = scan_bytes / (scan_us * 1e-6) / 1e9
-    traffic = read_traffic("vote_scan_%s_traffic.txt" % args.workload, scan_bytes)
+    traffic = read_traffic("vote_scan_%s%s_traffic.txt" % (
+        args.workload, "_per_query_head" if w.per_query_head else ""), scan_bytes)
     row_bytes = 2 * w.d * (2 if w.dtype == "bf16" else 4) + 4
-    attn_bytes = float(BH * w.k * row_bytes + 2 * w.batch * w.n_q_heads * w.d *
+    attn_bytes = float(U * w.k * row_bytes + 2 * w.batch * w.n_q_heads * w.d *
                        (2 if w.dtype == "bf16" else 4))
     attn_us = float(kern[:, 6].mean())
     C = pk.pariskv_retrieve_sizes(layers[0][0].handle, w.k)[1]
-    rerank_bytes = 96.0 * C * BH
+    rerank_bytes = 96.0 * C * U
     rerank_us = float(kern[:, 3].mean())
 
     result = {
@@ -301,6 +311,8 @@ def main():
             "rho": w.rho, "tiers": list(w.tiers),
             "candidate_fraction": "%d/%d" % (w.cand_num, w.cand_den),
             "candidates_per_head": C, "layers_in_rotation": Lr,
+            "retrieval": ("per query head (%d units)" % U if w.per_query_head
+                          else "shared by the %d query heads of a KV head" % w.G),
             "parallelism": "single GPU", "launch": mode,
             "kv_placement": {"none": "HBM", "v": "V in pinned host memory",
                              "kv": "K and V in pinned host memory"}[args.uva],
@@ -362,23 +374,31 @@ def main():
     result["recall"] = recall_at_k(pk, torch, np, w, layers[0], idx, cap)
     result["stream_copy"] = stream_copy(torch)
     result["roofline"]["frac_of_stream_copy"] = achieved / result["stream_copy"]["gbps"]
-    if not args.no_dense and args.uva == "none" and not args.window:
+    if not args.no_dense and args.uva == "none" and not args.window \
+            and not w.per_query_head:
         result["dense_attention"] = dense_attention(pk, torch, w, layers[0],
                                                     cap, scale, dt_code)
         result["dense_attention"]["speedup_of_step"] = \
             result["dense_attention"]["us"] / us_per_step
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not w.per_query_head:
         result["cpu_baseline"] = cpu_baseline(w, layers[0][1], args.cpu_steps)
     print(json.dumps(result), flush=True)
 
 
 def exact_topk_rows(torch, w, lay, n):
     """Exact top-k' positions in [S, n) of the group-summed logits
-    sum_g <q_g, k_i> (fp32, on the GPU) for every (batch, KV head)."""
+    sum_g <q_g, k_i> (fp32, on the GPU) for every (batch, KV head), or of
+    each query head's own logits <q_h, k_i> in the unshared mode."""
     S, kp = w.sinks, w.k - w.sinks
     G = w.G
     out = []
     for b in range(w.batch):
+        if w.per_query_head:
+            for hq in range(w.n_q_heads):
+                q = lay["Q"][b, hq].float()
+                sc = torch.mv(lay["K"][b, hq // G, S:n].to(q.device).float(), q)
+                out.append(torch.topk(sc, kp).indices + S)
+            continue
         for h in range(w.n_kv_heads):
             qs = lay["Q"][b, h * G:(h + 1) * G].float().sum(0)
             sc = torch.mv(lay["K"][b, h, S:n].to(qs.device).float(), qs)
@@ -400,8 +420,10 @@ def recall_at_k(pk, torch, np, w, layer, idx, cap):
         rec.append(float(torch.isin(got, ex).sum().item()) / kp)
     return {"k": w.k, "mean": float(np.mean(rec)), "min": float(np.min(rec)),
             "heads": len(rec), "context": int(L.size),
-            "reference": "exact top-k' of the group-summed logits sum_g <q_g, k_i> "
-                         "over [sinks, N), fp32"}
+            "reference": ("exact top-k' of each query head's logits <q_h, k_i>"
+                          if w.per_query_head else
+                          "exact top-k' of the group-summed logits sum_g <q_g, k_i>")
+                         + " over [sinks, N), fp32"}
 
 
 def drift_run(args, pk, synth, np, torch):

@@ -266,6 +266,13 @@ PARISKV_API int32_t pariskv_sparse_attn_per_query_head(
     int32_t n_kv_heads, int32_t head_dim, int32_t dtype, float scale,
     void *out, void *ws, size_t ws_bytes, void *stream);
 
+/* Same, timing its two kernels as pariskv_sparse_attn_profiled does. */
+PARISKV_API int32_t pariskv_sparse_attn_per_query_head_profiled(
+    const void *Q, const void *K, const void *V, int64_t kv_rows_per_head,
+    const int32_t *idx, int32_t k, int32_t batch, int32_t n_q_heads,
+    int32_t n_kv_heads, int32_t head_dim, int32_t dtype, float scale,
+    void *out, void *ws, size_t ws_bytes, void *stream, void **events);
+
 /* ---------------------------------------------------------------------- */
 /* Sliding window.                                                         */
 /* [TS] System-Level Innovations 2: four regions per (b, h) -- Sink (first */

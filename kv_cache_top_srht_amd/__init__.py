@@ -88,6 +88,9 @@ def lib():
             "pariskv_sparse_attn_per_query_head": (i32, [P, P, P, i64, P, i32, i32, i32,
                                                          i32, i32, i32, C.c_float, P, P,
                                                          sz, P]),
+            "pariskv_sparse_attn_per_query_head_profiled": (
+                i32, [P, P, P, i64, P, i32, i32, i32, i32, i32, i32, C.c_float, P, P, sz, P,
+                      C.POINTER(P)]),
             "pariskv_window_create": (i32, [P, i64, i64, P, P, P, P, i64, C.POINTER(P)]),
             "pariskv_window_append": (i32, [P, P, P, i64, P]),
             "pariskv_window_state": (i32, [P, C.POINTER(i64), C.POINTER(i64),
@@ -233,6 +236,15 @@ def pariskv_sparse_attn_per_query_head(Q, K, V, kv_rows_per_head, idx, k, batch,
         _ptr(Q), _ptr(K), _ptr(V), int(kv_rows_per_head), _ptr(idx), int(k), int(batch),
         int(n_q_heads), int(n_kv_heads), int(head_dim), int(dtype), C.c_float(scale),
         _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def pariskv_sparse_attn_per_query_head_profiled(Q, K, V, kv_rows_per_head, idx, k,
+                                                batch, n_q_heads, n_kv_heads, head_dim,
+                                                dtype, scale, out, ws, events, stream=None):
+    _check(lib().pariskv_sparse_attn_per_query_head_profiled(
+        _ptr(Q), _ptr(K), _ptr(V), int(kv_rows_per_head), _ptr(idx), int(k), int(batch),
+        int(n_q_heads), int(n_kv_heads), int(head_dim), int(dtype), C.c_float(scale),
+        _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream), _events(events)))
 
 
 def pariskv_window_create(index_handle, n_local, n_update, K_near, V_near, K_far,

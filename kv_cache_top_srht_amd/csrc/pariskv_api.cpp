@@ -435,12 +435,11 @@ int32_t pariskv_retrieve_topk_profiled(const pariskv_index* ix, const void* Q, i
   return retrieve_impl(ix, Q, k, out_idx, out_est, ws, ws_bytes, stream, events);
 }
 
-int32_t pariskv_sparse_attn_per_query_head(const void* Q, const void* K, const void* V,
-                                           int64_t kv_rows_per_head, const int32_t* idx,
-                                           int32_t k, int32_t batch, int32_t n_q_heads,
-                                           int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
-                                           float scale, void* out, void* ws, size_t ws_bytes,
-                                           void* stream) {
+static int32_t attn_per_head_impl(const void* Q, const void* K, const void* V,
+                                  int64_t kv_rows_per_head, const int32_t* idx, int32_t k,
+                                  int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int32_t dtype, float scale, void* out,
+                                  void* ws, size_t ws_bytes, void* stream, void** events) {
   if (n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads) return PARISKV_ERR_INVALID_ARG;
   pkv::AttnRows rs;
   rs.K = K;
@@ -452,7 +451,29 @@ int32_t pariskv_sparse_attn_per_query_head(const void* Q, const void* K, const v
   rs.unit_div = n_q_heads / n_kv_heads;  // query head q reads KV head q / G
   // each query head is its own attention unit with one query row
   return attn_core(Q, rs, idx, k, batch, n_q_heads, n_q_heads, head_dim, dtype, scale, out, ws,
-                   ws_bytes, stream, nullptr);
+                   ws_bytes, stream, events);
+}
+
+int32_t pariskv_sparse_attn_per_query_head(const void* Q, const void* K, const void* V,
+                                           int64_t kv_rows_per_head, const int32_t* idx,
+                                           int32_t k, int32_t batch, int32_t n_q_heads,
+                                           int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                                           float scale, void* out, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  return attn_per_head_impl(Q, K, V, kv_rows_per_head, idx, k, batch, n_q_heads, n_kv_heads,
+                            head_dim, dtype, scale, out, ws, ws_bytes, stream, nullptr);
+}
+
+int32_t pariskv_sparse_attn_per_query_head_profiled(
+    const void* Q, const void* K, const void* V, int64_t kv_rows_per_head, const int32_t* idx,
+    int32_t k, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+    int32_t dtype, float scale, void* out, void* ws, size_t ws_bytes, void* stream,
+    void** events) {
+  if (!events) return PARISKV_ERR_INVALID_ARG;
+  for (int s = 0; s < 4; ++s)
+    if (!events[s]) return PARISKV_ERR_INVALID_ARG;
+  return attn_per_head_impl(Q, K, V, kv_rows_per_head, idx, k, batch, n_q_heads, n_kv_heads,
+                            head_dim, dtype, scale, out, ws, ws_bytes, stream, events);
 }
 
 const char* pariskv_stage_name(int32_t s) {

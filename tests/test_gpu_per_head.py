@@ -67,4 +67,15 @@ def test_per_query_head_retrieval(orc, name):
         ref_o = orc.attention(Qh[b, hq:hq + 1], Kh[b, hq // G], Vh[b, hq // G], ih[u],
                               w.d ** -0.5)
         assert np.max(np.abs(oh[b, hq] - ref_o[0])) <= ATTN_TOL_BF16
+    # the event-timed entry point runs the same kernels
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    out2 = torch.empty_like(Q)
+    pk.pariskv_sparse_attn_per_query_head_profiled(
+        Q, K, V, w.N, idx, w.k, w.batch, w.n_q_heads, w.n_kv_heads, w.d,
+        pk.PARISKV_DTYPE_BF16, w.d ** -0.5, out2, L.attn_ws, ev)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out)
+    assert ev[0].elapsed_time(ev[1]) > 0
     L.close()
