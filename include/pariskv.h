@@ -55,12 +55,15 @@ extern "C" {
 /*
  * Method parameters and shapes.  Validated by every call that takes it.
  *   head_dim     d, a power of two (this build: 128).
- *   n_subspaces  B; m = d / B coordinates per subspace (this build: m = 8).
- *                [TS] Coarse Candidate Generation: "split into B subspaces".
+ *   n_subspaces  B; m = d / B contiguous coordinates per subspace, each
+ *                with 2^m sign-pattern centroids ([TS] Coarse Candidate
+ *                Generation; this build: m = 8, B = 16, or m = 4, B = 32).
  *   rho          centroids the query keeps per subspace, 1..8.
  *   tier_w[s]    vote weight of the query's (s+1)-th ranked centroid,
- *                0..255, with B * max(tier_w) <= 255 ("tiered weights").
- *   cand_num/den candidate fraction f = num/den, 0 < num <= den ("top 5-10%").
+ *                0..255, with B * max(tier_w) <= 255 (the tiered votes of
+ *                [TS] Coarse Candidate Generation).
+ *   cand_num/den candidate fraction f = num/den, 0 < num <= den (the pages
+ *                keep the top 5 to 10 per cent).
  *                C = min(E, max(k', ceil(E f))), E = N - S, k' = k - S.
  *   n_sink       S: keys [0, S) are always selected and are not scored.
  *   batch, n_kv_heads, n_q_heads   n_q_heads % n_kv_heads == 0; the
@@ -102,9 +105,11 @@ typedef struct pariskv_window pariskv_window; /* opaque host-side handle */
 /* ---------------------------------------------------------------------- */
 
 /* Bytes of the device index buffer for `cfg`: per key and (b, h), 16 B of
- * bucket ids and a 128-byte record holding the 64 B of RSQ-IP codes and the
- * 32 B of fp16 calibration factors (one aligned line per key, so a rerank
- * gather touches one line), for `capacity` keys.
+ * bucket ids (byte s = the sign bits of coordinates 8 s .. 8 s + 7: one id
+ * for m = 8, two 4-bit ids for m = 4) and a 128-byte record holding the
+ * 64 B of RSQ-IP codes and the B fp16 calibration factors (32 B for m = 8,
+ * 64 B for m = 4; one aligned line per key, so a rerank gather touches one
+ * line), for `capacity` keys.
  * Errors: INVALID_ARG / UNSUPPORTED for a bad config. */
 PARISKV_API int32_t pariskv_index_bytes(const pariskv_config *cfg,
                                         size_t *bytes);
@@ -366,7 +371,9 @@ PARISKV_API int32_t pariskv_debug_export(const pariskv_index *index,
 
 /* Intermediates of the last pariskv_retrieve_topk that used `ws` (same
  * index, same k), copied to host after a device synchronisation.
- *   which = 0: vote LUT   uint8 [b][h][B][2^m]
+ *   which = 0: vote table uint8 [b][h][16][256], the one the scan reads:
+ *              row s is indexed by byte s of a key's ids; m = 8: subspace
+ *              s's LUT; m = 4: entry v = LUT_{2s}[v & 15] + LUT_{2s+1}[v >> 4]
  *           1: yq         float [b][h][d] (rotated group query)
  *           2: scores     uint8 [b][h][E]  (E = N - S)
  *           3: cand       int32 [b][h][C]  ascending key positions

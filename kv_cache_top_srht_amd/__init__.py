@@ -329,10 +329,10 @@ def pariskv_retrieve_sizes(handle, k):
     return E.value, Cn.value
 
 
-def pariskv_debug_intermediate(handle, k, ws, which, BH, B=16, d=128):
+def pariskv_debug_intermediate(handle, k, ws, which, BH, d=128):
     E, Cn = pariskv_retrieve_sizes(handle, k)
     shape, dt = {
-        DEBUG_LUT: ((BH, B, 256), np.uint8),
+        DEBUG_LUT: ((BH, 16, 256), np.uint8),   # the scan's byte-indexed table
         DEBUG_YQ: ((BH, d), np.float32),
         DEBUG_SCORES: ((BH, E), np.uint8),
         DEBUG_CAND: ((BH, Cn), np.int32),

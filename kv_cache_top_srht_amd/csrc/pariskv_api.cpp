@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "pariskv.h"
 #include "pariskv_internal.h"
@@ -65,6 +66,9 @@ int max_tier(const pariskv_config* c) {
   return mx;
 }
 
+// coordinates per subspace
+int m_of(const pariskv_config* c) { return c->head_dim / c->n_subspaces; }
+
 int32_t check_cfg(const pariskv_config* c) {
   if (!c) return PARISKV_ERR_INVALID_ARG;
   const int d = c->head_dim;
@@ -87,9 +91,9 @@ int32_t check_cfg(const pariskv_config* c) {
   if (c->per_query_head != 0 && c->per_query_head != 1) return PARISKV_ERR_INVALID_ARG;
   if ((int64_t)c->batch * c->n_kv_heads > 65535) return PARISKV_ERR_UNSUPPORTED;
   if (units_of(c) > 65535) return PARISKV_ERR_UNSUPPORTED;
-  // kernels of this build: d = 128 split into 16 subspaces of 8, and 1, 2, 4
-  // or 8 query heads per KV head
-  if (d != 128 || m != 8) return PARISKV_ERR_UNSUPPORTED;
+  // kernels of this build: d = 128 split into 16 subspaces of 8 or 32 of 4,
+  // and 1, 2, 4 or 8 query heads per KV head
+  if (d != 128 || (m != 8 && m != 4)) return PARISKV_ERR_UNSUPPORTED;
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PARISKV_ERR_UNSUPPORTED;
   return PARISKV_OK;
@@ -167,9 +171,10 @@ int32_t flush_pending(pariskv_index* ix) {
   ix->pending.n = 0;
   const int BH = ix->cfg.batch * ix->cfg.n_kv_heads;
   (void)hipGetLastError();
-  return hip_status(pkv::launch_encode(ix->cfg.key_dtype, job.K, job.rows_per_head, job.lo, job.n,
-                                       BH, ix->cfg.capacity, ix->ids, ix->rec, ix->signs,
-                                       ix->rot_c, ix->pending_stream, pkv::EvPair{}));
+  return hip_status(pkv::launch_encode(m_of(&ix->cfg), ix->cfg.key_dtype, job.K,
+                                       job.rows_per_head, job.lo, job.n, BH, ix->cfg.capacity,
+                                       ix->ids, ix->rec, ix->signs, ix->rot_c,
+                                       ix->pending_stream, pkv::EvPair{}));
 }
 
 int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t* out_idx,
@@ -235,8 +240,8 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   };
   (void)hipGetLastError();  // launches below report only their own errors
   hipError_t e;
-  e = pkv::launch_qprep(c->key_dtype, Q, BH, units_per_batch, G, ix->signs, ix->rot_c, c->rho, tw,
-                        lut, yq, ptab, app, udiv, st, ev(0));
+  e = pkv::launch_qprep(m_of(c), c->key_dtype, Q, BH, units_per_batch, G, ix->signs, ix->rot_c,
+                        c->rho, tw, lut, yq, ptab, app, udiv, st, ev(0));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_scan(kpt, nch, BH, ix->ids, c->capacity, S, E, lut, scores, L.Epad, chist,
                        (int)L.nchunks_max, L.nbins, L.rstride, udiv, st, ev(1));
@@ -244,7 +249,7 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, L.rstride, C, meta, coff,
                          st, ev(2));
   if (e != hipSuccess) return hip_status(e);
-  e = pkv::launch_compact_rerank(kpt, nch, BH, scores, L.Epad, S, E, meta, coff,
+  e = pkv::launch_compact_rerank(m_of(c), kpt, nch, BH, scores, L.Epad, S, E, meta, coff,
                                  (int)L.nchunks_max, ptab, ix->rec, c->capacity, cand, est,
                                  L.cstride, C, mmc, L.nbins, udiv, st, ev(3));
   if (e != hipSuccess) return hip_status(e);
@@ -369,7 +374,7 @@ int32_t pariskv_build_index(const pariskv_config* cfg, const int8_t* srht_signs,
   ix->pending_stream = nullptr;
   const int BH = cfg->batch * cfg->n_kv_heads;
   (void)hipGetLastError();
-  hipError_t e = pkv::launch_encode(cfg->key_dtype, K, k_rows_per_head, 0, n_keys, BH,
+  hipError_t e = pkv::launch_encode(m_of(cfg), cfg->key_dtype, K, k_rows_per_head, 0, n_keys, BH,
                                     cfg->capacity, ix->ids, ix->rec, ix->signs, ix->rot_c,
                                     (hipStream_t)stream, pkv::EvPair{});
   if (e != hipSuccess) {
@@ -406,9 +411,9 @@ int32_t pariskv_append_keys(pariskv_index* ix, const void* K_new, int64_t new_ro
   }
   const int BH = ix->cfg.batch * ix->cfg.n_kv_heads;
   (void)hipGetLastError();
-  hipError_t e = pkv::launch_encode(ix->cfg.key_dtype, K_new, new_rows_per_head, ix->n, n_new, BH,
-                                    ix->cfg.capacity, ix->ids, ix->rec, ix->signs,
-                                    ix->rot_c, (hipStream_t)stream, pkv::EvPair{});
+  hipError_t e = pkv::launch_encode(m_of(&ix->cfg), ix->cfg.key_dtype, K_new, new_rows_per_head,
+                                    ix->n, n_new, BH, ix->cfg.capacity, ix->ids, ix->rec,
+                                    ix->signs, ix->rot_c, (hipStream_t)stream, pkv::EvPair{});
   if (e != hipSuccess) return PARISKV_ERR_HIP;
   ix->n += n_new;
   return PARISKV_OK;
@@ -508,17 +513,28 @@ int32_t pariskv_debug_export(const pariskv_index* ix, int64_t lo, int64_t hi, ui
   if (hipDeviceSynchronize() != hipSuccess) return PARISKV_ERR_HIP;
   const int64_t BH = (int64_t)ix->cfg.batch * ix->cfg.n_kv_heads;
   const int64_t cap = ix->cfg.capacity, n = hi - lo;
+  const int B = ix->cfg.n_subspaces;  // 16 (m = 8) or 32 (m = 4)
   if (n == 0) return PARISKV_OK;
+  std::vector<uint8_t> packed(B == 16 ? 0 : (size_t)n * 16);
   for (int64_t bh = 0; bh < BH; ++bh) {
     const int64_t key = bh * cap + lo;
-    if (ids_host && hipMemcpy(ids_host + bh * n * 16, ix->ids + key * 16, n * 16,
-                              hipMemcpyDeviceToHost) != hipSuccess)
-      return PARISKV_ERR_HIP;
+    if (ids_host) {
+      // device byte s holds the sign bits of coordinates 8 s .. 8 s + 7:
+      // one id (m = 8), or the ids of subspaces 2 s and 2 s + 1 (m = 4)
+      uint8_t* dst = B == 16 ? ids_host + bh * n * 16 : packed.data();
+      if (hipMemcpy(dst, ix->ids + key * 16, n * 16, hipMemcpyDeviceToHost) != hipSuccess)
+        return PARISKV_ERR_HIP;
+      if (B == 32)
+        for (int64_t i = 0; i < n * 16; ++i) {
+          ids_host[bh * n * 32 + 2 * i] = packed[i] & 15u;
+          ids_host[bh * n * 32 + 2 * i + 1] = packed[i] >> 4;
+        }
+    }
     const uint8_t* rec = (const uint8_t*)ix->rec + key * 128;
     if (nib_host && hipMemcpy2D(nib_host + bh * n * 64, 64, rec, 128, 64, n,
                                 hipMemcpyDeviceToHost) != hipSuccess)
       return PARISKV_ERR_HIP;
-    if (w_host && hipMemcpy2D(w_host + bh * n * 16, 32, rec + 64, 128, 32, n,
+    if (w_host && hipMemcpy2D(w_host + bh * n * B, 2 * B, rec + 64, 128, 2 * B, n,
                               hipMemcpyDeviceToHost) != hipSuccess)
       return PARISKV_ERR_HIP;
   }
@@ -625,9 +641,9 @@ int32_t pariskv_window_append(pariskv_window* w, const void* K_new, const void* 
                          w->U * rb, BH, hipMemcpyDefault, st);
   if (e != hipSuccess) return PARISKV_ERR_HIP;
   if (int32_t rc = flush_pending(ix)) return rc;
-  e = pkv::launch_encode(ix->cfg.key_dtype, w->Kn + slot0 * rb, w->S + w->ring, ix->n, w->U,
-                         (int)BH, ix->cfg.capacity, ix->ids, ix->rec, ix->signs, ix->rot_c, st,
-                         pkv::EvPair{});
+  e = pkv::launch_encode(m_of(&ix->cfg), ix->cfg.key_dtype, w->Kn + slot0 * rb, w->S + w->ring,
+                         ix->n, w->U, (int)BH, ix->cfg.capacity, ix->ids, ix->rec, ix->signs,
+                         ix->rot_c, st, pkv::EvPair{});
   if (e != hipSuccess) return PARISKV_ERR_HIP;
   ix->n += w->U;
   ix->last = st;

@@ -40,10 +40,10 @@ struct EvPair {
   hipEvent_t stop = nullptr;
 };
 
-hipError_t launch_encode(int dtype, const void* K, int64_t rows_per_head, int64_t lo, int64_t n,
-                         int BH, int64_t cap, uint8_t* ids, uint32_t* rec, const SignMask& sg,
-                         float c, hipStream_t st, const EvPair& ev);
-hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
+hipError_t launch_encode(int m, int dtype, const void* K, int64_t rows_per_head, int64_t lo,
+                         int64_t n, int BH, int64_t cap, uint8_t* ids, uint32_t* rec,
+                         const SignMask& sg, float c, hipStream_t st, const EvPair& ev);
+hipError_t launch_qprep(int m, int dtype, const void* Q, int BH, int n_kv_heads, int G,
                         const SignMask& sg, float c, int rho, const Tiers& tw, uint8_t* lut,
                         float* yq, float* ptab, const AppendJob& app, int unit_div,
                         hipStream_t st, const EvPair& ev);
@@ -54,7 +54,7 @@ hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t
 hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nchunks, int nbins,
                          int rstride, int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st,
                          const EvPair& ev);
-hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* scores,
+hipError_t launch_compact_rerank(int m, int kpt, int nchunks, int BH, const uint8_t* scores,
                                  int64_t Epad, int64_t S, int64_t E, const int32_t* meta,
                                  const uint32_t* coff, int chunk_stride, const float* ptab,
                                  const uint32_t* rec, int64_t cap, int32_t* cand, float* est,

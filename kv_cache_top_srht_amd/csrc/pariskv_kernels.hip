@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <stdint.h>
+#include <type_traits>
 
 #include "codebook_tables.h"
 #include "pariskv_internal.h"
@@ -29,6 +30,24 @@ __constant__ float c_levels[8] = {
 __constant__ float c_thresh[7] = {
     kThresh_m8[0], kThresh_m8[1], kThresh_m8[2], kThresh_m8[3],
     kThresh_m8[4], kThresh_m8[5], kThresh_m8[6]};
+__constant__ float c_levels4[8] = {
+    kLevels_m4[0], kLevels_m4[1], kLevels_m4[2], kLevels_m4[3],
+    kLevels_m4[4], kLevels_m4[5], kLevels_m4[6], kLevels_m4[7]};
+__constant__ float c_thresh4[7] = {
+    kThresh_m4[0], kThresh_m4[1], kThresh_m4[2], kThresh_m4[3],
+    kThresh_m4[4], kThresh_m4[5], kThresh_m4[6]};
+
+// codebook of subspace size M (8 or 4): level i and threshold i
+template <int M>
+__device__ __forceinline__ float cb_level(int i) {
+  if constexpr (M == 8) return c_levels[i];
+  else return c_levels4[i];
+}
+template <int M>
+__device__ __forceinline__ float cb_thresh(int i) {
+  if constexpr (M == 8) return c_thresh[i];
+  else return c_thresh4[i];
+}
 
 // ---------------------------------------------------------------------------
 // Element loads: 8 consecutive elements of a bf16 or fp32 row as fp32.
@@ -104,24 +123,30 @@ __device__ __forceinline__ uint32_t sign_byte_of(const SignMask& sg, int sub) {
 // ---------------------------------------------------------------------------
 // K1 encode: [TS] Coarse Candidate Generation (bucket = nearest analytic
 // sign centroid of each subspace direction) and Candidate Reranking (RSQ-IP)
-// Quantization + Calibration.  One key per 16-lane group; lane `sub` encodes
-// subspace `sub` of its key:
+// Quantization + Calibration.  One key per 16-lane group; lane `sub` owns
+// coordinates [8 sub, 8 sub + 8): one subspace of M = 8, or the two
+// subspaces 2 sub, 2 sub + 1 of M = 4.  Per subspace z (coordinates j):
 //   id   = sum_j [z_j < 0] 2^j
-//   n    = sqrt(((z_0 z_0 + z_1 z_1) + ...) + z_7 z_7)
+//   n    = sqrt(((z_0 z_0 + z_1 z_1) + ...) + z_{M-1} z_{M-1})
 //   u_j  = z_j / n; mag_j = #{l : |u_j| >= tau_l}; code_j = sign_j << 3 | mag_j
 //   a    = ((v_0 u_0 + v_1 u_1) + ...), v_j = +-L[mag_j]
 //   w    = fp16_rne(n / a)           (n == 0: magnitudes 0, w = 0)
+// with the Lloyd-Max codebook (L, tau) of subspace size M.
 // Index layout per (b,h): ids [cap][16] bytes and a 128-byte record per key
 // (one L2 line): dwords 0..15 = codes (nibble j of dword s = coordinate
-// 8 s + j), bytes 64..95 = w as 16 fp16, bytes 96..127 unused.
+// 8 s + j), then w as fp16 per subspace from byte 64 (M = 8: 16 of them,
+// bytes 96..127 unused; M = 4: 32 of them).  Byte s of the ids holds the
+// sign bits of coordinates 8 s .. 8 s + 7: the id of subspace s (M = 8), or
+// the ids of subspaces 2 s (low nibble) and 2 s + 1 (high nibble) (M = 4).
 // ---------------------------------------------------------------------------
-// Encodes key row r of (b, h) = bh (16 lanes, lane `sub` = subspace `sub`)
-// into index position `pos`.
-template <typename T>
+// Encodes key row r of (b, h) = bh (16 lanes, lane `sub` = coordinates
+// 8 sub .. 8 sub + 7) into index position `pos`.
+template <typename T, int M>
 __device__ __forceinline__ void encode_key(const T* __restrict__ K, int64_t rows_per_head,
                                            int64_t bh, int64_t r, int64_t pos, int64_t cap,
                                            uint8_t* __restrict__ ids, uint32_t* __restrict__ rec,
                                            const SignMask& sg, float c, int sub) {
+  static_assert(M == 8 || M == 4, "subspaces of 8 or 4 coordinates");
   float x[8];
   load8(K + ((bh * rows_per_head + r) << 7) + sub * 8, x);
   srht16(x, sign_byte_of(sg, sub), sub, c);
@@ -129,41 +154,47 @@ __device__ __forceinline__ void encode_key(const T* __restrict__ K, int64_t rows
   uint32_t id = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) id |= (x[j] < 0.0f ? 1u : 0u) << j;
-  float n2 = 0.0f;
+  uint32_t code = 0, wpack = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) n2 = n2 + x[j] * x[j];
-  const float nrm = sqrtf(n2);
-  uint32_t code = 0;
-  uint16_t wbits = 0;
-  if (nrm != 0.0f) {
-    float a = 0.0f;
+  for (int sb = 0; sb < 8 / M; ++sb) {
+    const int j0 = sb * M;
+    float n2 = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float u = x[j] / nrm;
-      const float au = fabsf(u);
-      uint32_t mag = 0;
-      float lv = c_levels[0];
+    for (int j = j0; j < j0 + M; ++j) n2 = n2 + x[j] * x[j];
+    const float nrm = sqrtf(n2);
+    if (nrm != 0.0f) {
+      float a = 0.0f;
 #pragma unroll
-      for (int l = 0; l < 7; ++l)
-        if (au >= c_thresh[l]) { mag = l + 1; lv = c_levels[l + 1]; }
-      const uint32_t sgn = (id >> j) & 1u;
-      const float v = sgn ? -lv : lv;
-      a = a + v * u;
-      code |= ((sgn << 3) | mag) << (4 * j);
+      for (int j = j0; j < j0 + M; ++j) {
+        const float u = x[j] / nrm;
+        const float au = fabsf(u);
+        uint32_t mag = 0;
+        float lv = cb_level<M>(0);
+#pragma unroll
+        for (int l = 0; l < 7; ++l)
+          if (au >= cb_thresh<M>(l)) { mag = l + 1; lv = cb_level<M>(l + 1); }
+        const uint32_t sgn = (id >> j) & 1u;
+        const float v = sgn ? -lv : lv;
+        a = a + v * u;
+        code |= ((sgn << 3) | mag) << (4 * j);
+      }
+      const _Float16 hw = (_Float16)(nrm / a);
+      wpack |= (uint32_t)__builtin_bit_cast(uint16_t, hw) << (16 * sb);
+    } else {
+#pragma unroll
+      for (int j = j0; j < j0 + M; ++j) code |= ((id >> j) & 1u) << (4 * j + 3);
     }
-    const _Float16 hw = (_Float16)(nrm / a);
-    wbits = __builtin_bit_cast(uint16_t, hw);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) code |= ((id >> j) & 1u) << (4 * j + 3);
   }
   const int64_t key = bh * cap + pos;
   ids[key * 16 + sub] = (uint8_t)id;
   rec[key * 32 + sub] = code;
-  reinterpret_cast<uint16_t*>(rec)[key * 64 + 32 + sub] = wbits;
+  if constexpr (M == 8)
+    reinterpret_cast<uint16_t*>(rec)[key * 64 + 32 + sub] = (uint16_t)wpack;
+  else
+    rec[key * 32 + 16 + sub] = wpack;
 }
 
-template <typename T>
+template <typename T, int M>
 __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ K, int64_t rows_per_head,
                                                 int64_t lo, int64_t n, int64_t total, int64_t cap,
                                                 uint8_t* __restrict__ ids, uint32_t* __restrict__ rec,
@@ -173,7 +204,7 @@ __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ K, int64_t
   if (g >= total) return;  // whole 16-lane groups leave together
   const int64_t bh = g / n;
   const int64_t r = g - bh * n;
-  encode_key(K, rows_per_head, bh, r, lo + r, cap, ids, rec, sg, c, sub);
+  encode_key<T, M>(K, rows_per_head, bh, r, lo + r, cap, ids, rec, sg, c, sub);
 }
 
 // ---------------------------------------------------------------------------
@@ -217,12 +248,17 @@ __device__ __forceinline__ uint2 block_exscan2(uint2 v, uint2* s_warp, uint2& to
 // ---------------------------------------------------------------------------
 // K2 query prep: [TS] Coarse Candidate Generation, query side.  Group query
 // q = (q_0 + q_1 + ... + q_{G-1}) * fp32(1/G) in head order, yq = SRHT(q).
-// Per subspace s, the 256 centroid scores sc_p = sum_j (bit j of p ? -yq : +yq)
+// Per subspace, the 2^M centroid scores sc_p = sum_j (bit j of p ? -yq : +yq)
 // (sequential in j from the j = 0 term); the rho best by (sc desc, p asc)
-// get tier weights in the vote LUT, all other centroids 0.
-// One 1024-thread block per (b, h): wave s handles subspace s, lane l scores
-// centroids 4 l .. 4 l + 3 and keeps them in order; rho rounds of a wave
-// maximum over 64-bit (score, centroid) keys pick the winners.
+// get tier weights, all other centroids 0.
+// One 1024-thread block per (b, h); wave s builds row s of the vote table,
+// indexed by byte s of a key's ids.  M = 8: row s is subspace s's LUT; lane
+// l scores centroids 4 l .. 4 l + 3 and keeps them in order; rho rounds of a
+// wave maximum over 64-bit (score, centroid) keys pick the winners.  M = 4:
+// row s is the pair table of subspaces 2 s and 2 s + 1, entry v = lut_2s[v &
+// 15] + lut_2s+1[v >> 4], so the scan's sum over 16 bytes equals the sum
+// over the 32 subspaces; rows 0 and 1 of the wave (16 lanes each) score the
+// 16 centroids of the two subspaces and pick their winners by row maxima.
 // ---------------------------------------------------------------------------
 // Centroid p of a subspace with score sc as one 64-bit key: larger key means
 // earlier in (sc desc, p asc); -0 and +0 tie.
@@ -243,20 +279,26 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
 }
 __device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-// Maximum over the 64 lanes, received by every lane: in each row of 16 lanes
-// DPP quad swaps (lane ^ 1, lane ^ 2), the half-row mirror and the row
-// mirror; then lane ^ 16 and lane ^ 32 across rows.
-__device__ __forceinline__ uint64_t wave_max64(uint64_t k) {
+// Maximum over each row of 16 lanes, received by every lane of the row: DPP
+// quad swaps (lane ^ 1, lane ^ 2), the half-row mirror and the row mirror.
+__device__ __forceinline__ uint64_t row_max64(uint64_t k) {
   k = max64(k, dpp64<0xB1>(k));   // quad_perm [1, 0, 3, 2]
   k = max64(k, dpp64<0x4E>(k));   // quad_perm [2, 3, 0, 1]
   k = max64(k, dpp64<0x141>(k));  // row_half_mirror
   k = max64(k, dpp64<0x140>(k));  // row_mirror
+  return k;
+}
+
+// Maximum over the 64 lanes, received by every lane: the row maximum, then
+// lane ^ 16 and lane ^ 32 across rows.
+__device__ __forceinline__ uint64_t wave_max64(uint64_t k) {
+  k = row_max64(k);
   k = max64(k, shfl_xor64(k, 16));
   k = max64(k, shfl_xor64(k, 32));
   return k;
 }
 
-template <typename T, int G>
+template <typename T, int G, int M>
 __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_kv_heads,
                                                 float invG, SignMask sg, float c, int rho, Tiers tw,
                                                 uint8_t* __restrict__ lut_out, float* __restrict__ yq_out,
@@ -275,8 +317,8 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
   if (app.n > 0 && tid >= 256 && bh % unit_div == 0) {
     const int r = (tid - 256) >> 4;
     if (r < app.n)
-      encode_key((const T*)app.K, app.rows_per_head, bh / unit_div, r, app.lo + r, app.cap,
-                 app.ids, app.rec, sg, c, tid & 15);
+      encode_key<T, M>((const T*)app.K, app.rows_per_head, bh / unit_div, r, app.lo + r,
+                       app.cap, app.ids, app.rec, sg, c, tid & 15);
   }
   if (tid < 16) {
     const int sub = tid;
@@ -306,10 +348,44 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
   // product table for the rerank: ptab[j][code] = fl(+-L[code & 7] yq_j), the
   // sign bit (code & 8) negating the product exactly
   for (int e = tid; e < 2048; e += 1024) {
-    const float pr = c_levels[e & 7] * s_yq[e >> 4];
+    const float pr = cb_level<M>(e & 7) * s_yq[e >> 4];
     ptab_out[(int64_t)bh * 2048 + e] = (e & 8) ? -pr : pr;
   }
   const int s = tid >> 6, l = tid & 63;
+  uint32_t* lut_row = reinterpret_cast<uint32_t*>(lut_out + ((int64_t)bh * 16 + s) * 256);
+  if constexpr (M == 4) {
+    // lane l scores centroid p = l & 15 of subspace 2 s + ((l >> 4) & 1)
+    // (rows 2 and 3 repeat rows 0 and 1)
+    const int half = (l >> 4) & 1, p = l & 15;
+    float z4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z4[j] = s_yq[s * 8 + half * 4 + j];
+    float acc = (p & 1) ? -z4[0] : z4[0];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) acc = acc + (((p >> j) & 1) ? -z4[j] : z4[j]);
+    uint64_t key = centroid_key(acc, p);
+    // rho rounds: the row's best remaining centroid gets tier weight r and
+    // drops out (key 0 is below every centroid)
+    uint32_t wt = 0;
+    for (int r = 0; r < rho; ++r) {
+      const uint64_t W = row_max64(key);
+      if (key == W) {
+        wt = (uint32_t)tw.w[r];
+        key = 0;
+      }
+    }
+    // entries v = 4 l .. 4 l + 3: low nibble's weight from row 0, high
+    // nibble's (v >> 4 = l >> 2) from row 1
+    const uint32_t whi = (uint32_t)__shfl((int)wt, 16 + (l >> 2));
+    uint32_t word = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t wlo = (uint32_t)__shfl((int)wt, (4 * l + q) & 15);
+      word |= (wlo + whi) << (8 * q);
+    }
+    lut_row[l] = word;
+    return;
+  }
   float z[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) z[j] = s_yq[s * 8 + j];
@@ -346,8 +422,7 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
       key[3] = 0;
     }
   }
-  reinterpret_cast<uint32_t*>(lut_out + ((int64_t)bh * 16 + s) * 256)[l] =
-      lv[0] | (lv[1] << 8) | (lv[2] << 16) | (lv[3] << 24);
+  lut_row[l] = lv[0] | (lv[1] << 8) | (lv[2] << 16) | (lv[3] << 24);
 }
 
 // ---------------------------------------------------------------------------
@@ -644,7 +719,7 @@ __device__ __forceinline__ float quad_lane(float v) {
 constexpr int kPtabRow = 132;
 constexpr int kPtabLds = 16 * kPtabRow;
 
-template <int KPT, int CPB>
+template <int KPT, int CPB, int M>
 __global__ __launch_bounds__(256) void k_compact_rerank(
     const uint8_t* __restrict__ scores, int64_t Epad, int64_t S, int64_t E,
     const int32_t* __restrict__ meta, const uint32_t* __restrict__ coff, int chunk_stride,
@@ -731,16 +806,19 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
   __syncthreads();
 
   const uint32_t ntot = nsel0 + nsel1;
-  // 4 lanes per candidate: lane q reads the codes of subspaces 4q..4q+3
-  // (16 B) and their w (8 B) from the candidate's 128-byte record and forms
-  // w_b p_b for them; DPP broadcasts give every lane all 16 terms, summed in
-  // b order.  Up to 4 candidates per group are fetched before any is used.
+  // 4 lanes per candidate: lane q reads the codes of coordinates 32 q ..
+  // 32 q + 31 (16 B) and the w of their NB subspaces (NB = 32 / M; 2 NB
+  // bytes) from the candidate's record and forms w_b p_b for them; DPP
+  // broadcasts give every lane all 4 NB terms, summed in b order.  Up to 4
+  // candidates per group are fetched before any is used.
+  constexpr int NB = 32 / M;
+  using WT = typename std::conditional<M == 8, uint2, uint4>::type;
   const int q = tid & 3;
   const uint32_t* rq = rec + (int64_t)(bh / unit_div) * cap * 32;  // the unit's KV head
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;  // order keys of this block's estimates
   for (uint32_t j0 = 0; j0 < ntot; j0 += 256) {
     uint4 cw[4];
-    uint2 ww[4];
+    WT ww[4];
     int64_t pi[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -753,32 +831,41 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
       // covers only the loads issued before it
       const uint32_t* rp = rq + (has ? pi[r] : 0) * 32;
       cw[r] = reinterpret_cast<const uint4*>(rp)[q];
-      ww[r] = reinterpret_cast<const uint2*>(rp + 16)[q];
+      ww[r] = reinterpret_cast<const WT*>(rp + 16)[q];
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (j0 + r * 64 >= ntot) break;  // uniform across the block
       const uint32_t j = j0 + r * 64 + (tid >> 2);
       const uint32_t cws[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
-      float t[4];
+      uint32_t wsw[NB / 2];
+      wsw[0] = ww[r].x;
+      wsw[1] = ww[r].y;
+      if constexpr (M == 4) {
+        wsw[2] = ww[r].z;
+        wsw[3] = ww[r].w;
+      }
+      float t[NB];
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
+      for (int i = 0; i < NB; ++i) {
+        // subspace 4 q NB / 4 + i: coordinates from nibble j0 of code dword bb
+        const int bb = (i * M) >> 3, j0 = (i * M) & 7;
         const float* pb = s_P + (4 * q + bb) * kPtabRow;
         float p = 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) p = p + pb[jj * 16 + ((cws[bb] >> (4 * jj)) & 15u)];
-        const uint16_t hb = (uint16_t)(((bb < 2) ? ww[r].x : ww[r].y) >> ((bb & 1) * 16));
-        t[bb] = (float)__builtin_bit_cast(_Float16, hb) * p;
+        for (int jj = j0; jj < j0 + M; ++jj) p = p + pb[jj * 16 + ((cws[bb] >> (4 * jj)) & 15u)];
+        const uint16_t hb = (uint16_t)(wsw[i >> 1] >> ((i & 1) * 16));
+        t[i] = (float)__builtin_bit_cast(_Float16, hb) * p;
       }
       float e = 0.0f;
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) e = e + quad_lane<0>(t[bb]);
+      for (int i = 0; i < NB; ++i) e = e + quad_lane<0>(t[i]);
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) e = e + quad_lane<1>(t[bb]);
+      for (int i = 0; i < NB; ++i) e = e + quad_lane<1>(t[i]);
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) e = e + quad_lane<2>(t[bb]);
+      for (int i = 0; i < NB; ++i) e = e + quad_lane<2>(t[i]);
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) e = e + quad_lane<3>(t[bb]);
+      for (int i = 0; i < NB; ++i) e = e + quad_lane<3>(t[i]);
       if (j < ntot) {
         if (q == 0) {
           const uint32_t o = (j >= nsel0) ? off_c[1] + (j - nsel0) : off_c[0] + j;
@@ -1656,26 +1743,35 @@ static hipError_t launch(F kernel, dim3 grid, dim3 block, hipStream_t st, const 
   return hipGetLastError();
 }
 
-hipError_t launch_encode(int dtype, const void* K, int64_t rows_per_head, int64_t lo, int64_t n,
-                         int BH, int64_t cap, uint8_t* ids, uint32_t* rec, const SignMask& sg,
-                         float c, hipStream_t st, const EvPair& ev) {
+hipError_t launch_encode(int m, int dtype, const void* K, int64_t rows_per_head, int64_t lo,
+                         int64_t n, int BH, int64_t cap, uint8_t* ids, uint32_t* rec,
+                         const SignMask& sg, float c, hipStream_t st, const EvPair& ev) {
   const int64_t total = (int64_t)BH * n;
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)((total + 15) / 16));
-  if (dtype == 0)
-    return launch(k_encode<uint16_t>, grid, dim3(256), st, ev, (const uint16_t*)K,
-                  rows_per_head, lo, n, total, cap, ids, rec, sg, c);
-  return launch(k_encode<float>, grid, dim3(256), st, ev, (const float*)K, rows_per_head, lo, n,
-                total, cap, ids, rec, sg, c);
+#define PKV_ENC(T, MM)                                                                       \
+  return launch(k_encode<T, MM>, grid, dim3(256), st, ev, (const T*)K, rows_per_head, lo, n, \
+                total, cap, ids, rec, sg, c)
+  if (m == 8) {
+    if (dtype == 0) PKV_ENC(uint16_t, 8);
+    PKV_ENC(float, 8);
+  }
+  if (m == 4) {
+    if (dtype == 0) PKV_ENC(uint16_t, 4);
+    PKV_ENC(float, 4);
+  }
+#undef PKV_ENC
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
-                        const SignMask& sg, float c, int rho, const Tiers& tw, uint8_t* lut,
-                        float* yq, float* ptab, const AppendJob& app, int unit_div,
-                        hipStream_t st, const EvPair& ev) {
+template <int M>
+static hipError_t launch_qprep_m(int dtype, const void* Q, int BH, int n_kv_heads, int G,
+                                 const SignMask& sg, float c, int rho, const Tiers& tw,
+                                 uint8_t* lut, float* yq, float* ptab, const AppendJob& app,
+                                 int unit_div, hipStream_t st, const EvPair& ev) {
   const float invG = 1.0f / (float)G;
-#define PKV_QP(T, GG)                                                                        \
-  return launch(k_qprep<T, GG>, dim3(BH), dim3(1024), st, ev, (const T*)Q, n_kv_heads, invG, \
+#define PKV_QP(T, GG)                                                                           \
+  return launch(k_qprep<T, GG, M>, dim3(BH), dim3(1024), st, ev, (const T*)Q, n_kv_heads, invG, \
                 sg, c, rho, tw, lut, yq, ptab, app, unit_div)
   if (dtype == 0) {
     switch (G) {
@@ -1694,6 +1790,19 @@ hipError_t launch_qprep(int dtype, const void* Q, int BH, int n_kv_heads, int G,
     default: return hipErrorInvalidValue;
   }
 #undef PKV_QP
+}
+
+hipError_t launch_qprep(int m, int dtype, const void* Q, int BH, int n_kv_heads, int G,
+                        const SignMask& sg, float c, int rho, const Tiers& tw, uint8_t* lut,
+                        float* yq, float* ptab, const AppendJob& app, int unit_div,
+                        hipStream_t st, const EvPair& ev) {
+  if (m == 8)
+    return launch_qprep_m<8>(dtype, Q, BH, n_kv_heads, G, sg, c, rho, tw, lut, yq, ptab, app,
+                             unit_div, st, ev);
+  if (m == 4)
+    return launch_qprep_m<4>(dtype, Q, BH, n_kv_heads, G, sg, c, rho, tw, lut, yq, ptab, app,
+                             unit_div, st, ev);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t cap, int64_t S,
@@ -1728,7 +1837,7 @@ hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nc
                 rstride, C, meta, coff);
 }
 
-hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* scores,
+hipError_t launch_compact_rerank(int m, int kpt, int nchunks, int BH, const uint8_t* scores,
                                  int64_t Epad, int64_t S, int64_t E, const int32_t* meta,
                                  const uint32_t* coff, int chunk_stride, const float* ptab,
                                  const uint32_t* rec, int64_t cap, int32_t* cand, float* est,
@@ -1736,16 +1845,25 @@ hipError_t launch_compact_rerank(int kpt, int nchunks, int BH, const uint8_t* sc
                                  int unit_div, hipStream_t st, const EvPair& ev) {
   const int swar = nbins <= 128 ? 1 : 0;  // every score below 128
   const dim3 grid((nchunks + kCompactChunks - 1) / kCompactChunks, BH);
-  switch (kpt) {
-#define PKV_CR(K)                                                                            \
-  case K:                                                                                    \
-    return launch(k_compact_rerank<K, kCompactChunks>, grid, dim3(256), st, ev, scores, Epad, \
-                  S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, cand, est, cstride, \
-                  C, mm, swar, unit_div);
-    PKV_CR(1) PKV_CR(2) PKV_CR(4) PKV_CR(8) PKV_CR(16)
-#undef PKV_CR
-    default: return hipErrorInvalidValue;
+#define PKV_CR(K, MM)                                                                         \
+  case K:                                                                                     \
+    return launch(k_compact_rerank<K, kCompactChunks, MM>, grid, dim3(256), st, ev, scores,   \
+                  Epad, S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, cand, est,     \
+                  cstride, C, mm, swar, unit_div);
+  if (m == 8) {
+    switch (kpt) {
+      PKV_CR(1, 8) PKV_CR(2, 8) PKV_CR(4, 8) PKV_CR(8, 8) PKV_CR(16, 8)
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (m == 4) {
+    switch (kpt) {
+      PKV_CR(1, 4) PKV_CR(2, 4) PKV_CR(4, 4) PKV_CR(8, 4) PKV_CR(16, 4)
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef PKV_CR
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cstride, int C,

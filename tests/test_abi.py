@@ -68,7 +68,8 @@ def test_sizes(pk):
 
 
 @pytest.mark.parametrize("field,value,rc", [
-    ("head_dim", 96, -1), ("head_dim", 64, -2), ("n_subspaces", 32, -2),
+    ("head_dim", 96, -1), ("head_dim", 64, -2), ("n_subspaces", 32, 0),
+    ("n_subspaces", 8, -1),
     ("n_subspaces", 7, -1), ("rho", 0, -1), ("rho", 9, -1),
     ("cand_num", 0, -1), ("cand_den", 0, -1), ("n_q_heads", 30, -1),
     ("key_dtype", 5, -1), ("capacity", 0, -1), ("n_sink", -1, -1),
@@ -85,6 +86,17 @@ def test_tier_overflow_rejected(pk):
     c = pk.make_config(capacity=4096, tiers=(16, 3, 2, 1))
     n = C.c_size_t()
     assert pk.lib().pariskv_index_bytes(C.byref(c), C.byref(n)) == -1
+    # 32 subspaces of 4: the largest score is 32 times the top tier
+    c = pk.make_config(capacity=4096, tiers=(7, 3, 2, 1))
+    c.n_subspaces = 32
+    assert pk.lib().pariskv_index_bytes(C.byref(c), C.byref(n)) == 0
+    c = pk.make_config(capacity=4096, tiers=(8, 3, 2, 1))
+    c.n_subspaces = 32
+    assert pk.lib().pariskv_index_bytes(C.byref(c), C.byref(n)) == -1
+    # 64 subspaces of 2: a valid configuration this build has no kernels for
+    c = pk.make_config(capacity=4096, tiers=(3, 2, 1, 1))
+    c.n_subspaces = 64
+    assert pk.lib().pariskv_index_bytes(C.byref(c), C.byref(n)) == -2
 
 
 def test_host_side_argument_errors(pk):

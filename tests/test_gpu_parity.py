@@ -42,6 +42,15 @@ SMALL = {
               k=300, seed=20),
     "rho1": W("rho 1", 1, 4, 4, 128, 20000, "bf16", rho=1, tiers=(1,),
               cand_num=1, cand_den=10, k=300, seed=21),
+    # 32 subspaces of 4 coordinates: scores up to 128 (general compare path),
+    # up to 96 (byte-wise path), and rho 8 of 16 centroids
+    "m4": W("32 subspaces of 4", 2, 2, 8, 128, 20000, "bf16", B=32, k=256,
+            seed=22),
+    "m4_sinks_fp32": W("m 4, sinks, fp32", 1, 2, 4, 128, 9001, "fp32", B=32,
+                       rho=2, tiers=(3, 1), cand_num=1, cand_den=10, k=200,
+                       sinks=32, seed=23),
+    "m4_rho8": W("m 4, rho 8", 1, 2, 8, 128, 30000, "bf16", B=32, rho=8,
+                 tiers=(7, 6, 5, 4, 3, 2, 1, 1), k=512, seed=24),
 }
 
 
@@ -67,7 +76,7 @@ def test_retrieve_parity_small(orc, name):
     w = SMALL[name]
     lay, cfg, L, idx, est = run_case(orc, w)
     BH = w.batch * w.n_kv_heads
-    ids, nib, wq = pk.pariskv_debug_export(L.handle, 0, w.N, BH)
+    ids, nib, wq = pk.pariskv_debug_export(L.handle, 0, w.N, BH, B=w.B)
     Kh = host_f32(lay["K"])
     Qh = host_f32(lay["Q"])
     heads = list(range(BH))
@@ -98,14 +107,15 @@ def test_retrieve_parity_small(orc, name):
     L.close()
 
 
-@pytest.mark.parametrize("dtype,n0,steps", [("bf16", 1000, [1, 7, 100, 1]),
-                                            ("fp32", 33, [16, 1, 250])])
-def test_append_equals_build(orc, dtype, n0, steps):
+@pytest.mark.parametrize("dtype,n0,steps,B", [("bf16", 1000, [1, 7, 100, 1], 16),
+                                              ("fp32", 33, [16, 1, 250], 16),
+                                              ("bf16", 500, [1, 3, 60], 32)])
+def test_append_equals_build(orc, dtype, n0, steps, B):
     """Appending keys in pieces encodes exactly what a one-shot build does,
     and both equal the oracle (decode keys need no re-clustering)."""
     total = n0 + sum(steps)
-    w = W("append", 2, 2, 8, 128, total, dtype, k=64, seed=21)
-    case("append %s n0=%d steps=%s" % (dtype, n0, steps))
+    w = W("append", 2, 2, 8, 128, total, dtype, B=B, k=64, seed=21)
+    case("append %s n0=%d steps=%s B=%d" % (dtype, n0, steps, B))
     lay = synth.make_layer(w, "cuda", capacity=total + 5)
     cfg = pk.config_for(w, capacity=total + 5)
     full = pk.Layer(cfg, lay["signs"], lay["K"], total, k=64)
@@ -117,8 +127,8 @@ def test_append_equals_build(orc, dtype, n0, steps):
     assert inc.size == total
     torch.cuda.synchronize()
     BH = w.batch * w.n_kv_heads
-    a = pk.pariskv_debug_export(full.handle, 0, total, BH)
-    b = pk.pariskv_debug_export(inc.handle, 0, total, BH)
+    a = pk.pariskv_debug_export(full.handle, 0, total, BH, B=B)
+    b = pk.pariskv_debug_export(inc.handle, 0, total, BH, B=B)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
     enc = oracle_encode_heads(orc, w, host_f32(lay["K"]), lay["signs"],
@@ -128,12 +138,13 @@ def test_append_equals_build(orc, dtype, n0, steps):
             assert np.array_equal(x[bh], y)
 
 
-def test_ties_duplicates_and_zero_keys(orc):
+@pytest.mark.parametrize("B", [16, 32])
+def test_ties_duplicates_and_zero_keys(orc, B):
     """Duplicated keys tie on both the vote score and the estimate; all-zero
     keys have w = 0 and estimate 0 (and -0 vs +0 must not matter)."""
-    w = W("ties", 1, 2, 4, 128, 3000, "bf16", cand_num=1, cand_den=5, k=300,
+    w = W("ties", 1, 2, 4, 128, 3000, "bf16", B=B, cand_num=1, cand_den=5, k=300,
           seed=31)
-    case("ties/duplicates/zero keys")
+    case("ties/duplicates/zero keys B=%d" % B)
     lay = synth.make_layer(w, "cuda")
     K = lay["K"]
     K[:, :, 1000:1600] = K[:, :, 100:700]        # duplicates

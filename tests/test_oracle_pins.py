@@ -172,8 +172,9 @@ def test_rotation_orthogonal_and_dense_match(orc):
 
 # -------------------------------------------------------------- encode ----
 
-def test_bucket_id_is_nearest_sign_centroid(orc):
-    d, m = 128, 8
+@pytest.mark.parametrize("m", [4, 8])
+def test_bucket_id_is_nearest_sign_centroid(orc, m):
+    d = 128
     D = signs_for(d)
     X = skewed_keys(300, d, 21)
     ids, nib, w = orc.encode_keys(D, X, m)
@@ -193,15 +194,16 @@ def _unpack(nib):
     return np.stack([lo, hi], axis=-1).reshape(nib.shape[0], -1)
 
 
-def test_codes_sign_bits_and_magnitudes(orc):
-    d, m = 128, 8
+@pytest.mark.parametrize("m", [4, 8])
+def test_codes_sign_bits_and_magnitudes(orc, m):
+    d = 128
     D = signs_for(d)
     X = skewed_keys(300, d, 22)
     ids, nib, w = orc.encode_keys(D, X, m)
     codes = _unpack(nib)                               # [n, 128]
     Y = orc.rotate(D, X).astype(np.float64)
     _, tau = orc.codebook(m)
-    for b in range(16):
+    for b in range(d // m):
         z = Y[:, b * m:(b + 1) * m]
         sgn = codes[:, b * m:(b + 1) * m] >> 3
         idbits = (ids[:, b:b + 1] >> np.arange(m)[None]) & 1
@@ -214,14 +216,16 @@ def test_codes_sign_bits_and_magnitudes(orc):
         assert np.array_equal(got[~near], mag[~near])
 
 
-def test_nibble_order_on_designed_direction(orc):
+@pytest.mark.parametrize("m", [4, 8])
+def test_nibble_order_on_designed_direction(orc, m):
     """A rotated key designed with known per-coordinate magnitudes: coordinate
-    j of subspace 0 has |u_j| inside magnitude cell j (cells 0..7), signs
-    alternating.  Decoding must return codes in coordinate order."""
-    d, m = 128, 8
+    j of subspace 0 has |u_j| inside magnitude cell j (8 // m) (cells 0..7 for
+    m = 8, 0, 2, 4, 6 for m = 4), signs alternating.  Decoding must return
+    codes in coordinate order."""
+    d = 128
     D = signs_for(d)
     L, tau = orc.codebook(m)
-    mids = L.copy()                                 # a level lies inside its cell
+    mids = L[::8 // m].copy()                       # a level lies inside its cell
     u = mids * np.where(np.arange(m) % 2 == 1, -1.0, 1.0)
     u = u / np.linalg.norm(u)
     # re-normalisation shrinks |u_j|; rescale so each stays in its cell
@@ -237,11 +241,12 @@ def test_nibble_order_on_designed_direction(orc):
     want_mag = np.searchsorted(tau, uu, side="right")
     want = ((yy < 0).astype(int) << 3) | want_mag
     assert list(codes) == list(want)
-    assert len(set(want_mag.tolist())) >= 6      # magnitudes really differ
+    assert len(set(want_mag.tolist())) >= m - 2  # magnitudes really differ
 
 
-def test_zero_subspace_gives_zero_w(orc):
-    d, m = 128, 8
+@pytest.mark.parametrize("m", [4, 8])
+def test_zero_subspace_gives_zero_w(orc, m):
+    d = 128
     D = signs_for(d)
     ids, nib, w = orc.encode_keys(D, np.zeros((1, d), np.float32), m)
     assert not ids.any() and not nib.any() and not w.any()
@@ -271,8 +276,9 @@ def _top_closed_form(yqb):
     return [r1, r2, r3, r4]
 
 
-def test_query_prep_top_rho(orc):
-    d, m, rho = 128, 8, 4
+@pytest.mark.parametrize("m", [4, 8])
+def test_query_prep_top_rho(orc, m):
+    d, rho = 128, 4
     tiers = [4, 3, 2, 1]
     D = signs_for(d)
     for seed in range(6):
@@ -296,8 +302,9 @@ def test_query_prep_top_rho(orc):
 
 # --------------------------------------------------------------- votes ----
 
-def test_votes_brute_force_collisions(orc):
-    d, m, rho = 128, 8, 4
+@pytest.mark.parametrize("m", [4, 8])
+def test_votes_brute_force_collisions(orc, m):
+    d, rho = 128, 4
     tiers = np.array([4, 3, 2, 1])
     D = signs_for(d)
     X = skewed_keys(2000, d, 31)
@@ -307,25 +314,27 @@ def test_votes_brute_force_collisions(orc):
     S = 5
     sc = orc.vote_scores(ids, lut, S, m)
     want = np.zeros(2000 - S, np.int64)
-    for b in range(16):
+    for b in range(d // m):
         for s in range(rho):
             want += tiers[s] * (ids[S:, b] == top[b, s])
     assert np.array_equal(sc, want)
-    assert sc.max() <= 64 and sc.min() >= 0
+    assert sc.max() <= 4 * (d // m) and sc.min() >= 0
 
 
-def test_votes_special_cases(orc):
+@pytest.mark.parametrize("m", [4, 8])
+def test_votes_special_cases(orc, m):
     """k = alpha q (alpha a power of two, G = 1) collides with the query's
-    top centroid in every subspace -> 16 * 4 = 64; k = -q lands on the
-    opposite sign pattern, which is never among the top rho -> 0."""
-    d, m = 128, 8
+    top centroid in every subspace -> B * 4 (64 for B = 16); k = -q lands on
+    the opposite sign pattern, which is never among the top rho -> 0."""
+    d = 128
     D = signs_for(d)
     q = skewed_keys(1, d, 41)
     K = np.concatenate([q * 2.0, q * 0.25, -q, q]).astype(np.float32)
     ids, _, _ = orc.encode_keys(D, K, m)
     yq, lut, top = orc.query_prep(D, q, m, 4, [4, 3, 2, 1])
     sc = orc.vote_scores(ids, lut, 0, m)
-    assert list(sc) == [64, 64, 0, 64]
+    top = 4 * (d // m)
+    assert list(sc) == [top, top, 0, top]
 
 
 # ---------------------------------------------------------- candidates ----
@@ -375,8 +384,9 @@ def _aligned_keys(orc, D, n, seed):
     return (orc.rotate(plus, y).astype(np.float64) * D).astype(np.float32)
 
 
-def test_rerank_exact_for_aligned_keys(orc):
-    d, m = 128, 8
+@pytest.mark.parametrize("m", [4, 8])
+def test_rerank_exact_for_aligned_keys(orc, m):
+    d = 128
     D = signs_for(d)
     K = _aligned_keys(orc, D, 200, 61)
     ids, nib, w = orc.encode_keys(D, K, m)
@@ -389,10 +399,11 @@ def test_rerank_exact_for_aligned_keys(orc):
     assert np.max(np.abs(est - truth) / scale) < 1e-3
 
 
-def test_rerank_self_inner_product(orc):
+@pytest.mark.parametrize("m", [4, 8])
+def test_rerank_self_inner_product(orc, m):
     """q = k: w <v, y_b> = (n/<v,u>) n <v,u> = n^2, so est = ||k||^2 up to
     the fp16 rounding of w (relative 2^-11)."""
-    d, m = 128, 8
+    d = 128
     D = signs_for(d)
     K = skewed_keys(100, d, 71)
     ids, nib, w = orc.encode_keys(D, K, m)
@@ -403,8 +414,9 @@ def test_rerank_self_inner_product(orc):
         assert abs(est - n2) / n2 < 1e-3
 
 
-def test_rerank_linear_in_query(orc):
-    d, m = 128, 8
+@pytest.mark.parametrize("m", [4, 8])
+def test_rerank_linear_in_query(orc, m):
+    d = 128
     D = signs_for(d)
     K = skewed_keys(300, d, 81)
     _, nib, w = orc.encode_keys(D, K, m)
@@ -419,11 +431,12 @@ def test_rerank_linear_in_query(orc):
     assert np.max(np.abs(e[2] - e[0] - e[1]) / ref) < 1e-4
 
 
-def test_rerank_sign_of_estimate_tracks_truth(orc):
+@pytest.mark.parametrize("m", [4, 8])
+def test_rerank_sign_of_estimate_tracks_truth(orc, m):
     """Loose statistical check of the estimator on skewed keys: the
     estimate correlates with the true inner product (the pages give no error
     bound, so only a coarse property is asserted)."""
-    d, m = 128, 8
+    d = 128
     D = signs_for(d)
     K = skewed_keys(2000, d, 91)
     _, nib, w = orc.encode_keys(D, K, m)
