@@ -61,6 +61,9 @@ def parse():
                     help="centroids kept per subspace (default: the workload's); "
                          "tiers become rho, rho-1, ..., 1 unless --tiers is given")
     ap.add_argument("--tiers", default="", help="comma-separated tier weights")
+    ap.add_argument("--subspaces", type=int, default=0,
+                    help="subspaces B (16: 8 coordinates each, 32: 4 each; "
+                         "default: the workload's)")
     ap.add_argument("--cand-frac", default="",
                     help="candidate fraction as num/den (default: the workload's)")
     ap.add_argument("--window", default="",
@@ -128,6 +131,8 @@ def main():
     if args.cand_frac:
         num, den = (int(x) for x in args.cand_frac.split("/"))
         w = w.scaled(cand_num=num, cand_den=den)
+    if args.subspaces:
+        w = w.scaled(B=args.subspaces)
     if args.per_query_head:
         if args.window:
             sys.exit("--per-query-head runs without --window")
@@ -135,6 +140,7 @@ def main():
     K_steps, W_steps, Lr = args.steps, args.warmup, max(1, args.layers)
     per_layer = math.ceil((K_steps + W_steps + args.profile_steps) / Lr) + 1
     cap = w.N + per_layer + max(0, args.warm_steps) + 1
+    BH = w.batch * w.n_kv_heads
     # retrieval units: one per (batch, KV head), or per (batch, query head)
     # in the unshared mode
     U = w.batch * (w.n_q_heads if w.per_query_head else w.n_kv_heads)
@@ -276,17 +282,22 @@ def main():
     value = keys_scanned / wall
     us_per_step = wall / K_steps * 1e6
 
-    scan_bytes = 16.0 * E_prof.mean() * U
+    # 16 B of ids per key and KV head: in the unshared mode one scan pass
+    # serves the G query heads of a KV head (chunks of 512 keys or more)
+    scan_bytes = 16.0 * E_prof.mean() * BH
     scan_us = float(kern[:, 1].mean())
     achieved = scan_bytes / (scan_us * 1e-6) / 1e9
-    traffic = read_traffic("vote_scan_%s%s_traffic.txt" % (
-        args.workload, "_per_query_head" if w.per_query_head else ""), scan_bytes)
+    variant = ("_per_query_head" if w.per_query_head else "") + \
+        ("_m%d" % w.m if w.m != 8 else "")
+    traffic = read_traffic("vote_scan_%s%s_traffic.txt" % (args.workload, variant),
+                           scan_bytes)
     row_bytes = 2 * w.d * (2 if w.dtype == "bf16" else 4) + 4
     attn_bytes = float(U * w.k * row_bytes + 2 * w.batch * w.n_q_heads * w.d *
                        (2 if w.dtype == "bf16" else 4))
     attn_us = float(kern[:, 6].mean())
     C = pk.pariskv_retrieve_sizes(layers[0][0].handle, w.k)[1]
-    rerank_bytes = 96.0 * C * U
+    # per candidate: 64 B of codes and B fp16 calibration factors
+    rerank_bytes = (64.0 + 2 * w.B) * C * U
     rerank_us = float(kern[:, 3].mean())
 
     result = {

@@ -524,6 +524,130 @@ __global__ __launch_bounds__(NT) void k_scan(const uint4* __restrict__ ids, int6
 }
 
 // ---------------------------------------------------------------------------
+// K3 for unshared retrieval: the GU query heads of one KV head scan its ids in
+// one pass, so each key's 16 B are read once instead of GU times.  Their GU
+// vote tables are interleaved in LDS, entry (s, v) holding head g's vote in
+// byte g % 4 of word g / 4, so one 32-bit read per subspace returns four
+// heads' votes and 32-bit adds sum them bytewise (a head's score is at most
+// 255, so no byte carries into the next).  Per head the outputs are those of
+// k_scan: score bytes and the cumulative chunk row, with per-wave histograms
+// of two 16-bit bins per word (a wave counts at most 512 keys).
+// Grid (chunks, b*H_kv); units kvh*GU .. kvh*GU + GU - 1 are the KV head's.
+// ---------------------------------------------------------------------------
+template <int KPT, int NT, int GU>
+__global__ __launch_bounds__(NT) void k_scan_group(const uint4* __restrict__ ids, int64_t cap,
+                                                   int64_t S, int64_t E,
+                                                   const uint8_t* __restrict__ lut,
+                                                   uint8_t* __restrict__ scores, int64_t Epad,
+                                                   uint32_t* __restrict__ chist,
+                                                   int chunk_stride, int nbins, int rstride) {
+  constexpr int NW = NT / 64;
+  constexpr int W = (GU + 3) / 4;  // words per table entry
+  constexpr int NQ = 1024 / NT;    // entry quads per thread and head
+  static_assert(NW >= GU, "one wave per head builds the chunk rows");
+  static_assert(KPT * 64 <= 65535, "16-bit wave bins");
+  const int kvh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  __shared__ uint32_t s_lut[W][16 * 256];
+  __shared__ uint32_t s_hist[GU][NW][128];
+  // table loads first, then the keys (unconditional, index clamped)
+  uint32_t lv[NQ][GU];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i)
+#pragma unroll
+    for (int g = 0; g < GU; ++g)
+      lv[i][g] = reinterpret_cast<const uint32_t*>(lut + ((int64_t)kvh * GU + g) * 4096)[tid + i * NT];
+  const uint4* src = ids + (int64_t)kvh * cap + S;
+  const int64_t p0 = (int64_t)chunk * (KPT * NT) + tid;
+  uint4 x[KPT];
+#pragma unroll
+  for (int t = 0; t < KPT; ++t) {
+    const int64_t p = p0 + t * NT;
+    x[t] = src[p < E ? p : E - 1];
+  }
+  // interleave: entry 4 q + e gets byte e of head g's word in byte g % 4
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int q4 = tid + i * NT;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int g = 4 * w; g < 4 * w + 4 && g < GU; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] |= ((lv[i][g] >> (8 * e)) & 0xFFu) << (8 * (g & 3));
+      reinterpret_cast<uint4*>(&s_lut[w][0])[q4] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  for (int i = tid; i < GU * NW * 128; i += NT) (&s_hist[0][0][0])[i] = 0;
+  __syncthreads();
+
+  uint32_t zeros[GU];
+#pragma unroll
+  for (int g = 0; g < GU; ++g) zeros[g] = 0;
+#pragma unroll
+  for (int t = 0; t < KPT; ++t) {
+    const int64_t p = p0 + t * NT;
+    const bool valid = p < E;
+    const uint32_t w4[4] = {x[t].x, x[t].y, x[t].z, x[t].w};
+    uint32_t acc[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) acc[w] = 0;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const uint32_t v = (w4[b >> 2] >> ((b & 3) * 8)) & 0xFFu;
+#pragma unroll
+      for (int w = 0; w < W; ++w) acc[w] += s_lut[w][b * 256 + v];
+    }
+#pragma unroll
+    for (int g = 0; g < GU; ++g) {
+      const uint32_t sc = (acc[g >> 2] >> (8 * (g & 3))) & 0xFFu;
+      zeros[g] += (uint32_t)__popcll(__ballot(valid && sc == 0));
+      if (valid) {
+        scores[((int64_t)kvh * GU + g) * Epad + p] = (uint8_t)sc;
+        if (sc != 0) atomicAdd(&s_hist[g][wv][sc >> 1], 1u << (16 * (sc & 1)));
+      }
+    }
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int g = 0; g < GU; ++g) atomicAdd(&s_hist[g][wv][0], zeros[g]);
+  __syncthreads();
+  // sum the wave histograms of every head into its row 0 (bins stay packed)
+  for (int i = tid; i < GU * 128; i += NT) {
+    const int g = i >> 7, wd = i & 127;
+    uint32_t a = s_hist[g][0][wd];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) a += s_hist[g][w][wd];
+    s_hist[g][0][wd] = a;
+  }
+  __syncthreads();
+  // wave g: head g's row = #(score >= v), lane l owning bins 4 l .. 4 l + 3
+  if (wv < GU) {
+    const int g = wv;
+    const uint32_t wa = s_hist[g][0][2 * lane], wb = s_hist[g][0][2 * lane + 1];
+    const uint32_t hv[4] = {wa & 0xFFFFu, wa >> 16, wb & 0xFFFFu, wb >> 16};
+    uint32_t h[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = (4 * lane + r < nbins) ? hv[r] : 0u;
+    const uint32_t loc = h[0] + h[1] + h[2] + h[3];
+    uint32_t inc = loc;  // sum over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t t = __shfl_down(inc, off);
+      if (lane + off < 64) inc += t;
+    }
+    uint32_t ge[4];
+    ge[3] = inc - loc + h[3];
+    ge[2] = ge[3] + h[2];
+    ge[1] = ge[2] + h[1];
+    ge[0] = ge[1] + h[0];
+    uint32_t* row = chist + (((int64_t)kvh * GU + g) * chunk_stride + chunk) * rstride;
+    if (4 * lane < rstride) reinterpret_cast<uint4*>(row)[lane] = make_uint4(ge[0], ge[1], ge[2], ge[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // K4a threshold: [TS] Coarse Candidate Generation keeps the top fraction.
 // Candidates = the first C eligible keys in (score desc, index asc) order:
 // T = largest v with #(score >= v) >= C; every key with score > T, plus the
@@ -1813,6 +1937,29 @@ hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t
   const dim3 grid(nchunks, BH);
   const uint4* id4 = (const uint4*)ids;
   constexpr int NT = kScanThreads;
+  if (unit_div > 1 && kpt >= 2) {
+    // unshared retrieval: one pass per KV head for its unit_div query heads
+    const dim3 gg(nchunks, BH / unit_div);
+#define PKV_SG(K, GU)                                                                           \
+  return launch(k_scan_group<(K * 256) / NT, NT, GU>, gg, dim3(NT), st, ev, id4, cap, S, E, lut, \
+                scores, Epad, chist, chunk_stride, nbins, rstride)
+#define PKV_SGK(GU)        \
+  switch (kpt) {           \
+    case 2: PKV_SG(2, GU); \
+    case 4: PKV_SG(4, GU); \
+    case 8: PKV_SG(8, GU); \
+    case 16: PKV_SG(16, GU); \
+    default: return hipErrorInvalidValue; \
+  }
+    switch (unit_div) {
+      case 2: PKV_SGK(2);
+      case 4: PKV_SGK(4);
+      case 8: PKV_SGK(8);
+      default: return hipErrorInvalidValue;
+    }
+#undef PKV_SGK
+#undef PKV_SG
+  }
   switch (kpt) {
 #define PKV_SCAN(K)                                                                          \
   case K:                                                                                    \

@@ -19,6 +19,15 @@ CASES = {
              per_query_head=True),
     "sinks": W("per head, sinks", 1, 3, 6, 128, 7001, "bf16", cand_num=1,
                cand_den=10, k=200, sinks=64, seed=72, per_query_head=True),
+    # large enough for chunks of 512 or more keys, where one scan pass serves
+    # all G query heads of a KV head: G = 4 with 2048-key chunks, G = 8 and
+    # G = 2 (m = 4) with 512-key chunks
+    "gqa4_long": W("per head, GQA 4, 140K", 1, 8, 32, 128, 140000, "bf16",
+                   k=1024, seed=73, per_query_head=True),
+    "gqa8": W("per head, GQA 8", 1, 2, 16, 128, 70000, "bf16", k=512, sinks=16,
+              seed=74, per_query_head=True),
+    "gqa2_m4": W("per head, GQA 2, m 4", 4, 4, 8, 128, 40000, "bf16", B=32,
+                 k=256, seed=75, per_query_head=True),
 }
 
 
@@ -50,7 +59,7 @@ def test_per_query_head_retrieval(orc, name):
     Kh, Vh, Qh = host_f32(K), host_f32(V), host_f32(Q)
     BH = w.batch * w.n_kv_heads
     enc = oracle_encode_heads(orc, w, Kh, lay["signs"], list(range(BH)))
-    ids, nib, wq = pk.pariskv_debug_export(L.handle, 0, w.N, BH)
+    ids, nib, wq = pk.pariskv_debug_export(L.handle, 0, w.N, BH, B=w.B)
     for bh in range(BH):
         assert np.array_equal(ids[bh], enc[bh][0])
         assert np.array_equal(nib[bh], enc[bh][1])
