@@ -6,7 +6,8 @@ benchmark's ``cpu_baseline`` leg may import this package.  The product path
 
 The arithmetic lives in ``oracle.c`` (plain C, -O2 -ffp-contract=off); this
 module only marshals numpy arrays.  Every function cites, in ``oracle.c``, the
-passage of "Technical Summary: ParisKV" it follows; the pins that check each
+passage of "Technical Summary: ParisKV" (or, for the Self-Indexing workload,
+of "Self-Indexing KVCache") it follows; the pins that check each
 function against closed forms, invariants and brute force are in
 ``tests/test_oracle_pins.py``.
 """
@@ -64,6 +65,10 @@ def lib():
             "orc_topk": (i32, [i64, P, P, i64, i64, P]),
             "orc_attention": (i32, [i32, i32, i64, P, P, P, P, f64, P]),
             "orc_exact_topk": (i32, [i32, i32, P, i64, i64, P, i64, P]),
+            "orc_si_build": (i32, [i32, i64, i64, P, P, P, P]),
+            "orc_si_ids": (i32, [i32, i64, P, P, P]),
+            "orc_si_lut": (i32, [i32, i32, P, P, P]),
+            "orc_si_scores": (i32, [i32, i64, i64, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -246,3 +251,60 @@ def retrieve_head(signs, Q, ids, nib, w, *, m, rho, tiers, S, k, num, den):
     idx = topk(cand, est, kprime, S)
     return dict(yq=yq, lut=lut, top=top, scores=sc, C=Cn, cand=cand, est=est,
                 idx=idx)
+
+
+# ------------------------------------------------------- Self-Indexing ----
+
+def si_build(X, S: int):
+    """Prefill index of one (b, h): X [n, d] fp32 keys, S sinks.
+    -> mean fp32 [d], ids uint8 [n, d/4], cb fp32 [d/4, 16, 4]."""
+    X = _c(X, np.float32)
+    n, d = X.shape
+    mean = np.zeros(d, np.float32)
+    ids = np.zeros((n, d // 4), np.uint8)
+    cb = np.zeros((d // 4, 16, 4), np.float32)
+    _ok(lib().orc_si_build(d, n, S, _p(X), _p(mean), _p(ids), _p(cb)))
+    return mean, ids, cb
+
+
+def si_ids(X, mean):
+    """Sign ids of appended keys with the prefill means -> uint8 [n, d/4]."""
+    X = _c(X, np.float32)
+    mean = _c(mean, np.float32)
+    n, d = X.shape
+    ids = np.zeros((n, d // 4), np.uint8)
+    _ok(lib().orc_si_ids(d, n, _p(X), _p(mean), _p(ids)))
+    return ids
+
+
+def si_lut(Q, cb):
+    """Q [G, d] fp32 query heads of one KV group -> lut fp32 [d/4, 16]."""
+    Q = _c(Q, np.float32)
+    cb = _c(cb, np.float32)
+    G, d = Q.shape
+    lut = np.zeros((d // 4, 16), np.float32)
+    _ok(lib().orc_si_lut(d, G, _p(Q), _p(cb), _p(lut)))
+    return lut
+
+
+def si_scores(ids, lut, S: int):
+    ids = _c(ids, np.uint8)
+    lut = _c(lut, np.float32)
+    n, B = ids.shape
+    sc = np.zeros(max(n - S, 0), np.float32)
+    _ok(lib().orc_si_scores(4 * B, n, S, _p(ids), _p(lut), _p(sc)))
+    return sc
+
+
+def si_retrieve_head(Q, ids, cb, *, S, k):
+    """Self-Indexing retrieval for one (batch, KV head): LUT, scores of keys
+    [S, N), and the top-k (sinks first, then the k - S best scores by
+    (score desc, position asc), ascending) with their scores."""
+    N = ids.shape[0]
+    if not (0 <= S < k <= N):
+        raise ValueError("need 0 <= S < k <= N")
+    lut = si_lut(Q, cb)
+    sc = si_scores(ids, lut, S)
+    cand = np.arange(S, N, dtype=np.int32)
+    idx = topk(cand, sc, k - S, S)
+    return dict(lut=lut, scores=sc, idx=idx, est=sc[idx[S:] - S])

@@ -22,6 +22,10 @@
  *   [ICML] "ParisKV: Fast and Drift-Robust KV-Cache Retrieval for
  *          Long-Context LLMs" (ICML 2026 poster abstract): collision-based
  *          candidate selection followed by quantised inner-product reranking.
+ *   [SI]  "Self-Indexing KVCache: Predicting Sparse Attention from
+ *         Compressed Keys" (gist.science/paper/2603.14224), Methodology A-C:
+ *         the second workload (channel-mean centring, 4-dim sign-pattern
+ *         clusters with mean centroids, LUT-GEMV scores, sink tokens).
  *
  * Where the pages leave a step open, the plainest reading is taken; each
  * such reading is stated at the function that implements it.
@@ -606,5 +610,131 @@ int orc_exact_topk(int d, int G, const float *Q, int64_t N, int64_t S,
     for (int64_t c = 0; c < kprime; c++) out[c] = v[c].idx;
     qsort(out, (size_t)kprime, sizeof(int64_t), cmp_i64);
     free(qb); free(v);
+    return ORC_OK;
+}
+
+/* ======================================================================== */
+/* Self-Indexing workload.                                                   */
+/* [SI] "Self-Indexing KVCache: Predicting Sparse Attention from Compressed  */
+/* Keys" (gist.science/paper/2603.14224), Methodology A "One-Pass Sign-Based */
+/* Vector Quantization", B "Compressed-Domain Top-k Retrieval (LUT-GEMV)",   */
+/* C "Sink Tokens".                                                          */
+/* ======================================================================== */
+
+/* Prefill index of one (b, h).  Readings:                                  */
+/*  - A.4 entropy-aware normalisation: the channel means are taken over the */
+/*    indexed prefill keys [S, n) (the S sink tokens stay in full precision */
+/*    and outside the index), sum in fp64 in key order, divided by the     */
+/*    count in fp64, rounded once to fp32; n == S gives mean 0.            */
+/*  - y = fp32(x - mean) for every key.                                     */
+/*  - A.1/A.2 sub-vectors are the contiguous groups of 4 coordinates; the  */
+/*    id of sub-vector b is sum_j [y_{4b+j} < 0] 2^j (zero on the + side). */
+/*  - A.3 the centroid of cluster (b, p) is the mean of y_b over the        */
+/*    prefill keys [S, n) with id_b = p (fp64 sum in key order / count,     */
+/*    rounded once to fp32); an empty cluster has centroid 0.               */
+/* ids [n][d/4] (every key gets ids), mean [d], cb [d/4][16][4].            */
+int orc_si_build(int d, int64_t n, int64_t S, const float *X, float *mean,
+                 uint8_t *ids, float *cb)
+{
+    if (d < 4 || d % 4 || n < 0 || S < 0) return ORC_EINVAL;
+    int B = d / 4;
+    int64_t m = n > S ? n - S : 0;
+    for (int c = 0; c < d; c++) {
+        double a = 0.0;
+        for (int64_t i = S; i < n; i++) a += (double)X[i * d + c];
+        mean[c] = m > 0 ? (float)(a / (double)m) : 0.0f;
+    }
+    for (int64_t i = 0; i < n; i++)
+        for (int b = 0; b < B; b++) {
+            unsigned id = 0;
+            for (int j = 0; j < 4; j++) {
+                float y = X[i * d + 4 * b + j] - mean[4 * b + j];
+                if (y < 0.0f) id |= 1u << j;
+            }
+            ids[i * B + b] = (uint8_t)id;
+        }
+    double *sum = (double *)calloc((size_t)B * 64, sizeof(double));
+    int64_t *cnt = (int64_t *)calloc((size_t)B * 16, sizeof(int64_t));
+    if (!sum || !cnt) { free(sum); free(cnt); return ORC_EINVAL; }
+    for (int64_t i = S; i < n; i++)
+        for (int b = 0; b < B; b++) {
+            int p = ids[i * B + b];
+            cnt[b * 16 + p]++;
+            for (int j = 0; j < 4; j++) {
+                float y = X[i * d + 4 * b + j] - mean[4 * b + j];
+                sum[(b * 16 + p) * 4 + j] += (double)y;
+            }
+        }
+    for (int e = 0; e < B * 16; e++)
+        for (int j = 0; j < 4; j++)
+            cb[e * 4 + j] = cnt[e] ? (float)(sum[e * 4 + j] / (double)cnt[e]) : 0.0f;
+    free(sum); free(cnt);
+    return ORC_OK;
+}
+
+/* Sign ids of keys appended after the prefill, with the prefill means (the */
+/* codebook is built once, in the prefill: [SI] Methodology A.3).           */
+int orc_si_ids(int d, int64_t n, const float *X, const float *mean, uint8_t *ids)
+{
+    if (d < 4 || d % 4 || n < 0) return ORC_EINVAL;
+    int B = d / 4;
+    for (int64_t i = 0; i < n; i++)
+        for (int b = 0; b < B; b++) {
+            unsigned id = 0;
+            for (int j = 0; j < 4; j++) {
+                float y = X[i * d + 4 * b + j] - mean[4 * b + j];
+                if (y < 0.0f) id |= 1u << j;
+            }
+            ids[i * B + b] = (uint8_t)id;
+        }
+    return ORC_OK;
+}
+
+/* [SI] Methodology B, the query's lookup table: the dot product of the     */
+/* query sub-vector with each of the 16 centroids.  The query of a KV head  */
+/* is the mean of its G query heads, as for ParisKV (fp32: q_0 + q_1 + ...  */
+/* in head order, times fp32(1/G)).  lut[b][p] = ((0 + q_{4b} c_0) +        */
+/* q_{4b+1} c_1) + ... in fp32.  The centring by the key means is left out  */
+/* of the query side: it shifts every key's score by the same <q, mean>.   */
+int orc_si_lut(int d, int G, const float *Q, const float *cb, float *lut)
+{
+    if (d < 4 || d % 4 || G < 1) return ORC_EINVAL;
+    int B = d / 4;
+    float invG = 1.0f / (float)G;
+    for (int b = 0; b < B; b++) {
+        float qb[4];
+        for (int j = 0; j < 4; j++) {
+            float acc = Q[4 * b + j];
+            for (int g = 1; g < G; g++) acc = acc + Q[(int64_t)g * d + 4 * b + j];
+            qb[j] = acc * invG;
+        }
+        for (int p = 0; p < 16; p++) {
+            float s = 0.0f;
+            for (int j = 0; j < 4; j++) s = s + qb[j] * cb[(b * 16 + p) * 4 + j];
+            lut[b * 16 + p] = s;
+        }
+    }
+    return ORC_OK;
+}
+
+/* [SI] Methodology B, the approximate score of a key: the sum of its LUT   */
+/* entries.  Reading of the fp32 order: the sub-vectors are taken in pairs  */
+/* (2t, 2t + 1), each pair summed first, and the pair sums added in order:  */
+/* s = 0; for t: s = s + (lut[2t][id_2t] + lut[2t+1][id_2t+1]).  Scores of  */
+/* keys [S, n).                                                              */
+int orc_si_scores(int d, int64_t n, int64_t S, const uint8_t *ids,
+                  const float *lut, float *scores)
+{
+    if (d < 8 || d % 8 || S < 0) return ORC_EINVAL;
+    int B = d / 4;
+    for (int64_t i = S; i < n; i++) {
+        float s = 0.0f;
+        for (int t = 0; t < B / 2; t++) {
+            float pr = lut[(2 * t) * 16 + ids[i * B + 2 * t]] +
+                       lut[(2 * t + 1) * 16 + ids[i * B + 2 * t + 1]];
+            s = s + pr;
+        }
+        scores[i - S] = s;
+    }
     return ORC_OK;
 }
