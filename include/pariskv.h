@@ -357,6 +357,134 @@ PARISKV_API int32_t pariskv_window_attn_profiled(const pariskv_window *w,
 PARISKV_API void pariskv_window_destroy(pariskv_window *w);
 
 /* ---------------------------------------------------------------------- */
+/* Self-Indexing retrieval (a second workload on the same machinery).      */
+/* [SI] "Self-Indexing KVCache: Predicting Sparse Attention from          */
+/* Compressed Keys" (gist.science/paper/2603.14224), Methodology:          */
+/*  A.4  keys are centred by their channel means mu (over the indexed      */
+/*       prefill keys [S, n_keys) of each (b, h)), y = fp32(k - mu);       */
+/*  A.1-2 y splits into 32 sub-vectors of 4 coordinates, each coded by its  */
+/*       sign pattern: id_b = sum_j [y_{4b+j} < 0] 2^j, 16 clusters;       */
+/*  A.3  the centroid of cluster (b, p) is the mean of its members' y_b    */
+/*       (over the same prefill keys; an empty cluster has centroid 0);    */
+/*  B    a query's LUT holds lut_b[p] = <qbar_b, c_{b,p}> and a key's score */
+/*       is the sum of its LUT entries; the top-k by score is selected;    */
+/*  C    the S sink tokens [0, S) are always selected and never scored.    */
+/* Decode keys appended later are coded with the prefill means and join    */
+/* the same clusters; the codebook is not updated.  qbar is the mean of    */
+/* the G query heads of a KV head, as for ParisKV.  Arithmetic (fp32, no   */
+/* contraction): lut_b[p] = ((0 + qbar_{4b} c_0) + qbar_{4b+1} c_1) + ...; */
+/* score = sum over the key's 16 id bytes s, in order from 0, of           */
+/* (lut_{2s}[id_{2s}] + lut_{2s+1}[id_{2s+1}]).  Means and centroids are   */
+/* accumulated in fp64 and rounded once to fp32.  Selection order: (score  */
+/* desc, position asc).  Attention over the selection: pariskv_sparse_attn. */
+/* ---------------------------------------------------------------------- */
+
+/* Shapes of a Self-Indexing index.
+ *   head_dim   d (this build: 128).
+ *   n_sink     S, keys [0, S) always selected, outside the means/codebook.
+ *   batch, n_kv_heads, n_q_heads   as pariskv_config (G in {1, 2, 4, 8}).
+ *   key_dtype  PARISKV_DTYPE_BF16 or _FP32 (K and Q).
+ *   capacity   keys per (b, h); capacity - S <= 4,194,304. */
+typedef struct pariskv_si_config {
+    int32_t head_dim;
+    int32_t n_sink;
+    int32_t batch;
+    int32_t n_kv_heads;
+    int32_t n_q_heads;
+    int32_t key_dtype;
+    int64_t capacity;
+} pariskv_si_config;
+
+typedef struct pariskv_si_index pariskv_si_index; /* opaque host-side handle */
+
+/* Stages pariskv_si_retrieve_topk_profiled brackets: LUT, scan, threshold,
+ * compaction, top-k histogram, top-k select. */
+#define PARISKV_SI_STAGES 6
+
+/* Bytes of the device index buffer: per key and (b, h) 16 B of sign ids
+ * (byte s: id_{2s} in the low nibble, id_{2s+1} in the high nibble), plus
+ * per (b, h) the 128 fp32 means and the 32 x 16 x 4 fp32 centroids.
+ * Errors: INVALID_ARG / UNSUPPORTED for a bad config. */
+PARISKV_API int32_t pariskv_si_index_bytes(const pariskv_si_config *cfg,
+                                           size_t *bytes);
+
+/* Bytes of the device scratch pariskv_si_build_index needs for n_keys keys
+ * (per-chunk fp64 partial sums; free after the build has run). */
+PARISKV_API int32_t pariskv_si_build_workspace_bytes(
+    const pariskv_si_config *cfg, int64_t n_keys, size_t *bytes);
+
+/* Bytes of the device workspace pariskv_si_retrieve_topk needs for any index
+ * size up to capacity (scores and candidate lists for up to capacity - S
+ * keys per (b, h)). */
+PARISKV_API int32_t pariskv_si_retrieve_workspace_bytes(
+    const pariskv_si_config *cfg, int32_t k, size_t *bytes);
+
+/* Creates a handle over `index_buf` (device, >= si_index_bytes, 256-byte
+ * aligned, must outlive the handle): means and codebook from keys
+ * [S, n_keys), sign ids of keys [0, n_keys), asynchronously on `stream`.
+ *   K   device-accessible, key_dtype, element (b, h, i, j) at
+ *       K[((b * n_kv_heads + h) * k_rows_per_head + i) * d + j].
+ *   build_ws   device scratch of >= si_build_workspace_bytes(n_keys) bytes,
+ *       in use until the build's kernels have run on `stream`.
+ * Errors: INVALID_ARG, UNSUPPORTED, CAPACITY, WORKSPACE, NOMEM, HIP. */
+PARISKV_API int32_t pariskv_si_build_index(
+    const pariskv_si_config *cfg, void *index_buf, size_t index_bytes,
+    const void *K, int64_t k_rows_per_head, int64_t n_keys, void *build_ws,
+    size_t build_ws_bytes, void *stream, pariskv_si_index **out);
+
+/* Codes n_new keys per (b, h) (rows K_new[(b * n_kv_heads + h) *
+ * new_rows_per_head + r], device-accessible) with the stored means,
+ * asynchronously on `stream`.  Errors: INVALID_ARG, CAPACITY, HIP. */
+PARISKV_API int32_t pariskv_si_append_keys(pariskv_si_index *index,
+                                           const void *K_new,
+                                           int64_t new_rows_per_head,
+                                           int64_t n_new, void *stream);
+
+/* Current number of keys per (b, h), or -1 for a NULL handle. */
+PARISKV_API int64_t pariskv_si_index_size(const pariskv_si_index *index);
+
+/* Frees the host handle (never the caller's buffers). */
+PARISKV_API void pariskv_si_index_destroy(pariskv_si_index *index);
+
+/* Top-k of every (b, KV head) by LUT-GEMV score, asynchronously on `stream`.
+ *   Q          device [batch][n_q_heads][d], key_dtype.
+ *   k          S < k <= N.
+ *   out_idx    device int32 [batch * n_kv_heads][k]: the sinks 0..S-1, then
+ *              the k - S selected positions in ascending order.
+ *   out_score  optional device fp32 [batch * n_kv_heads][k - S]: scores of
+ *              out_idx[S..] in the same order.
+ *   ws         device workspace of >= si_retrieve_workspace_bytes bytes
+ *              (no initialisation needed; one call at a time per ws).
+ * Errors: INVALID_ARG, WORKSPACE, HIP. */
+PARISKV_API int32_t pariskv_si_retrieve_topk(const pariskv_si_index *index,
+                                             const void *Q, int32_t k,
+                                             int32_t *out_idx, float *out_score,
+                                             void *ws, size_t ws_bytes,
+                                             void *stream);
+
+/* Same, with 2 * PARISKV_SI_STAGES caller-created hipEvent_t (start/stop per
+ * stage, stamped by the kernels' own dispatches). */
+PARISKV_API int32_t pariskv_si_retrieve_topk_profiled(
+    const pariskv_si_index *index, const void *Q, int32_t k, int32_t *out_idx,
+    float *out_score, void *ws, size_t ws_bytes, void *stream, void **events);
+
+/* Parity-test introspection (synchronous).  ids_host [b][h][hi - lo][32]
+ * (one 4-bit id per byte), mean_host [b][h][128], codebook_host
+ * [b][h][32][16][4]; any may be NULL. */
+PARISKV_API int32_t pariskv_si_debug_export(const pariskv_si_index *index,
+                                            int64_t lo, int64_t hi,
+                                            uint8_t *ids_host, float *mean_host,
+                                            float *codebook_host);
+
+/* Intermediates of the last pariskv_si_retrieve_topk that used `ws`:
+ * which = 0: LUT fp32 [b][h][32][16]; 1: scores fp32 [b][h][N - S];
+ * 2: int32 [b][h][4] = (threshold bin T, #bin > T, #bin == T, candidates). */
+PARISKV_API int32_t pariskv_si_debug_intermediate(const pariskv_si_index *index,
+                                                  int32_t k, const void *ws,
+                                                  size_t ws_bytes, int32_t which,
+                                                  void *dst, size_t dst_bytes);
+
+/* ---------------------------------------------------------------------- */
 /* Introspection for parity tests (synchronous; not for the hot path).     */
 /* ---------------------------------------------------------------------- */
 

@@ -48,6 +48,18 @@ class pariskv_config(C.Structure):
     ]
 
 
+class pariskv_si_config(C.Structure):
+    _fields_ = [
+        ("head_dim", C.c_int32),
+        ("n_sink", C.c_int32),
+        ("batch", C.c_int32),
+        ("n_kv_heads", C.c_int32),
+        ("n_q_heads", C.c_int32),
+        ("key_dtype", C.c_int32),
+        ("capacity", C.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -100,6 +112,19 @@ def lib():
             "pariskv_window_attn_profiled": (i32, [P, P, P, i32, C.c_float, P, P, sz, P,
                                                    C.POINTER(P)]),
             "pariskv_window_destroy": (None, [P]),
+            "pariskv_si_index_bytes": (i32, [P, C.POINTER(sz)]),
+            "pariskv_si_build_workspace_bytes": (i32, [P, i64, C.POINTER(sz)]),
+            "pariskv_si_retrieve_workspace_bytes": (i32, [P, i32, C.POINTER(sz)]),
+            "pariskv_si_build_index": (i32, [P, P, sz, P, i64, i64, P, sz, P,
+                                              C.POINTER(P)]),
+            "pariskv_si_append_keys": (i32, [P, P, i64, i64, P]),
+            "pariskv_si_index_size": (i64, [P]),
+            "pariskv_si_index_destroy": (None, [P]),
+            "pariskv_si_retrieve_topk": (i32, [P, P, i32, P, P, P, sz, P]),
+            "pariskv_si_retrieve_topk_profiled": (i32, [P, P, i32, P, P, P, sz, P,
+                                                        C.POINTER(P)]),
+            "pariskv_si_debug_export": (i32, [P, i64, i64, P, P, P]),
+            "pariskv_si_debug_intermediate": (i32, [P, i32, P, sz, i32, P, sz]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -407,6 +432,164 @@ class Layer:
     def close(self):
         if self.handle:
             pariskv_index_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------- Self-Indexing ----
+
+PARISKV_SI_STAGES = 6
+SI_DEBUG_LUT, SI_DEBUG_SCORES, SI_DEBUG_META = 0, 1, 2
+
+
+def make_si_config(*, head_dim=128, n_sink=0, batch=1, n_kv_heads=1, n_q_heads=1,
+                   key_dtype=PARISKV_DTYPE_BF16, capacity=4096):
+    c = pariskv_si_config()
+    c.head_dim, c.n_sink, c.batch = head_dim, n_sink, batch
+    c.n_kv_heads, c.n_q_heads, c.key_dtype, c.capacity = (n_kv_heads, n_q_heads,
+                                                          key_dtype, capacity)
+    return c
+
+
+def si_config_for(w, capacity=None):
+    """pariskv_si_config for a synth.Workload (its shapes and sinks)."""
+    return make_si_config(head_dim=w.d, n_sink=w.sinks, batch=w.batch,
+                          n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
+                          key_dtype=PARISKV_DTYPE_BF16 if w.dtype == "bf16"
+                          else PARISKV_DTYPE_FP32, capacity=capacity or w.N)
+
+
+def _size_call(fn, *args) -> int:
+    n = C.c_size_t()
+    _check(fn(*args, C.byref(n)))
+    return n.value
+
+
+def pariskv_si_index_bytes(cfg) -> int:
+    return _size_call(lib().pariskv_si_index_bytes, C.byref(cfg))
+
+
+def pariskv_si_build_workspace_bytes(cfg, n_keys) -> int:
+    return _size_call(lib().pariskv_si_build_workspace_bytes, C.byref(cfg), int(n_keys))
+
+
+def pariskv_si_retrieve_workspace_bytes(cfg, k) -> int:
+    return _size_call(lib().pariskv_si_retrieve_workspace_bytes, C.byref(cfg), int(k))
+
+
+def pariskv_si_build_index(cfg, index_buf, K, k_rows_per_head, n_keys, build_ws,
+                           stream=None):
+    h = C.c_void_p()
+    _check(lib().pariskv_si_build_index(C.byref(cfg), _ptr(index_buf), _nbytes(index_buf),
+                                        _ptr(K), int(k_rows_per_head), int(n_keys),
+                                        _ptr(build_ws), _nbytes(build_ws),
+                                        _stream(stream), C.byref(h)))
+    return h
+
+
+def pariskv_si_append_keys(handle, K_new, new_rows_per_head, n_new, stream=None):
+    _check(lib().pariskv_si_append_keys(handle, _ptr(K_new), int(new_rows_per_head),
+                                        int(n_new), _stream(stream)))
+
+
+def pariskv_si_index_size(handle) -> int:
+    return int(lib().pariskv_si_index_size(handle))
+
+
+def pariskv_si_index_destroy(handle):
+    lib().pariskv_si_index_destroy(handle)
+
+
+def pariskv_si_retrieve_topk(handle, Q, k, out_idx, out_score, ws, stream=None):
+    _check(lib().pariskv_si_retrieve_topk(handle, _ptr(Q), int(k), _ptr(out_idx),
+                                          _ptr(out_score), _ptr(ws), _nbytes(ws),
+                                          _stream(stream)))
+
+
+def pariskv_si_retrieve_topk_profiled(handle, Q, k, out_idx, out_score, ws, events,
+                                      stream=None):
+    _check(lib().pariskv_si_retrieve_topk_profiled(
+        handle, _ptr(Q), int(k), _ptr(out_idx), _ptr(out_score), _ptr(ws), _nbytes(ws),
+        _stream(stream), _events(events)))
+
+
+def pariskv_si_debug_export(handle, lo, hi, BH, d=128):
+    n = hi - lo
+    ids = np.zeros((BH, n, d // 4), np.uint8)
+    mean = np.zeros((BH, d), np.float32)
+    cb = np.zeros((BH, d // 4, 16, 4), np.float32)
+    _check(lib().pariskv_si_debug_export(handle, int(lo), int(hi),
+                                         ids.ctypes.data_as(C.c_void_p),
+                                         mean.ctypes.data_as(C.c_void_p),
+                                         cb.ctypes.data_as(C.c_void_p)))
+    return ids, mean, cb
+
+
+def pariskv_si_debug_intermediate(handle, k, ws, which, BH, E, d=128):
+    shape, dt = {
+        SI_DEBUG_LUT: ((BH, d // 4, 16), np.float32),
+        SI_DEBUG_SCORES: ((BH, E), np.float32),
+        SI_DEBUG_META: ((BH, 4), np.int32),
+    }[which]
+    out = np.zeros(shape, dt)
+    _check(lib().pariskv_si_debug_intermediate(handle, int(k), _ptr(ws), _nbytes(ws), which,
+                                               out.ctypes.data_as(C.c_void_p),
+                                               out.nbytes))
+    return out
+
+
+class SiLayer:
+    """One layer's Self-Indexing index over torch device buffers (the index,
+    the build scratch, released after the build, and the retrieval and
+    attention workspaces)."""
+
+    def __init__(self, cfg, K, n_keys, *, k, device="cuda", stream=None):
+        import torch
+        self.cfg = cfg
+        self.k = int(k)
+        self.BH = cfg.batch * cfg.n_kv_heads
+        self.index_buf = torch.empty(pariskv_si_index_bytes(cfg), dtype=torch.uint8,
+                                     device=device)
+        build_ws = torch.empty(pariskv_si_build_workspace_bytes(cfg, n_keys),
+                               dtype=torch.uint8, device=device)
+        self.ws = torch.empty(pariskv_si_retrieve_workspace_bytes(cfg, self.k),
+                              dtype=torch.uint8, device=device)
+        self.attn_ws = torch.empty(
+            pariskv_attn_workspace_bytes(cfg.batch, cfg.n_q_heads, self.k, cfg.head_dim),
+            dtype=torch.uint8, device=device)
+        self.handle = pariskv_si_build_index(cfg, self.index_buf, K, K.shape[2], n_keys,
+                                             build_ws, stream)
+        # the build's kernels must finish before the scratch is released
+        (stream or torch.cuda.current_stream()).synchronize()
+        del build_ws
+
+    @property
+    def size(self) -> int:
+        return pariskv_si_index_size(self.handle)
+
+    def append(self, K_new, n_new, rows_per_head=None, stream=None):
+        pariskv_si_append_keys(self.handle, K_new,
+                               rows_per_head if rows_per_head is not None
+                               else K_new.shape[2], n_new, stream)
+
+    def retrieve(self, Q, out_idx, out_score=None, stream=None):
+        pariskv_si_retrieve_topk(self.handle, Q, self.k, out_idx, out_score, self.ws, stream)
+
+    def attend(self, Q, K, V, idx, out, scale=None, stream=None):
+        c = self.cfg
+        pariskv_sparse_attn(Q, K, V, K.shape[2], idx, self.k, c.batch, c.n_q_heads,
+                            c.n_kv_heads, c.head_dim, c.key_dtype,
+                            scale if scale is not None else c.head_dim ** -0.5, out,
+                            self.attn_ws, stream)
+
+    def close(self):
+        if self.handle:
+            pariskv_si_index_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

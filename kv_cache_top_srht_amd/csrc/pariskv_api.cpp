@@ -246,8 +246,8 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   e = pkv::launch_scan(kpt, nch, BH, ix->ids, c->capacity, S, E, lut, scores, L.Epad, chist,
                        (int)L.nchunks_max, L.nbins, L.rstride, udiv, st, ev(1));
   if (e != hipSuccess) return hip_status(e);
-  e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, L.rstride, C, meta, coff,
-                         st, ev(2));
+  e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, L.rstride, C, 0, meta,
+                         coff, st, ev(2));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_compact_rerank(m_of(c), kpt, nch, BH, scores, L.Epad, S, E, meta, coff,
                                  (int)L.nchunks_max, ptab, ix->rec, c->capacity, cand, est,

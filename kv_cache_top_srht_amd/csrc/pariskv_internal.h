@@ -52,8 +52,8 @@ hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t
                        uint32_t* chist, int chunk_stride, int nbins, int rstride,
                        int unit_div, hipStream_t st, const EvPair& ev);
 hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nchunks, int nbins,
-                         int rstride, int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st,
-                         const EvPair& ev);
+                         int rstride, int64_t C, int all_ties, int32_t* meta, uint32_t* coff,
+                         hipStream_t st, const EvPair& ev);
 hipError_t launch_compact_rerank(int m, int kpt, int nchunks, int BH, const uint8_t* scores,
                                  int64_t Epad, int64_t S, int64_t E, const int32_t* meta,
                                  const uint32_t* coff, int chunk_stride, const float* ptab,
@@ -65,6 +65,36 @@ hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cs
                        int nchunks, uint32_t* range, uint32_t* rows, int32_t* tkmeta,
                        uint2* sorted, int32_t* out_idx, float* out_est, hipStream_t st,
                        const EvPair& ev_hist, const EvPair& ev_select);
+// top-k with per-unit candidate counts read from cmeta[unit * 4 + 3] on the
+// device (at most Cmax); hist + general select
+hipError_t launch_topk_counted(int BH, const float* est, const int32_t* cand, int64_t cstride,
+                               const int32_t* cmeta, int Cmax, int kprime, int S, int k,
+                               const uint32_t* mmc, int chunk_stride, int nchunks,
+                               uint32_t* range, uint32_t* rows, int32_t* tkmeta, uint2* sorted,
+                               int32_t* out_idx, float* out_est, hipStream_t st,
+                               const EvPair& ev_hist, const EvPair& ev_select);
+
+// Self-Indexing workload: keys per build chunk (channel and cluster sums)
+constexpr int kSiChunk = 4096;
+size_t si_build_ws_bytes(int BH, int64_t S, int64_t n);
+hipError_t launch_si_build(int dtype, const void* K, int64_t rows_per_head, int64_t S, int64_t n,
+                           int BH, int64_t cap, uint8_t* ids, float* mean, float* cb,
+                           void* build_ws, hipStream_t st);
+hipError_t launch_si_encode(int dtype, const void* K, int64_t rows_per_head, int64_t lo, int64_t n,
+                            int BH, const float* mean, int64_t cap, uint8_t* ids, hipStream_t st);
+hipError_t launch_si_lut(int dtype, const void* Q, int units, int n_kv_heads, int G,
+                         const float* cb, float* lut, float* tab, float* range, hipStream_t st,
+                         const EvPair& ev);
+hipError_t launch_si_scan(int kpt, int nchunks, int units, const uint8_t* ids, int64_t cap,
+                          int64_t S, int64_t E, const float* tab, const float* range,
+                          float* fscore, uint8_t* bins, int64_t Epad, uint32_t* chist,
+                          int chunk_stride, hipStream_t st, const EvPair& ev);
+hipError_t launch_si_compact(int kpt, int nchunks, int units, const uint8_t* bins,
+                             const float* fscore, int64_t Epad, int64_t S, int64_t E,
+                             const int32_t* meta, const uint32_t* coff, int chunk_stride,
+                             int32_t* cand, float* est, int64_t cstride, uint32_t* mm,
+                             hipStream_t st, const EvPair& ev);
+
 // candidates per top-k block and the largest threshold bin ranked pairwise
 constexpr int kTopkSlice = 4096;
 constexpr int kTopkMaxMembers = 4096;

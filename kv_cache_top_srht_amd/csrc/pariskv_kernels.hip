@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "codebook_tables.h"
+#include "pariskv_device.h"
 #include "pariskv_internal.h"
 
 #pragma clang fp contract(off)
@@ -47,35 +48,6 @@ template <int M>
 __device__ __forceinline__ float cb_thresh(int i) {
   if constexpr (M == 8) return c_thresh[i];
   else return c_thresh4[i];
-}
-
-// ---------------------------------------------------------------------------
-// Element loads: 8 consecutive elements of a bf16 or fp32 row as fp32.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
-
-__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
-  uint4 v = *reinterpret_cast<const uint4*>(p);
-  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
-}
-__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
-  float4 a = reinterpret_cast<const float4*>(p)[0];
-  float4 b = reinterpret_cast<const float4*>(p)[1];
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-
-// Order key of an estimate: unsigned order == (est desc) order, -0 == +0.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (f == 0.0f) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-// Inverse of order_key (a -0 input comes back as +0).
-__device__ __forceinline__ float key_float(uint32_t o) {
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
 // ---------------------------------------------------------------------------
@@ -205,44 +177,6 @@ __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ K, int64_t
   const int64_t bh = g / n;
   const int64_t r = g - bh * n;
   encode_key<T, M>(K, rows_per_head, bh, r, lo + r, cap, ids, rec, sg, c, sub);
-}
-
-// ---------------------------------------------------------------------------
-// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
-// 4 and 8 within each row of 16 lanes, then the last lane of row 0 (2) added
-// to row 1 (3) and the last lane of row 1 added to rows 2 and 3.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return x;
-}
-
-// ---------------------------------------------------------------------------
-// Block-wide exclusive scan of a pair of uint32 values (NT threads): DPP
-// scans within each wave, wave totals through LDS.
-// ---------------------------------------------------------------------------
-template <int NT>
-__device__ __forceinline__ uint2 block_exscan2(uint2 v, uint2* s_warp, uint2& total) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint32_t ix = wave_incl_scan(v.x), iy = wave_incl_scan(v.y);
-  if (lane == 63) s_warp[wv] = make_uint2(ix, iy);
-  __syncthreads();
-  uint2 base = make_uint2(0, 0), tot = make_uint2(0, 0);
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint2 t = s_warp[w];
-    if (w < wv) { base.x += t.x; base.y += t.y; }
-    tot.x += t.x; tot.y += t.y;
-  }
-  __syncthreads();  // s_warp may be reused by the caller
-  total = tot;
-  return make_uint2(base.x + ix - v.x, base.y + iy - v.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -659,7 +593,8 @@ __global__ __launch_bounds__(NT) void k_scan_group(const uint4* __restrict__ ids
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ chist, int chunk_stride,
                                                  int nchunks, int nbins, int rstride, int64_t C,
-                                                 int32_t* __restrict__ meta, uint32_t* __restrict__ coff) {
+                                                 int all_ties, int32_t* __restrict__ meta,
+                                                 uint32_t* __restrict__ coff) {
   const int bh = blockIdx.x, tid = threadIdx.x;
   __shared__ uint32_t s_tot[260];
   __shared__ int s_T;
@@ -697,15 +632,17 @@ __global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ ch
   }
   __syncthreads();
   if (tid < nbins && (int64_t)s_tot[tid] >= C && (int64_t)s_tot[tid + 1] < C) {
+    // all_ties: every key of bin T is kept, so C grows to #(score >= T)
+    const int64_t Ce = all_ties ? (int64_t)s_tot[tid] : C;
     s_T = tid;
     meta[bh * 4 + 0] = tid;
     meta[bh * 4 + 1] = (int32_t)s_tot[tid + 1];
-    meta[bh * 4 + 2] = (int32_t)(C - (int64_t)s_tot[tid + 1]);
-    meta[bh * 4 + 3] = (int32_t)C;
+    meta[bh * 4 + 2] = (int32_t)(Ce - (int64_t)s_tot[tid + 1]);
+    meta[bh * 4 + 3] = (int32_t)Ce;
   }
   __syncthreads();
   const int T = s_T;
-  const int64_t Q = C - (int64_t)s_tot[T + 1];
+  const int64_t Q = (all_ties ? (int64_t)s_tot[T] : C) - (int64_t)s_tot[T + 1];
   uint32_t carry_tie = 0, carry_off = 0;
   for (int c0 = 0; c0 < nchunks; c0 += 1024) {
     const int c = c0 + tid;
@@ -745,59 +682,6 @@ __global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ ch
 // ascending-position order, and the block's estimate range (order keys).
 // Grid (ceil(chunks / 2), b*H_kv), 256 threads.
 // ---------------------------------------------------------------------------
-template <int KPT>
-__device__ __forceinline__ void load_scores(const uint8_t* sp, uint8_t (&sc)[KPT]) {
-  if constexpr (KPT == 16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(sp);
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int t = 0; t < 16; ++t) sc[t] = (uint8_t)(w4[t >> 2] >> ((t & 3) * 8));
-  } else if constexpr (KPT == 8) {
-    const uint2 v = *reinterpret_cast<const uint2*>(sp);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) sc[t] = (uint8_t)(((t < 4) ? v.x : v.y) >> ((t & 3) * 8));
-  } else if constexpr (KPT == 4) {
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(sp);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) sc[t] = (uint8_t)(v >> (t * 8));
-  } else {
-#pragma unroll
-    for (int t = 0; t < KPT; ++t) sc[t] = sp[t];
-  }
-}
-
-// Block-wide exclusive scan of two uint32 values per thread (NT threads),
-// each the packed pair (lo 16 bits, hi 16 bits) of counts whose block total
-// stays below 65536.
-template <int NT>
-__device__ __forceinline__ uint2 block_exscan_packed(uint2 v, uint2* s_warp, uint2& total) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint32_t ix = wave_incl_scan(v.x), iy = wave_incl_scan(v.y);
-  if (lane == 63) s_warp[wv] = make_uint2(ix, iy);
-  __syncthreads();
-  uint2 base = make_uint2(0, 0), tot = make_uint2(0, 0);
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint2 t = s_warp[w];
-    if (w < wv) { base.x += t.x; base.y += t.y; }
-    tot.x += t.x; tot.y += t.y;
-  }
-  total = tot;
-  return make_uint2(base.x + ix - v.x, base.y + iy - v.y);
-}
-
-// the lowest r set bits of m
-__device__ __forceinline__ uint32_t lowest_bits(uint32_t m, uint32_t r) {
-  uint32_t out = 0;
-  for (uint32_t i = 0; i < r && m; ++i) {
-    const uint32_t low = m & (0u - m);
-    out |= low;
-    m ^= low;
-  }
-  return out;
-}
-
 // key masks of one chunk's KPT scores of this thread: bit t of gtm / eqm is
 // set when key t (t < nval) has score > T / == T.  For 8 keys with every
 // score below 128 the bytes are compared four at a time (SWAR: adding
@@ -1127,8 +1011,15 @@ __device__ void topk_radix_block(const float* __restrict__ e, const int32_t* __r
 __global__ __launch_bounds__(1024) void k_topk_hist(
     const float* __restrict__ est, int64_t cstride, int C, int P,
     const uint32_t* __restrict__ mmc, int chunk_stride, int nchunks,
-    uint32_t* __restrict__ rows, uint32_t* __restrict__ range, uint2* __restrict__ sorted) {
+    uint32_t* __restrict__ rows, uint32_t* __restrict__ range, uint2* __restrict__ sorted,
+    const int32_t* __restrict__ cmeta) {
   const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  // cmeta: this unit's candidate count is cmeta[bh * 4 + 3] (grid P is an
+  // upper bound; slices past the unit's own have nothing to do)
+  if (cmeta) {
+    C = cmeta[bh * 4 + 3];
+    if (p * TK_SL >= C) return;
+  }
   const float* e = est + bh * cstride;
   __shared__ uint32_t s_hist[2048];
   __shared__ uint2 s_w[16];
@@ -1191,8 +1082,16 @@ __global__ __launch_bounds__(1024) void k_topk_select(
     const float* __restrict__ est, const int32_t* __restrict__ cand, int64_t cstride, int C,
     int kprime, int S, int k, int P, const uint32_t* __restrict__ range,
     const uint32_t* __restrict__ rows, const uint2* __restrict__ sorted,
-    int32_t* __restrict__ tkmeta, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
+    int32_t* __restrict__ tkmeta, int32_t* __restrict__ out_idx, float* __restrict__ out_est,
+    const int32_t* __restrict__ cmeta) {
   const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  // rows are laid out for P slices; Pu of them are this unit's
+  int Pu = P;
+  if (cmeta) {
+    C = cmeta[bh * 4 + 3];
+    Pu = (C + TK_SL - 1) / TK_SL;
+    if (p >= Pu) return;
+  }
   const float* e = est + bh * cstride;
   const int32_t* cd = cand + bh * cstride;
   int32_t* oi = out_idx + (int64_t)bh * k;
@@ -1215,10 +1114,10 @@ __global__ __launch_bounds__(1024) void k_topk_select(
   const uint32_t* rb = rows + (int64_t)bh * P * 2048;
   for (int b = tid; b < 2048; b += 1024) {
     uint32_t acc = 0;
-    for (int q0 = 0; q0 < P; q0 += 8) {  // 8 rows in flight
+    for (int q0 = 0; q0 < Pu; q0 += 8) {  // 8 rows in flight
       uint32_t v[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) v[r] = (q0 + r < P) ? rb[(int64_t)(q0 + r) * 2048 + b] : 0u;
+      for (int r = 0; r < 8; ++r) v[r] = (q0 + r < Pu) ? rb[(int64_t)(q0 + r) * 2048 + b] : 0u;
 #pragma unroll
       for (int r = 0; r < 8; ++r) acc += v[r];
     }
@@ -1255,7 +1154,7 @@ __global__ __launch_bounds__(1024) void k_topk_select(
   {
     const int q = tid;
     uint32_t nq = 0, sq = 0;
-    if (q < P) {
+    if (q < Pu) {
       sq = (b1 + 1 < 2048) ? rb[(int64_t)q * 2048 + b1 + 1] : 0u;
       nq = rb[(int64_t)q * 2048 + b1] - sq;
     }
@@ -1267,7 +1166,7 @@ __global__ __launch_bounds__(1024) void k_topk_select(
   }
   __syncthreads();
   for (uint32_t j = tid; j < M; j += 1024) {
-    int lo = 0, hi = P - 1;  // last block q with s_pref[q] <= j
+    int lo = 0, hi = Pu - 1;  // last block q with s_pref[q] <= j
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_pref[mid] <= j) lo = mid; else hi = mid - 1;
@@ -1860,13 +1759,6 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 // itself timestamps the kernel's execution (exact per-kernel durations even
 // when launches are host-bound); with null events it is a plain launch.
 // ---------------------------------------------------------------------------
-template <typename F, typename... Args>
-static hipError_t launch(F kernel, dim3 grid, dim3 block, hipStream_t st, const EvPair& ev,
-                         Args... args) {
-  hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev.start, ev.stop, 0, args...);
-  return hipGetLastError();
-}
-
 hipError_t launch_encode(int m, int dtype, const void* K, int64_t rows_per_head, int64_t lo,
                          int64_t n, int BH, int64_t cap, uint8_t* ids, uint32_t* rec,
                          const SignMask& sg, float c, hipStream_t st, const EvPair& ev) {
@@ -1978,10 +1870,10 @@ hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t
 }
 
 hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nchunks, int nbins,
-                         int rstride, int64_t C, int32_t* meta, uint32_t* coff, hipStream_t st,
-                         const EvPair& ev) {
+                         int rstride, int64_t C, int all_ties, int32_t* meta, uint32_t* coff,
+                         hipStream_t st, const EvPair& ev) {
   return launch(k_thresh, dim3(BH), dim3(1024), st, ev, chist, chunk_stride, nchunks, nbins,
-                rstride, C, meta, coff);
+                rstride, C, all_ties, meta, coff);
 }
 
 hipError_t launch_compact_rerank(int m, int kpt, int nchunks, int BH, const uint8_t* scores,
@@ -2030,7 +1922,7 @@ hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cs
     return hipEventRecord(ev_select.stop, st);
   }
   hipError_t e = launch(k_topk_hist, grid, dim3(1024), st, ev_hist, est, cstride, C, P, mmc,
-                        chunk_stride, nchunks, rows, range, sorted);
+                        chunk_stride, nchunks, rows, range, sorted, (const int32_t*)nullptr);
   if (e != hipSuccess) return e;
   if (P <= kTopkFewSlices)
     return launch(k_topk_select_few<kTopkFewSlices>, grid, dim3(1024), st, ev_select, est, cand,
@@ -2038,7 +1930,25 @@ hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cs
                   (const uint2*)sorted, tkmeta, out_idx, out_est);
   return launch(k_topk_select, grid, dim3(1024), st, ev_select, est, cand, cstride, C, kprime, S,
                 k, P, (const uint32_t*)range, (const uint32_t*)rows, (const uint2*)sorted, tkmeta,
-                out_idx, out_est);
+                out_idx, out_est, (const int32_t*)nullptr);
+}
+
+hipError_t launch_topk_counted(int BH, const float* est, const int32_t* cand, int64_t cstride,
+                               const int32_t* cmeta, int Cmax, int kprime, int S, int k,
+                               const uint32_t* mmc, int chunk_stride, int nchunks,
+                               uint32_t* range, uint32_t* rows, int32_t* tkmeta, uint2* sorted,
+                               int32_t* out_idx, float* out_est, hipStream_t st,
+                               const EvPair& ev_hist, const EvPair& ev_select) {
+  // per-unit candidate counts known on the device only: grid for the
+  // largest, the general select (any number of slices)
+  const int P = (Cmax + kTopkSlice - 1) / kTopkSlice;
+  const dim3 grid(P, BH);
+  hipError_t e = launch(k_topk_hist, grid, dim3(1024), st, ev_hist, est, cstride, Cmax, P, mmc,
+                        chunk_stride, nchunks, rows, range, sorted, cmeta);
+  if (e != hipSuccess) return e;
+  return launch(k_topk_select, grid, dim3(1024), st, ev_select, est, cand, cstride, Cmax, kprime,
+                S, k, P, (const uint32_t*)range, (const uint32_t*)rows, (const uint2*)sorted,
+                tkmeta, out_idx, out_est, cmeta);
 }
 
 hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs,
