@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--per-query-head", action="store_true",
                     help="unshared retrieval: every query head selects its own "
                          "top-k with its own query over its KV head's index")
+    ap.add_argument("--si", action="store_true",
+                    help="the Self-Indexing workload instead: sign-VQ index with "
+                         "LUT-GEMV scores over every key, exact top-k, same attention")
     ap.add_argument("--uva", choices=["none", "v", "kv"], default="none",
                     help="keep V (v) or K and V (kv) of every layer in pinned host "
                          "memory, read by the kernels over the host link")
@@ -133,6 +136,8 @@ def main():
         w = w.scaled(cand_num=num, cand_den=den)
     if args.subspaces:
         w = w.scaled(B=args.subspaces)
+    if args.si and (args.window or args.per_query_head or args.uva != "none"):
+        sys.exit("--si runs alone (no --window, --per-query-head or --uva)")
     if args.per_query_head:
         if args.window:
             sys.exit("--per-query-head runs without --window")
@@ -155,6 +160,12 @@ def main():
     layers = []
     for l in range(Lr):
         lay = synth.make_layer(w.scaled(N=cap), dev, layer=l)
+        if args.si:
+            L = pk.SiLayer(pk.si_config_for(w, capacity=cap), lay["K"], w.N, k=w.k,
+                           device=dev)
+            layers.append((L, lay))
+            torch.cuda.synchronize()
+            continue
         cfg = pk.config_for(w, capacity=cap)
         L = pk.Layer(cfg, lay["signs"], lay["K"], w.N - win_L, k=w.k, device=dev)
         if args.window:
@@ -223,8 +234,9 @@ def main():
         else:
             # ev[0:12]: start/stop of the 6 retrieval kernels, ev[12:16]: of
             # the 2 attention kernels, stamped by the dispatches themselves
-            pk.pariskv_retrieve_topk_profiled(L.handle, lay["Q"], w.k, idx, None,
-                                              L.ws, ev[0:12])
+            retr = (pk.pariskv_si_retrieve_topk_profiled if args.si
+                    else pk.pariskv_retrieve_topk_profiled)
+            retr(L.handle, lay["Q"], w.k, idx, None, L.ws, ev[0:12])
             attn = (pk.pariskv_sparse_attn_per_query_head_profiled if w.per_query_head
                     else pk.pariskv_sparse_attn_profiled)
             attn(lay["Q"], lay["K"], lay["V"], cap, idx, w.k, w.batch, w.n_q_heads,
@@ -271,7 +283,10 @@ def main():
     E_prof = np.array(E_of, dtype=np.float64)
     kern = np.array([[events[t][2 * i].elapsed_time(events[t][2 * i + 1])
                       for i in range(8)] for t in range(P)]) * 1e3   # us
-    names = [pk.pariskv_stage_name(i) for i in range(pk.PARISKV_RETRIEVE_STAGES)] + \
+    names = ["si_lut", "si_scan", "threshold", "si_compact", "topk",
+             "topk_second_pass"] if args.si else \
+        [pk.pariskv_stage_name(i) for i in range(pk.PARISKV_RETRIEVE_STAGES)]
+    names = names + \
         ["attn_split", "attn_merge"]
     stage_us = {n: float(kern[:, i].mean()) for i, n in enumerate(names)}
     step_us = np.array([events[t][0].elapsed_time(events[t][15])
@@ -288,14 +303,20 @@ def main():
     scan_us = float(kern[:, 1].mean())
     achieved = scan_bytes / (scan_us * 1e-6) / 1e9
     variant = ("_per_query_head" if w.per_query_head else "") + \
-        ("_m%d" % w.m if w.m != 8 else "")
+        ("_m%d" % w.m if w.m != 8 else "") + ("_si" if args.si else "")
     traffic = read_traffic("vote_scan_%s%s_traffic.txt" % (args.workload, variant),
                            scan_bytes)
     row_bytes = 2 * w.d * (2 if w.dtype == "bf16" else 4) + 4
     attn_bytes = float(U * w.k * row_bytes + 2 * w.batch * w.n_q_heads * w.d *
                        (2 if w.dtype == "bf16" else 4))
     attn_us = float(kern[:, 6].mean())
-    C = pk.pariskv_retrieve_sizes(layers[0][0].handle, w.k)[1]
+    if args.si:
+        meta = pk.pariskv_si_debug_intermediate(layers[0][0].handle, w.k, layers[0][0].ws,
+                                                pk.SI_DEBUG_META, BH,
+                                                layers[0][0].size - w.sinks)
+        C = int(round(float(meta[:, 3].mean())))   # keys in the threshold bin and above
+    else:
+        C = pk.pariskv_retrieve_sizes(layers[0][0].handle, w.k)[1]
     # per candidate: 64 B of codes and B fp16 calibration factors
     rerank_bytes = (64.0 + 2 * w.B) * C * U
     rerank_us = float(kern[:, 3].mean())
@@ -324,6 +345,8 @@ def main():
             "candidates_per_head": C, "layers_in_rotation": Lr,
             "retrieval": ("per query head (%d units)" % U if w.per_query_head
                           else "shared by the %d query heads of a KV head" % w.G),
+            "method": ("Self-Indexing sign VQ + LUT-GEMV over all keys" if args.si
+                       else "ParisKV votes + RSQ-IP rerank"),
             "parallelism": "single GPU", "launch": mode,
             "kv_placement": {"none": "HBM", "v": "V in pinned host memory",
                              "kv": "K and V in pinned host memory"}[args.uva],
@@ -332,7 +355,7 @@ def main():
                        if args.window else None),
         },
         "roofline": {
-            "kernel": "vote_scan",
+            "kernel": "si_scan" if args.si else "vote_scan",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
@@ -350,7 +373,7 @@ def main():
             "algorithmic_bytes_per_launch": attn_bytes,
             "avg_launch_us": attn_us,
         },
-        "rerank_gather": {
+        "rerank_gather": None if args.si else {
             "kernel": "compact_rerank",
             "achieved": rerank_bytes / (rerank_us * 1e-6) / 1e9,
             "unit": "GB/s", "algorithmic_bytes_per_launch": rerank_bytes,
@@ -386,12 +409,12 @@ def main():
     result["stream_copy"] = stream_copy(torch)
     result["roofline"]["frac_of_stream_copy"] = achieved / result["stream_copy"]["gbps"]
     if not args.no_dense and args.uva == "none" and not args.window \
-            and not w.per_query_head:
+            and not w.per_query_head and not args.si:
         result["dense_attention"] = dense_attention(pk, torch, w, layers[0],
                                                     cap, scale, dt_code)
         result["dense_attention"]["speedup_of_step"] = \
             result["dense_attention"]["us"] / us_per_step
-    if not args.no_cpu_baseline and not w.per_query_head:
+    if not args.no_cpu_baseline and not w.per_query_head and not args.si:
         result["cpu_baseline"] = cpu_baseline(w, layers[0][1], args.cpu_steps)
     print(json.dumps(result), flush=True)
 

@@ -66,9 +66,10 @@ hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cs
                        uint2* sorted, int32_t* out_idx, float* out_est, hipStream_t st,
                        const EvPair& ev_hist, const EvPair& ev_select);
 // top-k with per-unit candidate counts read from cmeta[unit * 4 + 3] on the
-// device (at most Cmax); hist + general select
+// device (at most Cmax); hist + general select, grid_slices blocks per unit
 hipError_t launch_topk_counted(int BH, const float* est, const int32_t* cand, int64_t cstride,
-                               const int32_t* cmeta, int Cmax, int kprime, int S, int k,
+                               const int32_t* cmeta, int Cmax, int grid_slices, int kprime,
+                               int S, int k,
                                const uint32_t* mmc, int chunk_stride, int nchunks,
                                uint32_t* range, uint32_t* rows, int32_t* tkmeta, uint2* sorted,
                                int32_t* out_idx, float* out_est, hipStream_t st,

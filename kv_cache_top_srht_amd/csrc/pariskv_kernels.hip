@@ -1008,18 +1008,12 @@ __device__ void topk_radix_block(const float* __restrict__ e, const int32_t* __r
   }
 }
 
-__global__ __launch_bounds__(1024) void k_topk_hist(
+__device__ __forceinline__ void topk_hist_slice(
     const float* __restrict__ est, int64_t cstride, int C, int P,
     const uint32_t* __restrict__ mmc, int chunk_stride, int nchunks,
     uint32_t* __restrict__ rows, uint32_t* __restrict__ range, uint2* __restrict__ sorted,
-    const int32_t* __restrict__ cmeta) {
-  const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  // cmeta: this unit's candidate count is cmeta[bh * 4 + 3] (grid P is an
-  // upper bound; slices past the unit's own have nothing to do)
-  if (cmeta) {
-    C = cmeta[bh * 4 + 3];
-    if (p * TK_SL >= C) return;
-  }
+    int p) {
+  const int bh = blockIdx.y, tid = threadIdx.x;
   const float* e = est + bh * cstride;
   __shared__ uint32_t s_hist[2048];
   __shared__ uint2 s_w[16];
@@ -1078,20 +1072,33 @@ __global__ __launch_bounds__(1024) void k_topk_hist(
   }
 }
 
-__global__ __launch_bounds__(1024) void k_topk_select(
-    const float* __restrict__ est, const int32_t* __restrict__ cand, int64_t cstride, int C,
-    int kprime, int S, int k, int P, const uint32_t* __restrict__ range,
-    const uint32_t* __restrict__ rows, const uint2* __restrict__ sorted,
-    int32_t* __restrict__ tkmeta, int32_t* __restrict__ out_idx, float* __restrict__ out_est,
+// cmeta (optional): this unit's candidate count is cmeta[bh * 4 + 3], at
+// most P slices; the grid may be narrower than the unit's slices, each block
+// then takes slices blockIdx.x, blockIdx.x + gridDim.x, ...
+__global__ __launch_bounds__(1024) void k_topk_hist(
+    const float* __restrict__ est, int64_t cstride, int C, int P,
+    const uint32_t* __restrict__ mmc, int chunk_stride, int nchunks,
+    uint32_t* __restrict__ rows, uint32_t* __restrict__ range, uint2* __restrict__ sorted,
     const int32_t* __restrict__ cmeta) {
-  const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  // rows are laid out for P slices; Pu of them are this unit's
   int Pu = P;
   if (cmeta) {
-    C = cmeta[bh * 4 + 3];
+    C = cmeta[blockIdx.y * 4 + 3];
     Pu = (C + TK_SL - 1) / TK_SL;
-    if (p >= Pu) return;
   }
+  for (int p = blockIdx.x; p < Pu; p += gridDim.x) {
+    topk_hist_slice(est, cstride, C, P, mmc, chunk_stride, nchunks, rows, range, sorted, p);
+    __syncthreads();  // LDS is reused by the next slice
+  }
+}
+
+__device__ __forceinline__ void topk_select_slice(
+    const float* __restrict__ est, const int32_t* __restrict__ cand, int64_t cstride, int C,
+    int kprime, int S, int k, int P, int Pu, const uint32_t* __restrict__ range,
+    const uint32_t* __restrict__ rows, const uint2* __restrict__ sorted,
+    int32_t* __restrict__ tkmeta, int32_t* __restrict__ out_idx, float* __restrict__ out_est,
+    int p) {
+  // rows are laid out for P slices; Pu of them are this unit's
+  const int bh = blockIdx.y, tid = threadIdx.x;
   const float* e = est + bh * cstride;
   const int32_t* cd = cand + bh * cstride;
   int32_t* oi = out_idx + (int64_t)bh * k;
@@ -1221,6 +1228,25 @@ __global__ __launch_bounds__(1024) void k_topk_select(
       if (out_est) out_est[(int64_t)bh * kprime + pos] = f[r];
       ++pos;
     }
+  }
+}
+
+// cmeta as for k_topk_hist; every slice a block takes repeats the resolve
+__global__ __launch_bounds__(1024) void k_topk_select(
+    const float* __restrict__ est, const int32_t* __restrict__ cand, int64_t cstride, int C,
+    int kprime, int S, int k, int P, const uint32_t* __restrict__ range,
+    const uint32_t* __restrict__ rows, const uint2* __restrict__ sorted,
+    int32_t* __restrict__ tkmeta, int32_t* __restrict__ out_idx, float* __restrict__ out_est,
+    const int32_t* __restrict__ cmeta) {
+  int Pu = P;
+  if (cmeta) {
+    C = cmeta[blockIdx.y * 4 + 3];
+    Pu = (C + TK_SL - 1) / TK_SL;
+  }
+  for (int p = blockIdx.x; p < Pu; p += gridDim.x) {
+    topk_select_slice(est, cand, cstride, C, kprime, S, k, P, Pu, range, rows, sorted, tkmeta,
+                      out_idx, out_est, p);
+    __syncthreads();  // LDS is reused by the next slice
   }
 }
 
@@ -1934,15 +1960,16 @@ hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cs
 }
 
 hipError_t launch_topk_counted(int BH, const float* est, const int32_t* cand, int64_t cstride,
-                               const int32_t* cmeta, int Cmax, int kprime, int S, int k,
-                               const uint32_t* mmc, int chunk_stride, int nchunks,
+                               const int32_t* cmeta, int Cmax, int grid_slices, int kprime,
+                               int S, int k, const uint32_t* mmc, int chunk_stride, int nchunks,
                                uint32_t* range, uint32_t* rows, int32_t* tkmeta, uint2* sorted,
                                int32_t* out_idx, float* out_est, hipStream_t st,
                                const EvPair& ev_hist, const EvPair& ev_select) {
-  // per-unit candidate counts known on the device only: grid for the
-  // largest, the general select (any number of slices)
+  // per-unit candidate counts known on the device only: rows laid out for
+  // the largest (P slices), a grid of grid_slices blocks per unit looping
+  // over the unit's own slices; the general select (any number of slices)
   const int P = (Cmax + kTopkSlice - 1) / kTopkSlice;
-  const dim3 grid(P, BH);
+  const dim3 grid(grid_slices < P ? grid_slices : P, BH);
   hipError_t e = launch(k_topk_hist, grid, dim3(1024), st, ev_hist, est, cstride, Cmax, P, mmc,
                         chunk_stride, nchunks, rows, range, sorted, cmeta);
   if (e != hipSuccess) return e;

@@ -160,9 +160,12 @@ int32_t si_retrieve_impl(const pariskv_si_index* ix, const void* Q, int32_t k, i
   e = pkv::launch_si_compact(kpt, nch, BH, bins, fscore, L.Epad, S, E, meta, coff,
                              (int)L.nchunks_max, cand, est, L.cstride, mmc, st, ev(3));
   if (e != hipSuccess) return hip_status(e);
-  e = pkv::launch_topk_counted(BH, est, cand, L.cstride, meta, (int)E, (int)kp, (int)S, k, mmc,
-                               (int)L.nchunks_max, nch, tkrange, rows, tkmeta, sorted, out_idx,
-                               out_score, st, ev(4), ev(5));
+  // candidates are usually a little over k' (the keys of the bins down to
+  // the one holding rank k'): blocks for twice that, more slices are looped
+  const int grid_slices = (int)ceil_div(2 * kp, pkv::kTopkSlice) + 1;
+  e = pkv::launch_topk_counted(BH, est, cand, L.cstride, meta, (int)E, grid_slices, (int)kp,
+                               (int)S, k, mmc, (int)L.nchunks_max, nch, tkrange, rows, tkmeta,
+                               sorted, out_idx, out_score, st, ev(4), ev(5));
   return hip_status(e);
 }
 
