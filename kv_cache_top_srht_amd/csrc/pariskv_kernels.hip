@@ -369,19 +369,32 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
 // within the chunk.
 // Grid (chunks, b*H_kv); chunk = KPT * 256 keys.
 // ---------------------------------------------------------------------------
-template <int KPT, int NT>
-__device__ __forceinline__ void scan_chunk(const uint4 (&x)[KPT], int chunk, int64_t E,
-                                           const uint8_t* s_lut, uint32_t (*s_hist)[256],
-                                           uint8_t* __restrict__ dst, uint32_t* __restrict__ row,
-                                           int nbins, int rstride) {
+// The keys of one chunk: loads (clamped to E - 1 unless the chunk is full,
+// i.e. FULL), the LUT into LDS, then per key the score byte and the wave
+// histogram.  A full chunk has no per-key bounds tests.
+template <int KPT, int NT, bool FULL>
+__device__ __forceinline__ void scan_keys(const uint4* __restrict__ src, int chunk, int64_t E,
+                                          const uint4 lutv, uint8_t* s_lut,
+                                          uint32_t (*s_hist)[256], uint8_t* __restrict__ dst) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t p0 = (int64_t)chunk * (KPT * NT) + tid;
+  uint4 x[KPT];
+#pragma unroll
+  for (int t = 0; t < KPT; ++t) {
+    const int64_t p = p0 + t * NT;
+    x[t] = src[(FULL || p < E) ? p : E - 1];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // the LUT store waits for the LUT load alone (issued before the keys)
+  reinterpret_cast<uint4*>(s_lut)[tid & 255] = lutv;
+  for (int i = tid; i < NW * 256; i += NT) (&s_hist[0][0])[i] = 0;
+  __syncthreads();
   uint32_t zeros = 0;
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
     const int64_t p = p0 + t * NT;
-    const bool valid = p < E;
+    const bool valid = FULL || p < E;
     const uint32_t w4[4] = {x[t].x, x[t].y, x[t].z, x[t].w};
     uint32_t sc = 0;
 #pragma unroll
@@ -394,6 +407,14 @@ __device__ __forceinline__ void scan_chunk(const uint4 (&x)[KPT], int chunk, int
     }
   }
   if (lane == 0) s_hist[wv][0] = zeros;
+}
+
+// The chunk's cumulative row from the wave histograms.
+template <int NT>
+__device__ __forceinline__ void scan_rows(uint32_t (*s_hist)[256], uint32_t* __restrict__ row,
+                                          int nbins, int rstride) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   __syncthreads();
   // sum the wave histograms into row 0
   for (int v = tid; v < nbins; v += NT) {
@@ -432,29 +453,22 @@ __global__ __launch_bounds__(NT) void k_scan(const uint4* __restrict__ ids, int6
                                              uint8_t* __restrict__ scores, int64_t Epad,
                                              uint32_t* __restrict__ chist, int chunk_stride, int nbins,
                                              int rstride, int unit_div) {
-  constexpr int NW = NT / 64;
   const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   __shared__ uint8_t s_lut[16 * 256];
-  __shared__ uint32_t s_hist[NW][256];
-  // The LUT load goes out first: loads complete in issue order, so the LUT
-  // is written to LDS while the keys are still in flight.  The key loads are
-  // unconditional (index clamped; keys past E are not used), which keeps
-  // each wait down to the loads it needs.
-  uint4 lutv = make_uint4(0, 0, 0, 0);
-  if (tid < 256) lutv = reinterpret_cast<const uint4*>(lut + (int64_t)bh * 4096)[tid];
-  const uint4* src = ids + (int64_t)(bh / unit_div) * cap + S;  // the unit's KV head
-  const int64_t p0 = (int64_t)chunk * (KPT * NT) + tid;
-  uint4 x[KPT];
-#pragma unroll
-  for (int t = 0; t < KPT; ++t) {
-    const int64_t p = p0 + t * NT;
-    x[t] = src[p < E ? p : E - 1];
-  }
-  if (tid < 256) reinterpret_cast<uint4*>(s_lut)[tid] = lutv;
-  for (int i = tid; i < NW * 256; i += NT) (&s_hist[0][0])[i] = 0;
-  __syncthreads();
-  scan_chunk<KPT, NT>(x, chunk, E, s_lut, s_hist, scores + bh * Epad,
-                      chist + ((int64_t)bh * chunk_stride + chunk) * rstride, nbins, rstride);
+  __shared__ uint32_t s_hist[NT / 64][256];
+  // The LUT load goes out first, from every thread (a load under a branch
+  // would make the compiler wait for it at the join, before the key loads
+  // are issued; threads tid and tid + 256 store the same bytes).
+  const uint4 lutv = reinterpret_cast<const uint4*>(lut + (int64_t)bh * 4096)[tid & 255];
+  __builtin_amdgcn_sched_barrier(0);
+  const int kvh = unit_div == 1 ? bh : bh / unit_div;  // the unit's KV head
+  const uint4* src = ids + (int64_t)kvh * cap + S;
+  uint8_t* dst = scores + bh * Epad;
+  if ((int64_t)(chunk + 1) * (KPT * NT) <= E)
+    scan_keys<KPT, NT, true>(src, chunk, E, lutv, s_lut, s_hist, dst);
+  else
+    scan_keys<KPT, NT, false>(src, chunk, E, lutv, s_lut, s_hist, dst);
+  scan_rows<NT>(s_hist, chist + ((int64_t)bh * chunk_stride + chunk) * rstride, nbins, rstride);
 }
 
 // ---------------------------------------------------------------------------
