@@ -32,8 +32,9 @@ sys.path.insert(0, ROOT)
 METRIC = ("decode retrieval+sparse-attn µs/step/layer and keys scanned/s "
           "at 128K-1M ctx")
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "kv_cache_top_srht_amd", "csrc",
-                          "pariskv_kernels.hip")
+# the sources the vote-scan kernel is built from
+KERNEL_SRC = [os.path.join(ROOT, "kv_cache_top_srht_amd", "csrc", f)
+              for f in ("pariskv_kernels.hip", "pariskv_device.h", "pariskv_internal.h")]
 
 
 def parse():
@@ -83,7 +84,10 @@ def parse():
 
 
 def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(name: str, launches_bytes: float):
