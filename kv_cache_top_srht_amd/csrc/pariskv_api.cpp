@@ -246,12 +246,22 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   e = pkv::launch_scan(kpt, nch, BH, ix->ids, c->capacity, S, E, lut, scores, L.Epad, chist,
                        (int)L.nchunks_max, L.nbins, L.rstride, udiv, st, ev(1));
   if (e != hipSuccess) return hip_status(e);
-  e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, L.rstride, C, 0, meta,
-                         coff, st, ev(2));
-  if (e != hipSuccess) return hip_status(e);
+  // up to kFusedThreshChunks chunks per unit the compaction finds the
+  // threshold itself (the stage's events are then recorded back to back)
+  const bool fused_thresh = nch <= pkv::kFusedThreshChunks;
+  if (fused_thresh) {
+    const pkv::EvPair tp = ev(2);
+    if (tp.start && (e = hipEventRecord(tp.start, st)) != hipSuccess) return hip_status(e);
+    if (tp.stop && (e = hipEventRecord(tp.stop, st)) != hipSuccess) return hip_status(e);
+  } else {
+    e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, L.nbins, L.rstride, C, 0, meta,
+                           coff, st, ev(2));
+    if (e != hipSuccess) return hip_status(e);
+  }
   e = pkv::launch_compact_rerank(m_of(c), kpt, nch, BH, scores, L.Epad, S, E, meta, coff,
                                  (int)L.nchunks_max, ptab, ix->rec, c->capacity, cand, est,
-                                 L.cstride, C, mmc, L.nbins, udiv, st, ev(3));
+                                 L.cstride, C, mmc, L.nbins, udiv, fused_thresh ? chist : nullptr,
+                                 L.rstride, meta, st, ev(3));
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_topk(BH, est, cand, L.cstride, (int)C, (int)kp, (int)S, k, P, mmc,
                        (int)L.nchunks_max, nch, range, rows, tkmeta, sorted, out_idx, out_est, st,

@@ -31,6 +31,8 @@ struct AppendJob {
 constexpr int kMaxFusedAppend = 48;
 // scan chunks per compact + rerank block (1 or 2)
 constexpr int kCompactChunks = 2;
+// up to this many chunks per unit, compact + rerank finds the threshold itself
+constexpr int kFusedThreshChunks = 256;
 // threads of a vote-scan block (256 or 512; chunks of 4+ keys per 256 threads)
 constexpr int kScanThreads = 512;
 
@@ -54,12 +56,15 @@ hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t
 hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nchunks, int nbins,
                          int rstride, int64_t C, int all_ties, int32_t* meta, uint32_t* coff,
                          hipStream_t st, const EvPair& ev);
+// chist (optional, nchunks <= kFusedThreshChunks): the chunk rows, read
+// instead of meta / coff (no threshold kernel); meta_out then receives meta
 hipError_t launch_compact_rerank(int m, int kpt, int nchunks, int BH, const uint8_t* scores,
                                  int64_t Epad, int64_t S, int64_t E, const int32_t* meta,
                                  const uint32_t* coff, int chunk_stride, const float* ptab,
                                  const uint32_t* rec, int64_t cap, int32_t* cand, float* est,
                                  int64_t cstride, int64_t C, uint32_t* mm, int nbins,
-                                 int unit_div, hipStream_t st, const EvPair& ev);
+                                 int unit_div, const uint32_t* chist, int rstride,
+                                 int32_t* meta_out, hipStream_t st, const EvPair& ev);
 hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cstride, int C,
                        int kprime, int S, int k, int P, const uint32_t* mmc, int chunk_stride,
                        int nchunks, uint32_t* range, uint32_t* rows, int32_t* tkmeta,

@@ -741,14 +741,20 @@ __device__ __forceinline__ float quad_lane(float v) {
 constexpr int kPtabRow = 132;
 constexpr int kPtabLds = 16 * kPtabRow;
 
-template <int KPT, int CPB, int M>
+// FT (at most kFusedThreshChunks chunks per unit): no separate threshold
+// kernel.  Every block finds T and the tie quota from the column sums of the
+// unit's chunk rows, and its chunks' offsets from block scans over the rows
+// before them -- the K4a arithmetic, repeated per block (block 0 of each unit
+// also writes meta); meta and coff are then not read.
+template <int KPT, int CPB, int M, bool FT>
 __global__ __launch_bounds__(256) void k_compact_rerank(
     const uint8_t* __restrict__ scores, int64_t Epad, int64_t S, int64_t E,
     const int32_t* __restrict__ meta, const uint32_t* __restrict__ coff, int chunk_stride,
     int nchunks, const float* __restrict__ ptab, const uint32_t* __restrict__ rec,
     int64_t cap, int32_t* __restrict__ cand,
     float* __restrict__ est, int64_t cstride, int64_t C, uint32_t* __restrict__ mm, int swar,
-    int unit_div) {
+    int unit_div, const uint32_t* __restrict__ chist, int nbins, int rstride,
+    int32_t* __restrict__ meta_out) {
   constexpr int CH = KPT * 256;
   const int bh = blockIdx.y, tid = threadIdx.x;
   const int c0 = blockIdx.x * CPB;
@@ -758,16 +764,22 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
   __shared__ uint2 s_w2[4];
   __shared__ uint32_t s_mm[8];
   // global reads first
-  const int T = meta[bh * 4 + 0];
-  const int64_t Q = meta[bh * 4 + 2];
-  uint32_t off_c[2], tieb_c[2];
+  int T = 0;
+  int64_t Q = 0;
+  uint32_t off_c[2] = {0, 0}, tieb_c[2] = {0, 0};
+  if constexpr (!FT) {
+    T = meta[bh * 4 + 0];
+    Q = meta[bh * 4 + 2];
+  }
   uint8_t sc[2][KPT];
   uint2 raw[2] = {make_uint2(0, 0), make_uint2(0, 0)};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int chunk = c0 + (h < nc ? h : 0);
-    off_c[h] = coff[((int64_t)bh * chunk_stride + chunk) * 2 + 0];
-    tieb_c[h] = coff[((int64_t)bh * chunk_stride + chunk) * 2 + 1];
+    if constexpr (!FT) {
+      off_c[h] = coff[((int64_t)bh * chunk_stride + chunk) * 2 + 0];
+      tieb_c[h] = coff[((int64_t)bh * chunk_stride + chunk) * 2 + 1];
+    }
     const uint8_t* sp = scores + bh * Epad + (int64_t)chunk * CH + tid * KPT;
     if constexpr (KPT == 8) {
       raw[h] = *reinterpret_cast<const uint2*>(sp);
@@ -783,6 +795,82 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
     const float4 v0 = src[tid], v1 = src[tid + 256];
     reinterpret_cast<float4*>(s_P + (tid >> 5) * kPtabRow)[tid & 31] = v0;
     reinterpret_cast<float4*>(s_P + ((tid + 256) >> 5) * kPtabRow)[tid & 31] = v1;
+  }
+  if constexpr (FT) {
+    __shared__ uint32_t s_tot[260];
+    __shared__ int s_T;
+    const uint32_t* hb = chist + (int64_t)bh * chunk_stride * rstride;
+    // column sums as K4a: thread = (row r0, group g of 4 bins), 16-byte loads,
+    // 8 rows in flight per thread, summed in registers, then LDS atomics
+    s_tot[tid] = 0u;
+    if (tid < 4) s_tot[256 + tid] = 0u;
+    const int ng = rstride >> 2, rpp = 256 / ng;
+    const int g = tid % ng, r0 = tid / ng;
+    uint32_t acc[4] = {0u, 0u, 0u, 0u};
+    if (r0 < rpp) {
+      const uint4* h4 = reinterpret_cast<const uint4*>(hb);
+      for (int rb = r0; rb < nchunks; rb += 8 * rpp) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = rb + u * rpp;
+          v[u] = h4[(int64_t)(row < nchunks ? row : nchunks - 1) * ng + g];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (rb + u * rpp < nchunks) {
+            acc[0] += v[u].x;
+            acc[1] += v[u].y;
+            acc[2] += v[u].z;
+            acc[3] += v[u].w;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (r0 < rpp) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (acc[i] && 4 * g + i < nbins) atomicAdd(&s_tot[4 * g + i], acc[i]);
+    }
+    __syncthreads();
+    if (tid < nbins && (int64_t)s_tot[tid] >= C && (int64_t)s_tot[tid + 1] < C) s_T = tid;
+    __syncthreads();
+    T = s_T;
+    Q = C - (int64_t)s_tot[T + 1];
+    if (blockIdx.x == 0 && tid == 0) {
+      meta_out[bh * 4 + 0] = T;
+      meta_out[bh * 4 + 1] = (int32_t)s_tot[T + 1];
+      meta_out[bh * 4 + 2] = (int32_t)Q;
+      meta_out[bh * 4 + 3] = (int32_t)C;
+    }
+    // row r = tid: ties before it and its output offset (as K4a)
+    uint32_t gt = 0, eq = 0;
+    if (tid < nchunks) {
+      const uint32_t* hc = hb + (int64_t)tid * rstride;
+      gt = (T + 1 < nbins) ? hc[T + 1] : 0u;
+      eq = hc[T] - gt;
+    }
+    uint2 tot;
+    const uint2 ex = block_exscan2<256>(make_uint2(eq, 0), s_w2, tot);
+    int64_t quota = Q - (int64_t)ex.x;
+    if (quota < 0) quota = 0;
+    const uint32_t sel = gt + (uint32_t)((int64_t)eq < quota ? eq : quota);
+    const uint2 ex2 = block_exscan2<256>(make_uint2(sel, 0), s_w2, tot);
+    // hand the two chunks' values to every thread
+    __shared__ uint32_t s_co[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (tid == c0 + (h < nc ? h : 0)) {
+        s_co[2 * h] = ex2.x;
+        s_co[2 * h + 1] = ex.x;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      off_c[h] = s_co[2 * h];
+      tieb_c[h] = s_co[2 * h + 1];
+    }
   }
   // candidate masks and counts of both chunks, one block scan
   int64_t quota[2];
@@ -1921,26 +2009,32 @@ hipError_t launch_compact_rerank(int m, int kpt, int nchunks, int BH, const uint
                                  const uint32_t* coff, int chunk_stride, const float* ptab,
                                  const uint32_t* rec, int64_t cap, int32_t* cand, float* est,
                                  int64_t cstride, int64_t C, uint32_t* mm, int nbins,
-                                 int unit_div, hipStream_t st, const EvPair& ev) {
+                                 int unit_div, const uint32_t* chist, int rstride,
+                                 int32_t* meta_out, hipStream_t st, const EvPair& ev) {
+  // chist: fold the threshold into this kernel (nchunks <= kFusedThreshChunks)
+  const bool ft = chist != nullptr;
   const int swar = nbins <= 128 ? 1 : 0;  // every score below 128
   const dim3 grid((nchunks + kCompactChunks - 1) / kCompactChunks, BH);
-#define PKV_CR(K, MM)                                                                         \
+#define PKV_CR(K, MM, FT)                                                                     \
   case K:                                                                                     \
-    return launch(k_compact_rerank<K, kCompactChunks, MM>, grid, dim3(256), st, ev, scores,   \
-                  Epad, S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, cand, est,     \
-                  cstride, C, mm, swar, unit_div);
+    return launch(k_compact_rerank<K, kCompactChunks, MM, FT>, grid, dim3(256), st, ev,       \
+                  scores, Epad, S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, cand,  \
+                  est, cstride, C, mm, swar, unit_div, chist, nbins, rstride, meta_out);
+#define PKV_CRK(MM, FT)                                                                      \
+  switch (kpt) {                                                                             \
+    PKV_CR(1, MM, FT) PKV_CR(2, MM, FT) PKV_CR(4, MM, FT) PKV_CR(8, MM, FT) PKV_CR(16, MM, FT) \
+    default: return hipErrorInvalidValue;                                                    \
+  }
+  if (ft && nchunks > kFusedThreshChunks) return hipErrorInvalidValue;
   if (m == 8) {
-    switch (kpt) {
-      PKV_CR(1, 8) PKV_CR(2, 8) PKV_CR(4, 8) PKV_CR(8, 8) PKV_CR(16, 8)
-      default: return hipErrorInvalidValue;
-    }
+    if (ft) PKV_CRK(8, true);
+    PKV_CRK(8, false);
   }
   if (m == 4) {
-    switch (kpt) {
-      PKV_CR(1, 4) PKV_CR(2, 4) PKV_CR(4, 4) PKV_CR(8, 4) PKV_CR(16, 4)
-      default: return hipErrorInvalidValue;
-    }
+    if (ft) PKV_CRK(4, true);
+    PKV_CRK(4, false);
   }
+#undef PKV_CRK
 #undef PKV_CR
   return hipErrorInvalidValue;
 }
