@@ -51,6 +51,13 @@ SMALL = {
                        sinks=32, seed=23),
     "m4_rho8": W("m 4, rho 8", 1, 2, 8, 128, 30000, "bf16", B=32, rho=8,
                  tiers=(7, 6, 5, 4, 3, 2, 1, 1), k=512, seed=24),
+    # degenerate sizes: one key to select, one eligible key, E a whole number
+    # of 256-key chunks (no partial chunk) and one key more (a 1-key chunk)
+    "kprime_one": W("k' = 1", 1, 2, 8, 128, 700, "bf16", k=33, sinks=32, seed=25),
+    "e_one": W("E = 1", 1, 1, 4, 128, 17, "bf16", k=17, sinks=16, seed=26),
+    "e_chunks_exact": W("E = 16 chunks", 1, 1, 4, 128, 4096, "bf16", k=64, seed=27),
+    "e_chunks_plus_one": W("E = 16 chunks + 1", 1, 1, 4, 128, 4097, "bf16", k=64,
+                           seed=28),
 }
 
 
@@ -248,3 +255,31 @@ def test_attention_dense_and_sparse(orc, G, dtype, k, N):
         ref = orc.attention(Qh[b, h * G:(h + 1) * G], Kh[b, h], Vh[b, h], ih[bh],
                             128 ** -0.5)
         assert np.max(np.abs(oh[b, h * G:(h + 1) * G] - ref)) <= tol
+
+
+def test_append_to_capacity(orc):
+    """Appends fill the index exactly to its capacity (then one more key is
+    refused on the host); the full index retrieves as the oracle does."""
+    N0, cap = 3000, 3040
+    w = W("append to capacity", 1, 2, 8, 128, cap, "bf16", k=100, sinks=4, seed=29)
+    case("append to capacity N0=%d cap=%d" % (N0, cap))
+    lay = synth.make_layer(w, "cuda")
+    cfg = pk.config_for(w, capacity=cap)
+    L = pk.Layer(cfg, lay["signs"], lay["K"], N0, k=w.k)
+    L.append(lay["K"][:, :, N0:], cap - N0 - 1, rows_per_head=cap)
+    L.append(lay["K"][:, :, cap - 1:], 1, rows_per_head=cap)
+    assert L.size == cap
+    with pytest.raises(pk.PariskvError):
+        L.append(lay["K"][:, :, cap - 1:], 1, rows_per_head=cap)
+    BH = w.batch * w.n_kv_heads
+    idx = torch.empty(BH, w.k, dtype=torch.int32, device="cuda")
+    est = torch.empty(BH, w.kprime, dtype=torch.float32, device="cuda")
+    L.retrieve(lay["Q"], idx, est)
+    torch.cuda.synchronize()
+    Kh, Qh = host_f32(lay["K"]), host_f32(lay["Q"])
+    enc = oracle_encode_heads(orc, w, Kh, lay["signs"], list(range(BH)))
+    ref = oracle_retrieve_heads(orc, w, Qh, enc, lay["signs"], list(range(BH)))
+    gi = gpu_intermediates(L, BH)
+    for bh in range(BH):
+        assert_retrieval_equal(w, gi, idx.cpu().numpy(), est.cpu().numpy(), ref[bh], bh)
+    L.close()
