@@ -390,6 +390,7 @@ def main():
                              "p50": float(np.percentile(step_us, 50)),
                              "p90": float(np.percentile(step_us, 90))},
         "kernel_sha256_16": kernel_sha(),
+        "gpu": gpu_info(torch),
     }
 
     # warm figure: the same step repeated on one layer, whose bucket ids stay
@@ -421,6 +422,18 @@ def main():
     if not args.no_cpu_baseline and not w.per_query_head and not args.si:
         result["cpu_baseline"] = cpu_baseline(w, layers[0][1], args.cpu_steps)
     print(json.dumps(result), flush=True)
+
+
+def gpu_info(torch):
+    """Name, architecture, compute units and clock of the GPU the run used."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1)}
+    clk = getattr(p, "clock_rate", None)
+    if clk:
+        info["clock_mhz"] = clk / 1000.0
+    return info
 
 
 def exact_topk_rows(torch, w, lay, n):
