@@ -1,0 +1,123 @@
+// Host-only stand-ins for the library's kernel launchers, so that the
+// C-ABI sources (pariskv_api.cpp, si_api.cpp) build with g++ under the
+// address and undefined-behaviour sanitizers and their validation, layout,
+// handle and error paths run without a GPU.  Every launcher succeeds
+// without touching memory.  Test infrastructure only.
+#include <hip/hip_runtime.h>
+
+#include "codebook_tables.h"
+#include "pariskv_internal.h"
+
+namespace pkv {
+
+hipError_t launch_encode(int m, int dtype, const void* K, int64_t rows_per_head, int64_t lo,
+                         int64_t n, int BH, int64_t cap, uint8_t* ids, uint32_t* rec,
+                         const SignMask& sg, float c, hipStream_t st, const EvPair& ev) {
+  return hipSuccess;
+}
+
+hipError_t launch_qprep(int m, int dtype, const void* Q, int BH, int n_kv_heads, int G,
+                        const SignMask& sg, float c, int rho, const Tiers& tw, uint8_t* lut,
+                        float* yq, float* ptab, const AppendJob& app, int unit_div,
+                        hipStream_t st, const EvPair& ev) {
+  return hipSuccess;
+}
+
+hipError_t launch_scan(int kpt, int nchunks, int BH, const uint8_t* ids, int64_t cap, int64_t S,
+                       int64_t E, const uint8_t* lut, uint8_t* scores, int64_t Epad,
+                       uint32_t* chist, int chunk_stride, int nbins, int rstride,
+                       int unit_div, hipStream_t st, const EvPair& ev) {
+  return hipSuccess;
+}
+
+hipError_t launch_thresh(int BH, const uint32_t* chist, int chunk_stride, int nchunks, int nbins,
+                         int rstride, int64_t C, int all_ties, int32_t* meta, uint32_t* coff,
+                         hipStream_t st, const EvPair& ev) {
+  return hipSuccess;
+}
+
+hipError_t launch_compact_rerank(int m, int kpt, int nchunks, int BH, const uint8_t* scores,
+                                 int64_t Epad, int64_t S, int64_t E, const int32_t* meta,
+                                 const uint32_t* coff, int chunk_stride, const float* ptab,
+                                 const uint32_t* rec, int64_t cap, int32_t* cand, float* est,
+                                 int64_t cstride, int64_t C, uint32_t* mm, int nbins,
+                                 int unit_div, const uint32_t* chist, int rstride,
+                                 int32_t* meta_out, hipStream_t st, const EvPair& ev) {
+  return hipSuccess;
+}
+
+hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cstride, int C,
+                       int kprime, int S, int k, int P, const uint32_t* mmc, int chunk_stride,
+                       int nchunks, uint32_t* range, uint32_t* rows, int32_t* tkmeta,
+                       uint2* sorted, int32_t* out_idx, float* out_est, hipStream_t st,
+                       const EvPair& ev_hist, const EvPair& ev_select) {
+  return hipSuccess;
+}
+
+hipError_t launch_topk_counted(int BH, const float* est, const int32_t* cand, int64_t cstride,
+                               const int32_t* cmeta, int Cmax, int grid_slices, int kprime,
+                               int S, int k,
+                               const uint32_t* mmc, int chunk_stride, int nchunks,
+                               uint32_t* range, uint32_t* rows, int32_t* tkmeta, uint2* sorted,
+                               int32_t* out_idx, float* out_est, hipStream_t st,
+                               const EvPair& ev_hist, const EvPair& ev_select) {
+  return hipSuccess;
+}
+
+hipError_t launch_si_build(int dtype, const void* K, int64_t rows_per_head, int64_t S, int64_t n,
+                           int BH, int64_t cap, uint8_t* ids, float* mean, float* cb,
+                           void* build_ws, hipStream_t st) {
+  return hipSuccess;
+}
+
+hipError_t launch_si_encode(int dtype, const void* K, int64_t rows_per_head, int64_t lo, int64_t n,
+                            int BH, const float* mean, int64_t cap, uint8_t* ids, hipStream_t st) {
+  return hipSuccess;
+}
+
+hipError_t launch_si_lut(int dtype, const void* Q, int units, int n_kv_heads, int G,
+                         const float* cb, float* lut, float* tab, float* range, hipStream_t st,
+                         const EvPair& ev) {
+  return hipSuccess;
+}
+
+hipError_t launch_si_scan(int kpt, int nchunks, int units, const uint8_t* ids, int64_t cap,
+                          int64_t S, int64_t E, const float* tab, const float* range,
+                          float* fscore, uint8_t* bins, int64_t Epad, uint32_t* chist,
+                          int chunk_stride, hipStream_t st, const EvPair& ev) {
+  return hipSuccess;
+}
+
+hipError_t launch_si_compact(int kpt, int nchunks, int units, const uint8_t* bins,
+                             const float* fscore, int64_t Epad, int64_t S, int64_t E,
+                             const int32_t* meta, const uint32_t* coff, int chunk_stride,
+                             int32_t* cand, float* est, int64_t cstride, uint32_t* mm,
+                             hipStream_t st, const EvPair& ev) {
+  return hipSuccess;
+}
+
+hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs,
+                             const int32_t* idx, int k, int batch, int n_kv_heads, float qscale,
+                             float* part, int nch, hipStream_t st, const EvPair& ev) {
+  return hipSuccess;
+}
+
+hipError_t launch_attn_merge(int dtype, const float* part, int nch, int rows, void* out,
+                             hipStream_t st,
+                         const EvPair& ev) {
+  return hipSuccess;
+}
+
+size_t si_build_ws_bytes(int BH, int64_t S, int64_t n) {
+  return (size_t)BH * (size_t)(n > S ? n - S : 1) * 32 + 4096;
+}
+void codebook_m8(float* L, float* tau) {
+  for (int i = 0; i < 8; ++i) L[i] = kLevels_m8[i];
+  for (int i = 0; i < 7; ++i) tau[i] = kThresh_m8[i];
+}
+void codebook_m4(float* L, float* tau) {
+  for (int i = 0; i < 8; ++i) L[i] = kLevels_m4[i];
+  for (int i = 0; i < 7; ++i) tau[i] = kThresh_m4[i];
+}
+
+}  // namespace pkv
