@@ -214,7 +214,7 @@ PARISKV_API int32_t pariskv_retrieve_topk(const pariskv_index *index,
  * s itself when that kernel starts and ends (hipExtLaunchKernel), so the
  * pair brackets exactly that kernel.  Stages: query prep, vote scan,
  * threshold, compact + rerank, top-k, top-k second pass.  Top-k is one
- * kernel for up to 4096 candidates per (batch, KV head); above that it is
+ * kernel for up to 16384 candidates per retrieval unit; above that it is
  * a histogram kernel (stage 4) and a select kernel (stage 5).  A stage that
  * a call does not run has its two events recorded back to back.
  * Not for use under stream capture. */

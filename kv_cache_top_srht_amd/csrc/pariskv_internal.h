@@ -104,8 +104,10 @@ hipError_t launch_si_compact(int kpt, int nchunks, int units, const uint8_t* bin
 // candidates per top-k block and the largest threshold bin ranked pairwise
 constexpr int kTopkSlice = 4096;
 constexpr int kTopkMaxMembers = 4096;
-// up to this many slices per (b, h), top-k runs as one kernel
-constexpr int kTopkFusedSlices = 1;
+// up to this many slices per (b, h), top-k runs as one kernel (every block
+// reads all of its (b, h)'s estimates: cheaper than a second kernel while
+// the slices are few)
+constexpr int kTopkFusedSlices = 4;
 // up to this many slices, the select kernel loads all histogram rows at once
 constexpr int kTopkFewSlices = 16;
 // split-K attention partial per (query head, chunk): o[128], m, l, 2 unused

@@ -2046,9 +2046,18 @@ hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cs
                        const EvPair& ev_hist, const EvPair& ev_select) {
   const dim3 grid(P, BH);
   if (P <= kTopkFusedSlices) {
-    // one slice: the whole top-k in one kernel
-    hipError_t e = launch(k_topk_fused<1>, grid, dim3(1024), st, ev_hist, est, cand, cstride, C,
-                          kprime, S, k, tkmeta, out_idx, out_est);
+    // few slices: the whole top-k in one kernel
+    static_assert(kTopkFusedSlices <= 4, "k_topk_fused instances");
+    hipError_t e;
+    if (P == 1)
+      e = launch(k_topk_fused<1>, grid, dim3(1024), st, ev_hist, est, cand, cstride, C, kprime, S,
+                 k, tkmeta, out_idx, out_est);
+    else if (P == 2)
+      e = launch(k_topk_fused<2>, grid, dim3(1024), st, ev_hist, est, cand, cstride, C, kprime, S,
+                 k, tkmeta, out_idx, out_est);
+    else
+      e = launch(k_topk_fused<4>, grid, dim3(1024), st, ev_hist, est, cand, cstride, C, kprime, S,
+                 k, tkmeta, out_idx, out_est);
     if (e != hipSuccess || !ev_select.start) return e;
     // the second stage does not run: its events are recorded back to back
     e = hipEventRecord(ev_select.start, st);

@@ -175,14 +175,19 @@ def test_ties_duplicates_and_zero_keys(orc, B):
 
 
 @pytest.mark.parametrize("N,den,k,copies", [
-    (60000, 5, 2048, 8000),     # 3 top-k slices, threshold bin of 8000 equal keys
+    (100000, 20, 1024, 0),      # 5000 candidates: 2 top-k slices, one kernel
+    (40000, 5, 1024, 5000),     # 2 slices, threshold bin of 5000 equal keys
+    (60000, 5, 2048, 8000),     # 3 slices, threshold bin of 8000 equal keys
+    (80000, 5, 2048, 0),        # 16000 candidates: 4 slices, the one-kernel limit
+    (90000, 5, 2048, 0),        # 18000 candidates: 5 slices, histogram + select
     (150000, 2, 4096, 0),       # 75000 candidates: 19 slices, generic select
     (150000, 2, 4096, 8000),    # 19 slices and the radix select of a tied bin
 ])
 def test_topk_paths(orc, N, den, k, copies):
-    """The top-k's other paths: more than 16 slices of 4096 candidates, and a
-    threshold bin holding more than 4096 members (identical keys tie exactly
-    on score and estimate; the lower positions win)."""
+    """The top-k's paths: one kernel up to 4 slices of 4096 candidates, the
+    histogram + select pair above that (more than 16 slices: the generic
+    select), and a threshold bin holding more than 4096 members (identical
+    keys tie exactly on score and estimate; the lower positions win)."""
     w = W("topk paths", 1, 1, 4, 128, N, "bf16", cand_num=1, cand_den=den, k=k,
           seed=33)
     case("top-k paths N=%d f=1/%d k=%d copies=%d" % (N, den, k, copies))
