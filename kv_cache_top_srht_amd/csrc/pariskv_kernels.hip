@@ -206,11 +206,6 @@ __device__ __forceinline__ uint64_t dpp64(uint64_t v) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
   return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
 __device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 // Maximum over each row of 16 lanes, received by every lane of the row: DPP
@@ -223,13 +218,17 @@ __device__ __forceinline__ uint64_t row_max64(uint64_t k) {
   return k;
 }
 
-// Maximum over the 64 lanes, received by every lane: the row maximum, then
-// lane ^ 16 and lane ^ 32 across rows.
+// lane l's value, wave-uniform
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Maximum over the 64 lanes, received by every lane: the row maxima, then
+// the four rows' values read into scalar registers (lanes 0, 16, 32, 48).
 __device__ __forceinline__ uint64_t wave_max64(uint64_t k) {
   k = row_max64(k);
-  k = max64(k, shfl_xor64(k, 16));
-  k = max64(k, shfl_xor64(k, 32));
-  return k;
+  return max64(max64(readlane64(k, 0), readlane64(k, 16)), max64(readlane64(k, 32), readlane64(k, 48)));
 }
 
 template <typename T, int G, int M>
@@ -237,23 +236,25 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
                                                 float invG, SignMask sg, float c, int rho, Tiers tw,
                                                 uint8_t* __restrict__ lut_out, float* __restrict__ yq_out,
                                                 float* __restrict__ ptab_out, AppendJob app,
-                                                int unit_div) {
+                                                int unit_div, int n_units) {
   // one block per retrieval unit: a (b, KV head), or a (b, query head) with
   // unit_div = G units per KV head (then G = 1 here and n_kv_heads counts
-  // units per batch entry)
+  // units per batch entry); blocks n_units.. encode appended keys
   const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (bh >= n_units) {
+    // blocks past the units encode the keys appended since the last
+    // retrieval (16 lanes per (KV head, key)), so the vote scan sees them
+    const int pair = (bh - n_units) * 64 + (tid >> 4);
+    const int kvh = pair / app.n, r = pair - kvh * app.n;
+    if (kvh < n_units / unit_div)
+      encode_key<T, M>((const T*)app.K, app.rows_per_head, kvh, r, app.lo + r, app.cap, app.ids,
+                       app.rec, sg, c, tid & 15);
+    return;
+  }
   const int b = bh / n_kv_heads, h = bh - b * n_kv_heads;
   const int Hq = n_kv_heads * G;
-  const int tid = threadIdx.x;
   __shared__ float s_yq[128];
-  // keys appended since the last retrieval are encoded here (threads 256+,
-  // 16 per key), so the vote scan that follows sees them
-  if (app.n > 0 && tid >= 256 && bh % unit_div == 0) {
-    const int r = (tid - 256) >> 4;
-    if (r < app.n)
-      encode_key<T, M>((const T*)app.K, app.rows_per_head, bh / unit_div, r, app.lo + r,
-                       app.cap, app.ids, app.rec, sg, c, tid & 15);
-  }
   if (tid < 16) {
     const int sub = tid;
     // all G query rows are loaded at once, then summed in head order
@@ -1914,9 +1915,11 @@ static hipError_t launch_qprep_m(int dtype, const void* Q, int BH, int n_kv_head
                                  uint8_t* lut, float* yq, float* ptab, const AppendJob& app,
                                  int unit_div, hipStream_t st, const EvPair& ev) {
   const float invG = 1.0f / (float)G;
+  // encode blocks: 64 (KV head, key) pairs each
+  const int nenc = app.n > 0 ? (int)(((int64_t)(BH / unit_div) * app.n + 63) / 64) : 0;
 #define PKV_QP(T, GG)                                                                           \
-  return launch(k_qprep<T, GG, M>, dim3(BH), dim3(1024), st, ev, (const T*)Q, n_kv_heads, invG, \
-                sg, c, rho, tw, lut, yq, ptab, app, unit_div)
+  return launch(k_qprep<T, GG, M>, dim3(BH + nenc), dim3(1024), st, ev, (const T*)Q, n_kv_heads, \
+                invG, sg, c, rho, tw, lut, yq, ptab, app, unit_div, BH)
   if (dtype == 0) {
     switch (G) {
       case 1: PKV_QP(uint16_t, 1);
