@@ -225,6 +225,32 @@ PARISKV_API int32_t pariskv_retrieve_topk_profiled(
 /* Name of retrieval stage s, or NULL. */
 PARISKV_API const char *pariskv_stage_name(int32_t stage);
 
+/* How pariskv_retrieve_topk runs on an index.
+ *   PARISKV_PATH_AUTO (the default): one kernel for small indexes -- units
+ *     of one (b, KV head) (shared retrieval), at most
+ *     PARISKV_SMALL_MAX_KEYS eligible keys and at most 16,384 candidates per
+ *     unit -- else the multi-kernel pipeline.
+ *   PARISKV_PATH_PIPELINE: always the multi-kernel pipeline.
+ *   PARISKV_PATH_SINGLE: always one kernel, one 1024-thread block per unit
+ *     running every stage; a retrieval it cannot serve (per-query-head
+ *     units, more than 16,384 candidates per unit) returns UNSUPPORTED.
+ * The two paths return the same bits and leave the same intermediates in
+ * the workspace.  Errors: INVALID_ARG. */
+#define PARISKV_PATH_AUTO 0
+#define PARISKV_PATH_PIPELINE 1
+#define PARISKV_PATH_SINGLE 2
+#define PARISKV_SMALL_MAX_KEYS 16384
+PARISKV_API int32_t pariskv_set_retrieval_path(pariskv_index *index,
+                                               int32_t path);
+
+/* The path (PARISKV_PATH_PIPELINE or PARISKV_PATH_SINGLE) a retrieval of
+ * k keys would take on the index now, or a negative status
+ * (INVALID_ARG, UNSUPPORTED).  With PARISKV_PATH_SINGLE the profiled call
+ * stamps the single kernel as stage 1 (vote scan) and records every other
+ * stage's events back to back. */
+PARISKV_API int32_t pariskv_retrieval_path(const pariskv_index *index,
+                                           int32_t k);
+
 /* ---------------------------------------------------------------------- */
 /* Sparse attention.                                                       */
 /* [TS] Problem Statement (attend to a Top-k subset of past tokens) and    */

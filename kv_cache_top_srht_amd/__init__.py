@@ -22,6 +22,9 @@ PARISKV_DTYPE_FP32 = 1
 PARISKV_RETRIEVE_STAGES = 6
 
 DEBUG_LUT, DEBUG_YQ, DEBUG_SCORES, DEBUG_CAND, DEBUG_EST, DEBUG_THRESH = range(6)
+# retrieval paths (pariskv_set_retrieval_path) and the default single-kernel limit
+PATH_AUTO, PATH_PIPELINE, PATH_SINGLE = 0, 1, 2
+SMALL_MAX_KEYS = 16384
 
 
 class PariskvError(RuntimeError):
@@ -94,6 +97,8 @@ def lib():
             "pariskv_debug_export": (i32, [P, i64, i64, P, P, P]),
             "pariskv_debug_intermediate": (i32, [P, i32, P, sz, i32, P, sz]),
             "pariskv_retrieve_sizes": (i32, [P, i32, C.POINTER(i64), C.POINTER(i64)]),
+            "pariskv_set_retrieval_path": (i32, [P, i32]),
+            "pariskv_retrieval_path": (i32, [P, i32]),
             "pariskv_codebook": (i32, [i32, P, P]),
             "pariskv_rot_scale": (C.c_float, [i32]),
             "pariskv_status_string": (C.c_char_p, [i32]),
@@ -348,6 +353,17 @@ def pariskv_debug_export(handle, lo, hi, BH, B=16, d=128):
     return ids, nib, w
 
 
+def pariskv_set_retrieval_path(handle, path):
+    _check(lib().pariskv_set_retrieval_path(handle, int(path)))
+
+
+def pariskv_retrieval_path(handle, k):
+    r = lib().pariskv_retrieval_path(handle, int(k))
+    if r < 0:
+        _check(r)
+    return r
+
+
 def pariskv_retrieve_sizes(handle, k):
     E, Cn = C.c_int64(), C.c_int64()
     _check(lib().pariskv_retrieve_sizes(handle, int(k), C.byref(E), C.byref(Cn)))
@@ -417,6 +433,13 @@ class Layer:
         pariskv_append_keys(self.handle, K_new,
                             rows_per_head if rows_per_head is not None
                             else K_new.shape[2], n_new, stream)
+
+    def set_path(self, path):
+        pariskv_set_retrieval_path(self.handle, path)
+
+    @property
+    def path(self) -> int:
+        return pariskv_retrieval_path(self.handle, self.k)
 
     def retrieve(self, Q, out_idx, out_est=None, stream=None):
         pariskv_retrieve_topk(self.handle, Q, self.k, out_idx, out_est, self.ws,

@@ -22,6 +22,7 @@ struct pariskv_index {
   hipStream_t last;
   pkv::AppendJob pending;       // appended rows the next retrieval encodes
   hipStream_t pending_stream;
+  int32_t path;                 // PARISKV_PATH_*
 };
 
 // Four-region window over one index (sinks, retrieval, local, update buffer).
@@ -177,6 +178,17 @@ int32_t flush_pending(pariskv_index* ix) {
                                        ix->pending_stream, pkv::EvPair{}));
 }
 
+// The retrieval path for E eligible keys and C candidates per unit: the
+// single kernel serves shared retrieval with at most kSmallTopkSlices top-k
+// slices; by default only small indexes take it.
+int32_t choose_path(const pariskv_index* ix, int64_t E, int64_t C) {
+  const bool fits = !ix->cfg.per_query_head &&
+                    C <= (int64_t)pkv::kSmallTopkSlices * pkv::kTopkSlice;
+  if (ix->path == PARISKV_PATH_PIPELINE) return PARISKV_PATH_PIPELINE;
+  if (ix->path == PARISKV_PATH_SINGLE) return fits ? PARISKV_PATH_SINGLE : PARISKV_ERR_UNSUPPORTED;
+  return fits && E <= PARISKV_SMALL_MAX_KEYS ? PARISKV_PATH_SINGLE : PARISKV_PATH_PIPELINE;
+}
+
 int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t* out_idx,
                       float* out_est, void* ws, size_t ws_bytes, void* stream, void** events) {
   if (!ix || !Q || !out_idx || !ws) return PARISKV_ERR_INVALID_ARG;
@@ -186,6 +198,12 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return PARISKV_ERR_INVALID_ARG;
   const WsLayout L = ws_layout(c, k);
   if (ws_bytes < L.total) return PARISKV_ERR_WORKSPACE;
+  // every refusal comes before the deferred appends are taken over below
+  const int64_t E = N - S, kp = k - S;
+  const int64_t C = cand_count(E, kp, c->cand_num, c->cand_den);
+  if (C > 1024ll * pkv::kTopkSlice) return PARISKV_ERR_UNSUPPORTED;  // > 4M candidates per head
+  const int32_t path = choose_path(ix, E, C);
+  if (path < 0) return path;
   hipStream_t st = (hipStream_t)stream;
   pariskv_index* mix = const_cast<pariskv_index*>(ix);
   mix->last = st;
@@ -205,9 +223,6 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   // a unit's query: the mean of its G query heads, or its own head when unshared
   const int G = c->per_query_head ? 1 : c->n_q_heads / c->n_kv_heads;
   const int units_per_batch = c->per_query_head ? c->n_q_heads : c->n_kv_heads;
-  const int64_t E = N - S, kp = k - S;
-  const int64_t C = cand_count(E, kp, c->cand_num, c->cand_den);
-  if (C > 1024ll * pkv::kTopkSlice) return PARISKV_ERR_UNSUPPORTED;  // > 4M candidates per head
   const int kpt = pick_kpt(E, BH);
   const int P = (int)ceil_div(C, pkv::kTopkSlice);
   const int nch = (int)ceil_div(E, 256 * kpt);
@@ -240,6 +255,19 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   };
   (void)hipGetLastError();  // launches below report only their own errors
   hipError_t e;
+  if (path == PARISKV_PATH_SINGLE) {
+    // one kernel, stamped as stage 1; the other stages' events back to back
+    for (int s = 0; s < PARISKV_RETRIEVE_STAGES; ++s) {
+      if (s == 1) continue;
+      const pkv::EvPair p = ev(s);
+      if (p.start && (e = hipEventRecord(p.start, st)) != hipSuccess) return hip_status(e);
+      if (p.stop && (e = hipEventRecord(p.stop, st)) != hipSuccess) return hip_status(e);
+    }
+    return hip_status(pkv::launch_retrieve_small(
+        m_of(c), c->key_dtype, Q, BH, units_per_batch, G, ix->signs, ix->rot_c, c->rho, tw, app,
+        ix->ids, ix->rec, c->capacity, S, E, C, (int)kp, k, L.nbins, lut, yq, scores, L.Epad,
+        meta, cand, est, L.cstride, out_idx, out_est, st, ev(1)));
+  }
   e = pkv::launch_qprep(m_of(c), c->key_dtype, Q, BH, units_per_batch, G, ix->signs, ix->rot_c,
                         c->rho, tw, lut, yq, ptab, app, udiv, st, ev(0));
   if (e != hipSuccess) return hip_status(e);
@@ -382,6 +410,7 @@ int32_t pariskv_build_index(const pariskv_config* cfg, const int8_t* srht_signs,
   ix->last = (hipStream_t)stream;
   ix->pending = pkv::AppendJob{};
   ix->pending_stream = nullptr;
+  ix->path = PARISKV_PATH_AUTO;
   const int BH = cfg->batch * cfg->n_kv_heads;
   (void)hipGetLastError();
   hipError_t e = pkv::launch_encode(m_of(cfg), cfg->key_dtype, K, k_rows_per_head, 0, n_keys, BH,
@@ -558,6 +587,21 @@ int32_t pariskv_retrieve_sizes(const pariskv_index* ix, int32_t k, int64_t* E, i
   *E = ix->n - S;
   *C = cand_count(*E, k - S, ix->cfg.cand_num, ix->cfg.cand_den);
   return PARISKV_OK;
+}
+
+int32_t pariskv_set_retrieval_path(pariskv_index* ix, int32_t path) {
+  if (!ix || (path != PARISKV_PATH_AUTO && path != PARISKV_PATH_PIPELINE &&
+              path != PARISKV_PATH_SINGLE))
+    return PARISKV_ERR_INVALID_ARG;
+  ix->path = path;
+  return PARISKV_OK;
+}
+
+int32_t pariskv_retrieval_path(const pariskv_index* ix, int32_t k) {
+  int64_t E = 0, C = 0;
+  const int32_t rc = pariskv_retrieve_sizes(ix, k, &E, &C);
+  if (rc) return rc;
+  return choose_path(ix, E, C);
 }
 
 int32_t pariskv_debug_intermediate(const pariskv_index* ix, int32_t k, const void* ws,

@@ -72,6 +72,16 @@ hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cs
                        const EvPair& ev_hist, const EvPair& ev_select);
 // top-k with per-unit candidate counts read from cmeta[unit * 4 + 3] on the
 // device (at most Cmax); hist + general select, grid_slices blocks per unit
+// The whole retrieval of every unit in one kernel (shared retrieval, E >= 1,
+// 1 <= k' <= C <= kSmallTopkSlices * kTopkSlice, at most 64 appended keys).
+hipError_t launch_retrieve_small(int m, int dtype, const void* Q, int BH, int n_kv_heads, int G,
+                                 const SignMask& sg, float c, int rho, const Tiers& tw,
+                                 const AppendJob& app, const uint8_t* ids, const uint32_t* rec,
+                                 int64_t cap, int64_t S, int64_t E, int64_t C, int kprime, int k,
+                                 int nbins, uint8_t* lut, float* yq, uint8_t* scores, int64_t Epad,
+                                 int32_t* meta, int32_t* cand, float* est, int64_t cstride,
+                                 int32_t* out_idx, float* out_est, hipStream_t st,
+                                 const EvPair& ev);
 hipError_t launch_topk_counted(int BH, const float* est, const int32_t* cand, int64_t cstride,
                                const int32_t* cmeta, int Cmax, int grid_slices, int kprime,
                                int S, int k,
@@ -108,6 +118,8 @@ constexpr int kTopkMaxMembers = 4096;
 // reads all of its (b, h)'s estimates: cheaper than a second kernel while
 // the slices are few)
 constexpr int kTopkFusedSlices = 4;
+// the single-kernel retrieval holds up to this many slices of candidates
+constexpr int kSmallTopkSlices = 4;
 // up to this many slices, the select kernel loads all histogram rows at once
 constexpr int kTopkFewSlices = 16;
 // split-K attention partial per (query head, chunk): o[128], m, l, 2 unused

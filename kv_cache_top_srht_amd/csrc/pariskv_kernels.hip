@@ -231,6 +231,86 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t k) {
   return max64(max64(readlane64(k, 0), readlane64(k, 16)), max64(readlane64(k, 32), readlane64(k, 48)));
 }
 
+// Word l (entries 4 l .. 4 l + 3) of row s of the vote table, computed by
+// lane l of one wave from the rotated query yq (LDS).  M = 8: row s is
+// subspace s, its 256 centroids scored 4 per lane, the rho best by wave
+// maxima of 64-bit (score, centroid) keys get the tier weights.  M = 4: row s
+// is the byte table of subspaces 2 s and 2 s + 1, each a row of 16 lanes
+// taking its rho best of 16 centroids by row maxima.
+template <int M>
+__device__ __forceinline__ uint32_t vote_table_word(const float* s_yq, int s, int l, int rho,
+                                                    const Tiers& tw) {
+  if constexpr (M == 4) {
+    // lane l scores centroid p = l & 15 of subspace 2 s + ((l >> 4) & 1)
+    // (rows 2 and 3 repeat rows 0 and 1)
+    const int half = (l >> 4) & 1, p = l & 15;
+    float z4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z4[j] = s_yq[s * 8 + half * 4 + j];
+    float acc = (p & 1) ? -z4[0] : z4[0];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) acc = acc + (((p >> j) & 1) ? -z4[j] : z4[j]);
+    uint64_t key = centroid_key(acc, p);
+    // rho rounds: the row's best remaining centroid gets tier weight r and
+    // drops out (key 0 is below every centroid)
+    uint32_t wt = 0;
+    for (int r = 0; r < rho; ++r) {
+      const uint64_t W = row_max64(key);
+      if (key == W) {
+        wt = (uint32_t)tw.w[r];
+        key = 0;
+      }
+    }
+    // entries v = 4 l .. 4 l + 3: low nibble's weight from row 0, high
+    // nibble's (v >> 4 = l >> 2) from row 1
+    const uint32_t whi = (uint32_t)__shfl((int)wt, 16 + (l >> 2));
+    uint32_t word = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t wlo = (uint32_t)__shfl((int)wt, (4 * l + q) & 15);
+      word |= (wlo + whi) << (8 * q);
+    }
+    return word;
+  }
+  float z[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) z[j] = s_yq[s * 8 + j];
+  uint64_t key[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int p = l * 4 + q;
+    float acc = (p & 1) ? -z[0] : z[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) acc = acc + (((p >> j) & 1) ? -z[j] : z[j]);
+    key[q] = centroid_key(acc, p);
+  }
+  // the lane's 4 in descending key order
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int j = 0; j < 3 - i; ++j)
+      if (key[j + 1] > key[j]) { const uint64_t t = key[j]; key[j] = key[j + 1]; key[j + 1] = t; }
+  // rho rounds: the wave's best remaining centroid gets tier weight r; its
+  // owner lane drops it (an exhausted lane offers key 0, below every centroid)
+  uint32_t lv[4] = {0, 0, 0, 0};
+  for (int r = 0; r < rho; ++r) {
+    const uint64_t W = wave_max64(key[0]);
+    const int wp = 255 - (int)(uint32_t)(W & 0xFFu);
+    if ((wp >> 2) == l) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if ((wp & 3) == q) lv[q] = (uint32_t)tw.w[r];
+    }
+    if (key[0] == W) {
+      key[0] = key[1];
+      key[1] = key[2];
+      key[2] = key[3];
+      key[3] = 0;
+    }
+  }
+  return lv[0] | (lv[1] << 8) | (lv[2] << 16) | (lv[3] << 24);
+}
+
 template <typename T, int G, int M>
 __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_kv_heads,
                                                 float invG, SignMask sg, float c, int rho, Tiers tw,
@@ -287,77 +367,8 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
     ptab_out[(int64_t)bh * 2048 + e] = (e & 8) ? -pr : pr;
   }
   const int s = tid >> 6, l = tid & 63;
-  uint32_t* lut_row = reinterpret_cast<uint32_t*>(lut_out + ((int64_t)bh * 16 + s) * 256);
-  if constexpr (M == 4) {
-    // lane l scores centroid p = l & 15 of subspace 2 s + ((l >> 4) & 1)
-    // (rows 2 and 3 repeat rows 0 and 1)
-    const int half = (l >> 4) & 1, p = l & 15;
-    float z4[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) z4[j] = s_yq[s * 8 + half * 4 + j];
-    float acc = (p & 1) ? -z4[0] : z4[0];
-#pragma unroll
-    for (int j = 1; j < 4; ++j) acc = acc + (((p >> j) & 1) ? -z4[j] : z4[j]);
-    uint64_t key = centroid_key(acc, p);
-    // rho rounds: the row's best remaining centroid gets tier weight r and
-    // drops out (key 0 is below every centroid)
-    uint32_t wt = 0;
-    for (int r = 0; r < rho; ++r) {
-      const uint64_t W = row_max64(key);
-      if (key == W) {
-        wt = (uint32_t)tw.w[r];
-        key = 0;
-      }
-    }
-    // entries v = 4 l .. 4 l + 3: low nibble's weight from row 0, high
-    // nibble's (v >> 4 = l >> 2) from row 1
-    const uint32_t whi = (uint32_t)__shfl((int)wt, 16 + (l >> 2));
-    uint32_t word = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t wlo = (uint32_t)__shfl((int)wt, (4 * l + q) & 15);
-      word |= (wlo + whi) << (8 * q);
-    }
-    lut_row[l] = word;
-    return;
-  }
-  float z[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) z[j] = s_yq[s * 8 + j];
-  uint64_t key[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int p = l * 4 + q;
-    float acc = (p & 1) ? -z[0] : z[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) acc = acc + (((p >> j) & 1) ? -z[j] : z[j]);
-    key[q] = centroid_key(acc, p);
-  }
-  // the lane's 4 in descending key order
-#pragma unroll
-  for (int i = 0; i < 3; ++i)
-#pragma unroll
-    for (int j = 0; j < 3 - i; ++j)
-      if (key[j + 1] > key[j]) { const uint64_t t = key[j]; key[j] = key[j + 1]; key[j + 1] = t; }
-  // rho rounds: the wave's best remaining centroid gets tier weight r; its
-  // owner lane drops it (an exhausted lane offers key 0, below every centroid)
-  uint32_t lv[4] = {0, 0, 0, 0};
-  for (int r = 0; r < rho; ++r) {
-    const uint64_t W = wave_max64(key[0]);
-    const int wp = 255 - (int)(uint32_t)(W & 0xFFu);
-    if ((wp >> 2) == l) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if ((wp & 3) == q) lv[q] = (uint32_t)tw.w[r];
-    }
-    if (key[0] == W) {
-      key[0] = key[1];
-      key[1] = key[2];
-      key[2] = key[3];
-      key[3] = 0;
-    }
-  }
-  lut_row[l] = lv[0] | (lv[1] << 8) | (lv[2] << 16) | (lv[3] << 24);
+  reinterpret_cast<uint32_t*>(lut_out + ((int64_t)bh * 16 + s) * 256)[l] =
+      vote_table_word<M>(s_yq, s, l, rho, tw);
 }
 
 // ---------------------------------------------------------------------------
@@ -742,6 +753,48 @@ __device__ __forceinline__ float quad_lane(float v) {
 constexpr int kPtabRow = 132;
 constexpr int kPtabLds = 16 * kPtabRow;
 
+// RSQ-IP estimate of one candidate by a group of 4 lanes (DPP quads): lane q
+// holds the codes of coordinates 32 q .. 32 q + 31 (cw) and the fp16 w of
+// their NB = 32 / M subspaces (ww), forms w_b p_b for them from the signed
+// product table in LDS, and every lane of the group returns the sum of all
+// B terms in b order.
+template <int M>
+__device__ __forceinline__ float rerank_estimate(
+    const uint4 cw, const typename std::conditional<M == 8, uint2, uint4>::type ww,
+    const float* s_P, int q) {
+  constexpr int NB = 32 / M;
+  const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+  uint32_t wsw[NB / 2];
+  wsw[0] = ww.x;
+  wsw[1] = ww.y;
+  if constexpr (M == 4) {
+    wsw[2] = ww.z;
+    wsw[3] = ww.w;
+  }
+  float t[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    // subspace 4 q NB / 4 + i: coordinates from nibble j0 of code dword bb
+    const int bb = (i * M) >> 3, j0 = (i * M) & 7;
+    const float* pb = s_P + (4 * q + bb) * kPtabRow;
+    float p = 0.0f;
+#pragma unroll
+    for (int jj = j0; jj < j0 + M; ++jj) p = p + pb[jj * 16 + ((cws[bb] >> (4 * jj)) & 15u)];
+    const uint16_t hb = (uint16_t)(wsw[i >> 1] >> ((i & 1) * 16));
+    t[i] = (float)__builtin_bit_cast(_Float16, hb) * p;
+  }
+  float e = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) e = e + quad_lane<0>(t[i]);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) e = e + quad_lane<1>(t[i]);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) e = e + quad_lane<2>(t[i]);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) e = e + quad_lane<3>(t[i]);
+  return e;
+}
+
 // FT (at most kFusedThreshChunks chunks per unit): no separate threshold
 // kernel.  Every block finds T and the tie quota from the column sums of the
 // unit's chunk rows, and its chunks' offsets from block scans over the rows
@@ -948,35 +1001,7 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
     for (int r = 0; r < 4; ++r) {
       if (j0 + r * 64 >= ntot) break;  // uniform across the block
       const uint32_t j = j0 + r * 64 + (tid >> 2);
-      const uint32_t cws[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
-      uint32_t wsw[NB / 2];
-      wsw[0] = ww[r].x;
-      wsw[1] = ww[r].y;
-      if constexpr (M == 4) {
-        wsw[2] = ww[r].z;
-        wsw[3] = ww[r].w;
-      }
-      float t[NB];
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        // subspace 4 q NB / 4 + i: coordinates from nibble j0 of code dword bb
-        const int bb = (i * M) >> 3, j0 = (i * M) & 7;
-        const float* pb = s_P + (4 * q + bb) * kPtabRow;
-        float p = 0.0f;
-#pragma unroll
-        for (int jj = j0; jj < j0 + M; ++jj) p = p + pb[jj * 16 + ((cws[bb] >> (4 * jj)) & 15u)];
-        const uint16_t hb = (uint16_t)(wsw[i >> 1] >> ((i & 1) * 16));
-        t[i] = (float)__builtin_bit_cast(_Float16, hb) * p;
-      }
-      float e = 0.0f;
-#pragma unroll
-      for (int i = 0; i < NB; ++i) e = e + quad_lane<0>(t[i]);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) e = e + quad_lane<1>(t[i]);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) e = e + quad_lane<2>(t[i]);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) e = e + quad_lane<3>(t[i]);
+      const float e = rerank_estimate<M>(cw[r], ww[r], s_P, q);
       if (j < ntot) {
         if (q == 0) {
           const uint32_t o = (j >= nsel0) ? off_c[1] + (j - nsel0) : off_c[0] + j;
@@ -1681,6 +1706,355 @@ __global__ __launch_bounds__(1024) void k_topk_fused(
 }
 
 // ---------------------------------------------------------------------------
+// Small-N retrieval in one kernel ([TS] Two-Stage GPU-Native Retrieval
+// Pipeline, every stage): one 1024-thread block per retrieval unit (a (b, KV
+// head); shared retrieval) encodes the keys appended since the last
+// retrieval, prepares the query, scans the ids, finds the threshold, lists
+// the candidates in index order, reranks them and selects the exact top-k,
+// with block barriers between the stages instead of kernel boundaries.  Each
+// stage is the fp32 operation sequence of its multi-kernel counterpart, and
+// the workspace receives the same vote table, yq, scores, threshold meta,
+// candidates and estimates.  For at most kSmallTopkSlices * 4096 candidates
+// (the top-k holds every estimate in registers); worth it while one CU per
+// unit streams the ids faster than the six kernel boundaries it saves.
+// ---------------------------------------------------------------------------
+template <typename T, int M>
+__global__ __launch_bounds__(1024) void k_retrieve_small(
+    const T* __restrict__ Q, int n_kv_heads, int G, float invG, SignMask sg, float c, int rho,
+    Tiers tw, AppendJob app, const uint4* __restrict__ ids, const uint32_t* __restrict__ rec,
+    int64_t cap, int64_t S, int64_t E, int64_t C, int kprime, int k, int nbins,
+    uint8_t* __restrict__ lut_out, float* __restrict__ yq_out, uint8_t* __restrict__ scores,
+    int64_t Epad, int32_t* __restrict__ meta, int32_t* __restrict__ cand, float* __restrict__ est,
+    int64_t cstride, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
+  constexpr int MAXS = kSmallTopkSlices;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = bh / n_kv_heads, h = bh - b * n_kv_heads, Hq = n_kv_heads * G;
+  __shared__ float s_yq[128];
+  __shared__ uint8_t s_lut[16 * 256];
+  __shared__ float s_P[kPtabLds];
+  __shared__ uint32_t s_wh[16][256];  // per-wave score histograms, then the top-k bins
+  __shared__ uint32_t s_ge[257];
+  __shared__ uint2 s_w[16];
+  __shared__ uint32_t s_sel[4];
+  __shared__ uint32_t s_r[32];
+  __shared__ uint64_t s_mem[TK_MAXMEM];
+  __shared__ uint32_t s_bits[MAXS * TK_SL / 32];
+
+  // (1) appended keys: 16 lanes per key into the index, before the scan reads
+  // them (the barriers below order this block's stores before its loads)
+  if ((tid >> 4) < app.n)
+    encode_key<T, M>((const T*)app.K, app.rows_per_head, bh, tid >> 4, app.lo + (tid >> 4),
+                     app.cap, app.ids, app.rec, sg, c, tid & 15);
+  // (2) query: mean of the G query rows (summed in head order), SRHT
+  if (tid < 16) {
+    const int sub = tid;
+    const T* q0 = Q + ((int64_t)(b * Hq + h * G) << 7) + sub * 8;
+    float x[8];
+    load8(q0, x);
+    for (int g = 1; g < G; ++g) {
+      float xg[8];
+      load8(q0 + ((int64_t)g << 7), xg);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = x[j] + xg[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = x[j] * invG;
+    srht16(x, sign_byte_of(sg, sub), sub, c);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_yq[sub * 8 + j] = x[j];
+    reinterpret_cast<float4*>(yq_out + (int64_t)bh * 128 + sub * 8)[0] =
+        make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4*>(yq_out + (int64_t)bh * 128 + sub * 8)[1] =
+        make_float4(x[4], x[5], x[6], x[7]);
+  }
+  for (int i = tid; i < 16 * 256; i += 1024) (&s_wh[0][0])[i] = 0u;
+  __threadfence_block();
+  __syncthreads();
+  // signed product table (rows of kPtabRow floats) and the vote table, row
+  // s = wave s
+  for (int e = tid; e < 2048; e += 1024) {
+    const float pr = cb_level<M>(e & 7) * s_yq[e >> 4];
+    s_P[(e >> 7) * kPtabRow + (e & 127)] = (e & 8) ? -pr : pr;
+  }
+  {
+    const uint32_t word = vote_table_word<M>(s_yq, wv, lane, rho, tw);
+    reinterpret_cast<uint32_t*>(s_lut)[wv * 64 + lane] = word;
+    reinterpret_cast<uint32_t*>(lut_out + (int64_t)bh * 4096)[wv * 64 + lane] = word;
+  }
+  __syncthreads();
+
+  // (3) vote scan over the eligible keys [S, S + E): score bytes out, zeros by
+  // wave ballot, other scores by per-wave LDS atomics
+  const uint4* src = ids + (int64_t)bh * cap + S;
+  uint8_t* dst = scores + (int64_t)bh * Epad;
+  {
+    constexpr int U = 8;  // keys per thread in flight
+    uint32_t zeros = 0;
+    for (int64_t base = 0; base < E; base += 1024 * U) {
+      uint4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t p = base + u * 1024 + tid;
+        x[u] = src[p < E ? p : E - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t p = base + u * 1024 + tid;
+        const bool valid = p < E;
+        const uint32_t w4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+        uint32_t sc = 0;
+#pragma unroll
+        for (int bb = 0; bb < 16; ++bb)
+          sc += s_lut[bb * 256 + ((w4[bb >> 2] >> ((bb & 3) * 8)) & 0xFFu)];
+        zeros += (uint32_t)__popcll(__ballot(valid && sc == 0));
+        if (valid) {
+          dst[p] = (uint8_t)sc;
+          if (sc != 0) atomicAdd(&s_wh[wv][sc], 1u);
+        }
+      }
+    }
+    if (lane == 0) s_wh[wv][0] = zeros;
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // (4) threshold: Tv = the largest v with #(score >= v) >= C, ties quota
+  // Qt = C - #(score > Tv)
+  if (tid < 256) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) a += s_wh[w][tid];
+    s_ge[tid] = a;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    uint32_t hc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) hc[r] = s_ge[4 * lane + r];
+    const uint32_t loc = hc[0] + hc[1] + hc[2] + hc[3];
+    uint32_t inc = loc;  // sum over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t t = __shfl_down(inc, off);
+      if (lane + off < 64) inc += t;
+    }
+    const uint32_t g3 = inc - loc + hc[3], g2 = g3 + hc[2], g1 = g2 + hc[1], g0 = g1 + hc[0];
+    s_ge[4 * lane + 0] = g0;
+    s_ge[4 * lane + 1] = g1;
+    s_ge[4 * lane + 2] = g2;
+    s_ge[4 * lane + 3] = g3;
+    if (lane == 0) s_ge[256] = 0u;
+  }
+  __syncthreads();
+  if (tid < 256 && (int64_t)s_ge[tid] >= C && (int64_t)s_ge[tid + 1] < C) s_sel[0] = (uint32_t)tid;
+  __syncthreads();
+  const int Tv = (int)s_sel[0];
+  const int64_t n_gt = s_ge[Tv + 1];
+  const int64_t Qt = C - n_gt;
+  if (tid == 0) {
+    meta[bh * 4 + 0] = Tv;
+    meta[bh * 4 + 1] = (int32_t)n_gt;
+    meta[bh * 4 + 2] = (int32_t)Qt;
+    meta[bh * 4 + 3] = (int32_t)C;
+  }
+
+  // (5) candidates in index order: tiles of 8192 keys, 8 per thread; every
+  // key with score > Tv and the first Qt keys with score == Tv
+  int32_t* cb = cand + (int64_t)bh * cstride;
+  {
+    const bool swar = nbins <= 128;
+    int64_t eq_seen = 0, out_base = 0;  // uniform across the block
+    for (int64_t base = 0; base < E; base += 8192) {
+      const int64_t p0 = base + (int64_t)tid * 8;
+      const int64_t rem = E - p0;
+      const int nval = rem <= 0 ? 0 : (rem >= 8 ? 8 : (int)rem);
+      const uint2 raw = nval > 0 ? *reinterpret_cast<const uint2*>(dst + p0) : make_uint2(0u, 0u);
+      uint8_t sc[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sc[t] = (uint8_t)(((t < 4) ? raw.x : raw.y) >> ((t & 3) * 8));
+      uint32_t gtm, eqm;
+      score_masks<8>(sc, raw, Tv, nval, swar, gtm, eqm);
+      uint2 tot;
+      const uint2 ex = block_exscan2<1024>(
+          make_uint2((uint32_t)__popc(gtm), (uint32_t)__popc(eqm)), s_w, tot);
+      const int64_t qleft = Qt - eq_seen;  // ties still to keep at the tile start
+      const int64_t mine = qleft - (int64_t)ex.y;
+      const uint32_t r = mine <= 0 ? 0u : (uint32_t)(mine < 32 ? mine : 32);
+      uint32_t sel = gtm | lowest_bits(eqm, r);
+      const int64_t keep_before = (int64_t)ex.y < qleft ? (int64_t)ex.y : (qleft > 0 ? qleft : 0);
+      int64_t o = out_base + ex.x + keep_before;
+      while (sel) {
+        const int t = __builtin_ctz(sel);
+        if (o < C) cb[o] = (int32_t)(S + p0 + t);
+        ++o;
+        sel &= sel - 1u;
+      }
+      out_base += (int64_t)tot.x + ((int64_t)tot.y < qleft ? (int64_t)tot.y : (qleft > 0 ? qleft : 0));
+      eq_seen += tot.y;
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // (6) RSQ-IP estimates, 4 lanes per candidate, 4 candidates per lane group
+  // fetched before any is used
+  float* eb = est + (int64_t)bh * cstride;
+  {
+    using WT = typename std::conditional<M == 8, uint2, uint4>::type;
+    const int q = tid & 3;
+    const uint32_t* rq = rec + (int64_t)bh * cap * 32;
+    for (int64_t j0 = 0; j0 < C; j0 += 1024) {
+      int32_t pi[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t j = j0 + r * 256 + (tid >> 2);
+        pi[r] = cb[j < C ? j : C - 1];
+      }
+      uint4 cw[4];
+      WT ww[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t* rp = rq + (int64_t)pi[r] * 32;
+        cw[r] = reinterpret_cast<const uint4*>(rp)[q];
+        ww[r] = reinterpret_cast<const WT*>(rp + 16)[q];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t j = j0 + r * 256 + (tid >> 2);
+        const float e = rerank_estimate<M>(cw[r], ww[r], s_P, q);
+        if (j < C && q == 0) eb[j] = e;
+      }
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // (7) exact top-k' by (est desc, position asc), as k_topk_fused with every
+  // slice written by this block
+  int32_t* oi = out_idx + (int64_t)bh * k;
+  float* oe = out_est ? out_est + (int64_t)bh * kprime : nullptr;
+  const int Ci = (int)C, P = (Ci + TK_SL - 1) / TK_SL;
+  uint32_t* s_hist = &s_wh[0][0];
+  float f[MAXS][4];
+#pragma unroll
+  for (int sl = 0; sl < MAXS; ++sl) {
+    const int c0 = sl * TK_SL + tid * 4;
+    const float4 t = *reinterpret_cast<const float4*>(eb + min(c0, (int)cstride - 4));
+    f[sl][0] = t.x; f[sl][1] = t.y; f[sl][2] = t.z; f[sl][3] = t.w;
+  }
+  for (int i = tid; i < 2049; i += 1024) s_hist[i] = 0u;
+  for (int i = tid; i < MAXS * TK_SL / 32; i += 1024) s_bits[i] = 0u;
+  if (tid < 4) s_sel[tid] = 0u;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int sl = 0; sl < MAXS; ++sl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (sl * TK_SL + tid * 4 + r < Ci) {
+        const uint32_t o = order_key(f[sl][r]);
+        kmin = min(kmin, o);
+        kmax = max(kmax, o);
+      }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  if (lane == 0) { s_r[wv] = kmin; s_r[16 + wv] = kmax; }
+  __syncthreads();
+  kmin = s_r[0];
+  kmax = s_r[16];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) { kmin = min(kmin, s_r[w]); kmax = max(kmax, s_r[16 + w]); }
+  float fmin, scale;
+  range_scale(kmin, kmax, fmin, scale);
+#pragma unroll
+  for (int sl = 0; sl < MAXS; ++sl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (sl * TK_SL + tid * 4 + r < Ci) atomicAdd(&s_hist[est_bin(f[sl][r], fmin, scale)], 1u);
+  __syncthreads();
+  {
+    // cumulative #(bin >= b); thread t owns bins 2047 - 2t and 2046 - 2t
+    const uint32_t hh = s_hist[2047 - 2 * tid], hl = s_hist[2046 - 2 * tid];
+    uint2 tot;
+    const uint2 ex = block_exscan2<1024>(make_uint2(hh + hl, 0), s_w, tot);
+    s_hist[2047 - 2 * tid] = ex.x + hh;
+    s_hist[2046 - 2 * tid] = ex.x + hh + hl;
+  }
+  __syncthreads();
+  for (int bn = tid; bn < 2048; bn += 1024)
+    if (s_hist[bn] >= (uint32_t)kprime && s_hist[bn + 1] < (uint32_t)kprime) s_sel[0] = bn;
+  __syncthreads();
+  const uint32_t b1 = s_sel[0];
+  const uint32_t above_tot = s_hist[b1 + 1];
+  const uint32_t Mb = s_hist[b1] - above_tot;
+  const uint32_t remaining = (uint32_t)kprime - above_tot;
+  if (Mb > (uint32_t)TK_MAXMEM) {
+    // tie-heavy threshold bin: whole-unit radix select
+    __syncthreads();  // s_hist is reused
+    topk_radix_block(eb, cb, Ci, kprime, (int)S, oi, oe, s_hist, s_w, s_sel);
+    return;
+  }
+  // b1's members, then their exact ranks; kept members are marked in s_bits
+#pragma unroll
+  for (int sl = 0; sl < MAXS; ++sl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int cc = sl * TK_SL + tid * 4 + r;
+      if (cc < Ci && est_bin(f[sl][r], fmin, scale) == b1) {
+        const uint32_t slot = atomicAdd(&s_sel[2], 1u);
+        s_mem[slot] = member_key(order_key(f[sl][r]), (uint32_t)cc);
+      }
+    }
+  __syncthreads();
+  for (uint32_t j = tid; j < Mb; j += 1024) {
+    const uint64_t mj = s_mem[j];
+    const uint32_t cj = ~(uint32_t)mj;
+    uint32_t rank = 0;
+#pragma unroll 8
+    for (uint32_t qq = 0; qq < Mb; ++qq) rank += (s_mem[qq] > mj) ? 1u : 0u;
+    if (rank < remaining) atomicOr(&s_bits[cj >> 5], 1u << (cj & 31));
+  }
+  __syncthreads();
+  for (int t = tid; t < (int)S; t += 1024) oi[t] = t;
+  // every slice's selection in position order after the sinks
+  uint32_t done = 0;  // selected candidates of the slices before
+  for (int p = 0; p < P; ++p) {
+    const int cp = p * TK_SL + tid * 4;
+    const int4 cv = *reinterpret_cast<const int4*>(cb + min(cp, (int)cstride - 4));
+    const int32_t ci[4] = {cv.x, cv.y, cv.z, cv.w};
+    uint32_t selm = 0;
+    float fo[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int sl = 0; sl < MAXS; ++sl) {
+      if (sl != p) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int cc = sl * TK_SL + tid * 4 + r;
+        fo[r] = f[sl][r];
+        if (cc < Ci) {
+          const uint32_t bn = est_bin(f[sl][r], fmin, scale);
+          if (bn > b1 || (bn == b1 && ((s_bits[cc >> 5] >> (cc & 31)) & 1u))) selm |= 1u << r;
+        }
+      }
+    }
+    uint2 tot;
+    const uint2 ex = block_exscan2<1024>(make_uint2((uint32_t)__popc(selm), 0u), s_w, tot);
+    uint32_t pos = done + ex.x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (((selm >> r) & 1u) && pos < (uint32_t)kprime) {  // bound holds by construction
+        oi[S + pos] = ci[r];
+        if (oe) oe[pos] = fo[r];
+        ++pos;
+      }
+    }
+    done += tot.x;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // K7 split-K sparse attention ([TS] Problem Statement; System-Level
 // Innovations 1: only the selected rows are fetched).  Block = 64 selected
 // rows of one (b, h); 16 lanes per row (16 B of K and of V per lane), 16 row
@@ -2096,6 +2470,36 @@ hipError_t launch_topk_counted(int BH, const float* est, const int32_t* cand, in
   return launch(k_topk_select, grid, dim3(1024), st, ev_select, est, cand, cstride, Cmax, kprime,
                 S, k, P, (const uint32_t*)range, (const uint32_t*)rows, (const uint2*)sorted,
                 tkmeta, out_idx, out_est, cmeta);
+}
+
+hipError_t launch_retrieve_small(int m, int dtype, const void* Q, int BH, int n_kv_heads, int G,
+                                 const SignMask& sg, float c, int rho, const Tiers& tw,
+                                 const AppendJob& app, const uint8_t* ids, const uint32_t* rec,
+                                 int64_t cap, int64_t S, int64_t E, int64_t C, int kprime, int k,
+                                 int nbins, uint8_t* lut, float* yq, uint8_t* scores, int64_t Epad,
+                                 int32_t* meta, int32_t* cand, float* est, int64_t cstride,
+                                 int32_t* out_idx, float* out_est, hipStream_t st,
+                                 const EvPair& ev) {
+  // one block per unit; appended keys take 16 lanes each of the block
+  if (E < 1 || C < 1 || C > E || C > (int64_t)kSmallTopkSlices * kTopkSlice || app.n > 64 ||
+      nbins > 256 || kprime < 1 || (int64_t)kprime > C)
+    return hipErrorInvalidValue;
+  const float invG = 1.0f / (float)G;
+  const uint4* id4 = (const uint4*)ids;
+#define PKV_RS(TT, MM)                                                                          \
+  return launch(k_retrieve_small<TT, MM>, dim3(BH), dim3(1024), st, ev, (const TT*)Q, n_kv_heads, \
+                G, invG, sg, c, rho, tw, app, id4, rec, cap, S, E, C, kprime, k, nbins, lut, yq,  \
+                scores, Epad, meta, cand, est, cstride, out_idx, out_est)
+  if (m == 8) {
+    if (dtype == 0) PKV_RS(uint16_t, 8);
+    PKV_RS(float, 8);
+  }
+  if (m == 4) {
+    if (dtype == 0) PKV_RS(uint16_t, 4);
+    PKV_RS(float, 4);
+  }
+#undef PKV_RS
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs,

@@ -69,6 +69,26 @@ void run_index(const pariskv_config& c, int32_t k) {
                                nullptr) == PARISKV_ERR_INVALID_ARG);
   int64_t E = 0, C = 0;
   EXPECT(pariskv_retrieve_sizes(ix, k, &E, &C) == PARISKV_OK && E == 50104 - c.n_sink && C > 0);
+  // retrieval paths: E > PARISKV_SMALL_MAX_KEYS takes the pipeline by default;
+  // the single kernel serves shared retrieval with at most 16384 candidates
+  EXPECT(pariskv_retrieval_path(ix, k) == PARISKV_PATH_PIPELINE);
+  EXPECT(pariskv_set_retrieval_path(ix, 7) == PARISKV_ERR_INVALID_ARG);
+  EXPECT(pariskv_set_retrieval_path(nullptr, PARISKV_PATH_SINGLE) == PARISKV_ERR_INVALID_ARG);
+  EXPECT(pariskv_set_retrieval_path(ix, PARISKV_PATH_SINGLE) == PARISKV_OK);
+  if (c.per_query_head) {
+    EXPECT(pariskv_retrieval_path(ix, k) == PARISKV_ERR_UNSUPPORTED);
+    // a refused retrieval leaves a deferred append pending (encoded at destroy)
+    EXPECT(pariskv_append_keys(ix, dev(3), c.capacity, 1, nullptr) == PARISKV_OK);
+    EXPECT(pariskv_retrieve_topk(ix, dev(4), k, (int32_t*)dev(5), nullptr, dev(7), ws,
+                                 nullptr) == PARISKV_ERR_UNSUPPORTED);
+    EXPECT(pariskv_index_size(ix) == 50105);
+  } else {
+    EXPECT(pariskv_retrieval_path(ix, k) == PARISKV_PATH_SINGLE);
+    EXPECT(pariskv_retrieve_topk(ix, dev(4), k, (int32_t*)dev(5), (float*)dev(6), dev(7), ws,
+                                 nullptr) == PARISKV_OK);
+  }
+  EXPECT(pariskv_retrieval_path(ix, c.n_sink) == PARISKV_ERR_INVALID_ARG);
+  EXPECT(pariskv_set_retrieval_path(ix, PARISKV_PATH_AUTO) == PARISKV_OK);
   // a window over the index
   if (!c.per_query_head) {
     pariskv_window* w = nullptr;

@@ -108,6 +108,17 @@ hipError_t launch_attn_merge(int dtype, const float* part, int nch, int rows, vo
   return hipSuccess;
 }
 
+hipError_t launch_retrieve_small(int m, int dtype, const void* Q, int BH, int n_kv_heads, int G,
+                                 const SignMask& sg, float c, int rho, const Tiers& tw,
+                                 const AppendJob& app, const uint8_t* ids, const uint32_t* rec,
+                                 int64_t cap, int64_t S, int64_t E, int64_t C, int kprime, int k,
+                                 int nbins, uint8_t* lut, float* yq, uint8_t* scores, int64_t Epad,
+                                 int32_t* meta, int32_t* cand, float* est, int64_t cstride,
+                                 int32_t* out_idx, float* out_est, hipStream_t st,
+                                 const EvPair& ev) {
+  return hipSuccess;
+}
+
 size_t si_build_ws_bytes(int BH, int64_t S, int64_t n) {
   return (size_t)BH * (size_t)(n > S ? n - S : 1) * 32 + 4096;
 }

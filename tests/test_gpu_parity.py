@@ -66,10 +66,15 @@ def _gpu():
     need_gpu()
 
 
-def run_case(orc, w, capacity=None, extra_rows=0):
-    case("%s: batch=%d Hkv=%d Hq=%d N=%d k=%d S=%d %s" % (
-        w.name, w.batch, w.n_kv_heads, w.n_q_heads, w.N, w.k, w.sinks, w.dtype))
+PATHS = {"pipeline": pk.PATH_PIPELINE, "single": pk.PATH_SINGLE}
+
+
+def run_case(orc, w, capacity=None, extra_rows=0, path="pipeline"):
+    case("%s: batch=%d Hkv=%d Hq=%d N=%d k=%d S=%d %s, %s path" % (
+        w.name, w.batch, w.n_kv_heads, w.n_q_heads, w.N, w.k, w.sinks, w.dtype, path))
     lay, cfg, L = gpu_layer(w, capacity=capacity)
+    L.set_path(PATHS[path])
+    assert L.path == PATHS[path]
     BH = w.batch * w.n_kv_heads
     idx = torch.empty(BH, w.k, dtype=torch.int32, device="cuda")
     est = torch.empty(BH, w.kprime, dtype=torch.float32, device="cuda")
@@ -78,10 +83,13 @@ def run_case(orc, w, capacity=None, extra_rows=0):
     return lay, cfg, L, idx, est
 
 
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("name", list(SMALL))
-def test_retrieve_parity_small(orc, name):
+def test_retrieve_parity_small(orc, name, path):
+    """Every intermediate and output against the oracle, on the multi-kernel
+    pipeline and on the single-kernel path (one block per unit)."""
     w = SMALL[name]
-    lay, cfg, L, idx, est = run_case(orc, w)
+    lay, cfg, L, idx, est = run_case(orc, w, path=path)
     BH = w.batch * w.n_kv_heads
     ids, nib, wq = pk.pariskv_debug_export(L.handle, 0, w.N, BH, B=w.B)
     Kh = host_f32(lay["K"])
@@ -145,13 +153,14 @@ def test_append_equals_build(orc, dtype, n0, steps, B):
             assert np.array_equal(x[bh], y)
 
 
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("B", [16, 32])
-def test_ties_duplicates_and_zero_keys(orc, B):
+def test_ties_duplicates_and_zero_keys(orc, B, path):
     """Duplicated keys tie on both the vote score and the estimate; all-zero
     keys have w = 0 and estimate 0 (and -0 vs +0 must not matter)."""
     w = W("ties", 1, 2, 4, 128, 3000, "bf16", B=B, cand_num=1, cand_den=5, k=300,
           seed=31)
-    case("ties/duplicates/zero keys B=%d" % B)
+    case("ties/duplicates/zero keys B=%d, %s path" % (B, path))
     lay = synth.make_layer(w, "cuda")
     K = lay["K"]
     K[:, :, 1000:1600] = K[:, :, 100:700]        # duplicates
@@ -159,6 +168,7 @@ def test_ties_duplicates_and_zero_keys(orc, B):
     K[:, :, 2100:2200] = -K[:, :, 2200:2300]      # opposite keys
     cfg = pk.config_for(w)
     L = pk.Layer(cfg, lay["signs"], K, w.N, k=w.k)
+    L.set_path(PATHS[path])
     BH = 2
     idx = torch.empty(BH, w.k, dtype=torch.int32, device="cuda")
     est = torch.empty(BH, w.kprime, dtype=torch.float32, device="cuda")
@@ -174,23 +184,28 @@ def test_ties_duplicates_and_zero_keys(orc, B):
     L.close()
 
 
-@pytest.mark.parametrize("N,den,k,copies", [
-    (100000, 20, 1024, 0),      # 5000 candidates: 2 top-k slices, one kernel
-    (40000, 5, 1024, 5000),     # 2 slices, threshold bin of 5000 equal keys
-    (60000, 5, 2048, 8000),     # 3 slices, threshold bin of 8000 equal keys
-    (80000, 5, 2048, 0),        # 16000 candidates: 4 slices, the one-kernel limit
-    (90000, 5, 2048, 0),        # 18000 candidates: 5 slices, histogram + select
-    (150000, 2, 4096, 0),       # 75000 candidates: 19 slices, generic select
-    (150000, 2, 4096, 8000),    # 19 slices and the radix select of a tied bin
+@pytest.mark.parametrize("N,den,k,copies,path", [
+    (100000, 20, 1024, 0, "pipeline"),    # 5000 candidates: 2 top-k slices, one kernel
+    (40000, 5, 1024, 5000, "pipeline"),   # 2 slices, threshold bin of 5000 equal keys
+    (60000, 5, 2048, 8000, "pipeline"),   # 3 slices, threshold bin of 8000 equal keys
+    (80000, 5, 2048, 0, "pipeline"),      # 16000 candidates: 4 slices, the one-kernel limit
+    (90000, 5, 2048, 0, "pipeline"),      # 18000 candidates: 5 slices, histogram + select
+    (150000, 2, 4096, 0, "pipeline"),     # 75000 candidates: 19 slices, generic select
+    (150000, 2, 4096, 8000, "pipeline"),  # 19 slices and the radix select of a tied bin
+    # the single-kernel path: its top-k over 2 and 4 slices, and its radix select
+    (100000, 20, 1024, 0, "single"),
+    (40000, 5, 1024, 5000, "single"),
+    (80000, 5, 2048, 0, "single"),
 ])
-def test_topk_paths(orc, N, den, k, copies):
+def test_topk_paths(orc, N, den, k, copies, path):
     """The top-k's paths: one kernel up to 4 slices of 4096 candidates, the
     histogram + select pair above that (more than 16 slices: the generic
     select), and a threshold bin holding more than 4096 members (identical
-    keys tie exactly on score and estimate; the lower positions win)."""
+    keys tie exactly on score and estimate; the lower positions win); the
+    single-kernel retrieval's own top-k up to 4 slices."""
     w = W("topk paths", 1, 1, 4, 128, N, "bf16", cand_num=1, cand_den=den, k=k,
           seed=33)
-    case("top-k paths N=%d f=1/%d k=%d copies=%d" % (N, den, k, copies))
+    case("top-k paths N=%d f=1/%d k=%d copies=%d, %s path" % (N, den, k, copies, path))
     lay = synth.make_layer(w, "cuda")
     K = lay["K"]
     if copies:
@@ -200,6 +215,7 @@ def test_topk_paths(orc, N, den, k, copies):
         K[0, 0, 1000:1000 + copies] = qbar.to(K.dtype)
     cfg = pk.config_for(w)
     L = pk.Layer(cfg, lay["signs"], K, w.N, k=w.k)
+    L.set_path(PATHS[path])
     idx = torch.empty(1, w.k, dtype=torch.int32, device="cuda")
     est = torch.empty(1, w.kprime, dtype=torch.float32, device="cuda")
     L.retrieve(lay["Q"], idx, est)
@@ -213,6 +229,50 @@ def test_topk_paths(orc, N, den, k, copies):
         # the tied copies fill the top-k in position order
         assert np.array_equal(idx.cpu().numpy()[0], np.arange(1000, 1000 + w.k))
     L.close()
+
+
+@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("fp32", 32)])
+def test_decode_steps_single_kernel(orc, dtype, B):
+    """Decode steps: one key appended per (b, h) and a retrieval each step. The
+    single kernel encodes the deferred key itself before scanning; its
+    outputs equal the pipeline's at every step and the oracle's at the end."""
+    n0, steps = 3000, 6
+    total = n0 + steps
+    w = W("decode steps", 2, 2, 8, 128, total, dtype, B=B, k=96, sinks=8, seed=35)
+    case("decode steps %s B=%d" % (dtype, B))
+    lay = synth.make_layer(w, "cuda", capacity=total + 5)
+    cfg = pk.config_for(w, capacity=total + 5)
+    K, Q = lay["K"], lay["Q"]
+    rows = K.shape[2]
+    single = pk.Layer(cfg, lay["signs"], K, n0, k=w.k)
+    pipe = pk.Layer(cfg, lay["signs"], K, n0, k=w.k)
+    single.set_path(pk.PATH_SINGLE)
+    pipe.set_path(pk.PATH_PIPELINE)
+    BH = w.batch * w.n_kv_heads
+    for t in range(steps):
+        outs = []
+        for L in (single, pipe):
+            L.append(K[:, :, n0 + t:], 1, rows_per_head=rows)
+            idx = torch.empty(BH, w.k, dtype=torch.int32, device="cuda")
+            est = torch.empty(BH, w.kprime, dtype=torch.float32, device="cuda")
+            L.retrieve(Q, idx, est)
+            torch.cuda.synchronize()
+            outs.append((idx.cpu().numpy(), est.cpu().numpy().view(np.uint32)))
+        assert np.array_equal(outs[0][0], outs[1][0]), t
+        assert np.array_equal(outs[0][1], outs[1][1]), t
+    assert single.size == total
+    Kh, Qh = host_f32(K), host_f32(Q)
+    heads = list(range(BH))
+    enc = oracle_encode_heads(orc, w, Kh, lay["signs"], heads, n=total)
+    ref = oracle_retrieve_heads(orc, w, Qh, enc, lay["signs"], heads)
+    a = pk.pariskv_debug_export(single.handle, 0, total, BH, B=B)
+    gi = gpu_intermediates(single, BH)
+    for bh in heads:
+        for x, y in zip(a, enc[bh]):
+            assert np.array_equal(x[bh], y), bh
+        assert_retrieval_equal(w, gi, outs[0][0], outs[0][1].view(np.float32), ref[bh], bh)
+    single.close()
+    pipe.close()
 
 
 def test_deterministic_repeat():
