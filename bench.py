@@ -71,6 +71,10 @@ def parse():
                     help="L,U: sliding-window regions with L local tokens and an "
                          "update buffer of U; the far store is HBM, or pinned host "
                          "memory with --uva kv")
+    ap.add_argument("--retrieval-path", default="auto",
+                    choices=["auto", "pipeline", "single"],
+                    help="retrieval path: the library's choice (auto), the "
+                         "multi-kernel pipeline, or the single kernel")
     ap.add_argument("--per-query-head", action="store_true",
                     help="unshared retrieval: every query head selects its own "
                          "top-k with its own query over its KV head's index")
@@ -172,6 +176,8 @@ def main():
             continue
         cfg = pk.config_for(w, capacity=cap)
         L = pk.Layer(cfg, lay["signs"], lay["K"], w.N - win_L, k=w.k, device=dev)
+        L.set_path({"auto": pk.PATH_AUTO, "pipeline": pk.PATH_PIPELINE,
+                    "single": pk.PATH_SINGLE}[args.retrieval_path])
         if args.window:
             # near store: sinks, then the ring of local + buffer rows; far store:
             # the layer's own K/V (positions at their rows), moved to pinned
@@ -324,6 +330,17 @@ def main():
     # per candidate: 64 B of codes and B fp16 calibration factors
     rerank_bytes = (64.0 + 2 * w.B) * C * U
     rerank_us = float(kern[:, 3].mean())
+    # the single-kernel path: its one kernel is stamped as the scan stage and
+    # moves the scan's and the rerank's bytes
+    single = (not args.si) and \
+        pk.pariskv_retrieval_path(layers[0][0].handle, w.k) == pk.PATH_SINGLE
+    roof_kernel = "si_scan" if args.si else "vote_scan"
+    if single:
+        roof_kernel = "retrieve_single"
+        scan_bytes = scan_bytes + rerank_bytes
+        achieved = scan_bytes / (scan_us * 1e-6) / 1e9
+        traffic = read_traffic("retrieve_single_%s%s_traffic.txt" % (args.workload, variant),
+                               scan_bytes)
 
     result = {
         "metric": METRIC,
@@ -352,6 +369,8 @@ def main():
             "method": ("Self-Indexing sign VQ + LUT-GEMV over all keys" if args.si
                        else "ParisKV votes + RSQ-IP rerank"),
             "parallelism": "single GPU", "launch": mode,
+            "retrieval_path": ("Self-Indexing kernels" if args.si else
+                               "single kernel" if single else "multi-kernel pipeline"),
             "kv_placement": {"none": "HBM", "v": "V in pinned host memory",
                              "kv": "K and V in pinned host memory"}[args.uva],
             "window": ({"sinks": w.sinks, "local": win_L, "update_buffer": win_U,
@@ -359,7 +378,7 @@ def main():
                        if args.window else None),
         },
         "roofline": {
-            "kernel": "si_scan" if args.si else "vote_scan",
+            "kernel": roof_kernel,
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
@@ -377,7 +396,7 @@ def main():
             "algorithmic_bytes_per_launch": attn_bytes,
             "avg_launch_us": attn_us,
         },
-        "rerank_gather": None if args.si else {
+        "rerank_gather": None if (args.si or single) else {
             "kernel": "compact_rerank",
             "achieved": rerank_bytes / (rerank_us * 1e-6) / 1e9,
             "unit": "GB/s", "algorithmic_bytes_per_launch": rerank_bytes,

@@ -226,20 +226,19 @@ PARISKV_API int32_t pariskv_retrieve_topk_profiled(
 PARISKV_API const char *pariskv_stage_name(int32_t stage);
 
 /* How pariskv_retrieve_topk runs on an index.
- *   PARISKV_PATH_AUTO (the default): one kernel for small indexes -- units
- *     of one (b, KV head) (shared retrieval), at most
- *     PARISKV_SMALL_MAX_KEYS eligible keys and at most 16,384 candidates per
- *     unit -- else the multi-kernel pipeline.
- *   PARISKV_PATH_PIPELINE: always the multi-kernel pipeline.
- *   PARISKV_PATH_SINGLE: always one kernel, one 1024-thread block per unit
- *     running every stage; a retrieval it cannot serve (per-query-head
- *     units, more than 16,384 candidates per unit) returns UNSUPPORTED.
+ *   PARISKV_PATH_AUTO (the default): the multi-kernel pipeline.
+ *   PARISKV_PATH_PIPELINE: the multi-kernel pipeline.
+ *   PARISKV_PATH_SINGLE: one kernel, one 1024-thread block per unit running
+ *     every stage with block barriers instead of kernel boundaries; it
+ *     serves units of one (b, KV head) (shared retrieval) with at most 16,384
+ *     candidates, and returns UNSUPPORTED otherwise.  Measured slower than
+ *     the pipeline from 4K keys per unit up (one block serialises every
+ *     dependent memory round trip), so AUTO does not pick it.
  * The two paths return the same bits and leave the same intermediates in
  * the workspace.  Errors: INVALID_ARG. */
 #define PARISKV_PATH_AUTO 0
 #define PARISKV_PATH_PIPELINE 1
 #define PARISKV_PATH_SINGLE 2
-#define PARISKV_SMALL_MAX_KEYS 16384
 PARISKV_API int32_t pariskv_set_retrieval_path(pariskv_index *index,
                                                int32_t path);
 

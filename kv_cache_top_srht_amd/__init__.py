@@ -22,9 +22,8 @@ PARISKV_DTYPE_FP32 = 1
 PARISKV_RETRIEVE_STAGES = 6
 
 DEBUG_LUT, DEBUG_YQ, DEBUG_SCORES, DEBUG_CAND, DEBUG_EST, DEBUG_THRESH = range(6)
-# retrieval paths (pariskv_set_retrieval_path) and the default single-kernel limit
+# retrieval paths (pariskv_set_retrieval_path)
 PATH_AUTO, PATH_PIPELINE, PATH_SINGLE = 0, 1, 2
-SMALL_MAX_KEYS = 16384
 
 
 class PariskvError(RuntimeError):

@@ -178,15 +178,14 @@ int32_t flush_pending(pariskv_index* ix) {
                                        ix->pending_stream, pkv::EvPair{}));
 }
 
-// The retrieval path for E eligible keys and C candidates per unit: the
-// single kernel serves shared retrieval with at most kSmallTopkSlices top-k
-// slices; by default only small indexes take it.
-int32_t choose_path(const pariskv_index* ix, int64_t E, int64_t C) {
+// The retrieval path for C candidates per unit: the single kernel, when
+// asked for, serves shared retrieval with at most kSmallTopkSlices top-k
+// slices; otherwise the pipeline.
+int32_t choose_path(const pariskv_index* ix, int64_t C) {
+  if (ix->path != PARISKV_PATH_SINGLE) return PARISKV_PATH_PIPELINE;
   const bool fits = !ix->cfg.per_query_head &&
                     C <= (int64_t)pkv::kSmallTopkSlices * pkv::kTopkSlice;
-  if (ix->path == PARISKV_PATH_PIPELINE) return PARISKV_PATH_PIPELINE;
-  if (ix->path == PARISKV_PATH_SINGLE) return fits ? PARISKV_PATH_SINGLE : PARISKV_ERR_UNSUPPORTED;
-  return fits && E <= PARISKV_SMALL_MAX_KEYS ? PARISKV_PATH_SINGLE : PARISKV_PATH_PIPELINE;
+  return fits ? PARISKV_PATH_SINGLE : PARISKV_ERR_UNSUPPORTED;
 }
 
 int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t* out_idx,
@@ -202,7 +201,7 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   const int64_t E = N - S, kp = k - S;
   const int64_t C = cand_count(E, kp, c->cand_num, c->cand_den);
   if (C > 1024ll * pkv::kTopkSlice) return PARISKV_ERR_UNSUPPORTED;  // > 4M candidates per head
-  const int32_t path = choose_path(ix, E, C);
+  const int32_t path = choose_path(ix, C);
   if (path < 0) return path;
   hipStream_t st = (hipStream_t)stream;
   pariskv_index* mix = const_cast<pariskv_index*>(ix);
@@ -601,7 +600,7 @@ int32_t pariskv_retrieval_path(const pariskv_index* ix, int32_t k) {
   int64_t E = 0, C = 0;
   const int32_t rc = pariskv_retrieve_sizes(ix, k, &E, &C);
   if (rc) return rc;
-  return choose_path(ix, E, C);
+  return choose_path(ix, C);
 }
 
 int32_t pariskv_debug_intermediate(const pariskv_index* ix, int32_t k, const void* ws,

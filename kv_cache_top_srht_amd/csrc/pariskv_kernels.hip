@@ -1715,8 +1715,10 @@ __global__ __launch_bounds__(1024) void k_topk_fused(
 // stage is the fp32 operation sequence of its multi-kernel counterpart, and
 // the workspace receives the same vote table, yq, scores, threshold meta,
 // candidates and estimates.  For at most kSmallTopkSlices * 4096 candidates
-// (the top-k holds every estimate in registers); worth it while one CU per
-// unit streams the ids faster than the six kernel boundaries it saves.
+// (the top-k holds every estimate in registers).  Opt-in: one block
+// serialises every dependent memory round trip of the stages (query, ids,
+// scores, candidates, records, estimates), which costs more than the kernel
+// boundaries it removes, from 4K keys per unit up.
 // ---------------------------------------------------------------------------
 template <typename T, int M>
 __global__ __launch_bounds__(1024) void k_retrieve_small(

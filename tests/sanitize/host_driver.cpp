@@ -69,8 +69,8 @@ void run_index(const pariskv_config& c, int32_t k) {
                                nullptr) == PARISKV_ERR_INVALID_ARG);
   int64_t E = 0, C = 0;
   EXPECT(pariskv_retrieve_sizes(ix, k, &E, &C) == PARISKV_OK && E == 50104 - c.n_sink && C > 0);
-  // retrieval paths: E > PARISKV_SMALL_MAX_KEYS takes the pipeline by default;
-  // the single kernel serves shared retrieval with at most 16384 candidates
+  // retrieval paths: the pipeline by default; the single kernel, when asked
+  // for, serves shared retrieval with at most 16384 candidates
   EXPECT(pariskv_retrieval_path(ix, k) == PARISKV_PATH_PIPELINE);
   EXPECT(pariskv_set_retrieval_path(ix, 7) == PARISKV_ERR_INVALID_ARG);
   EXPECT(pariskv_set_retrieval_path(nullptr, PARISKV_PATH_SINGLE) == PARISKV_ERR_INVALID_ARG);
