@@ -38,6 +38,10 @@ SMALL = {
                      tiers=(8, 7, 6, 5, 4, 3, 2, 1), k=512, seed=18),
     "wide_tiers": W("rho 4, tiers 15/10/5/1", 1, 2, 8, 128, 30000, "bf16",
                     tiers=(15, 10, 5, 1), cand_num=1, cand_den=10, k=512, seed=19),
+    # 241 score bins and 313 chunks of 256 keys: the threshold kernel's rows
+    # exceed one round of register-held loads (re-read path)
+    "wide_tiers_long": W("tiers 15/10/5/1, 80K keys", 1, 1, 4, 128, 80000, "bf16",
+                         tiers=(15, 10, 5, 1), k=1024, seed=37),
     "rho2": W("rho 2, tiers 2/1", 2, 2, 8, 128, 20000, "bf16", rho=2, tiers=(2, 1),
               k=300, seed=20),
     "rho1": W("rho 1", 1, 4, 4, 128, 20000, "bf16", rho=1, tiers=(1,),
