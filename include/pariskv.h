@@ -502,7 +502,10 @@ PARISKV_API int32_t pariskv_si_debug_export(const pariskv_si_index *index,
                                             float *codebook_host);
 
 /* Intermediates of the last pariskv_si_retrieve_topk that used `ws`:
- * which = 0: LUT fp32 [b][h][32][16]; 1: scores fp32 [b][h][N - S];
+ * which = 0: LUT fp32 [b][h][32][16]; 1: scores fp32 [b][h][N - S] (every
+ * eligible key's, recomputed by this call from the index and the workspace's
+ * byte table with the scan's arithmetic into a region of the workspace that
+ * the retrieval leaves unused: the retrieval itself stores bins only);
  * 2: int32 [b][h][4] = (threshold bin T, #bin > T, #bin == T, candidates). */
 PARISKV_API int32_t pariskv_si_debug_intermediate(const pariskv_si_index *index,
                                                   int32_t k, const void *ws,

@@ -125,7 +125,6 @@ int32_t si_retrieve_impl(const pariskv_si_index* ix, const void* Q, int32_t k, i
   float* lut = (float*)(base + L.lut);
   float* tab = (float*)(base + L.tab);
   float* range = (float*)(base + L.range);
-  float* fscore = (float*)(base + L.fscore);
   uint8_t* bins = base + L.bins;
   uint32_t* chist = (uint32_t*)(base + L.chist);
   uint32_t* coff = (uint32_t*)(base + L.coff);
@@ -150,15 +149,15 @@ int32_t si_retrieve_impl(const pariskv_si_index* ix, const void* Q, int32_t k, i
   e = pkv::launch_si_lut(c->key_dtype, Q, BH, c->n_kv_heads, G, ix->cb, lut, tab, range, st,
                          ev(0));
   if (e != hipSuccess) return hip_status(e);
-  e = pkv::launch_si_scan(kpt, nch, BH, ix->ids, c->capacity, S, E, tab, range, fscore, bins,
-                          L.Epad, chist, (int)L.nchunks_max, st, ev(1));
+  e = pkv::launch_si_scan(kpt, nch, BH, ix->ids, c->capacity, S, E, tab, range, bins, L.Epad,
+                          chist, (int)L.nchunks_max, st, ev(1));
   if (e != hipSuccess) return hip_status(e);
   // the bin holding rank k', every key of it kept
   e = pkv::launch_thresh(BH, chist, (int)L.nchunks_max, nch, 256, 256, kp, 1, meta, coff, st,
                          ev(2));
   if (e != hipSuccess) return hip_status(e);
-  e = pkv::launch_si_compact(kpt, nch, BH, bins, fscore, L.Epad, S, E, meta, coff,
-                             (int)L.nchunks_max, cand, est, L.cstride, mmc, st, ev(3));
+  e = pkv::launch_si_compact(kpt, nch, BH, bins, ix->ids, c->capacity, tab, L.Epad, S, E, meta,
+                             coff, (int)L.nchunks_max, cand, est, L.cstride, mmc, st, ev(3));
   if (e != hipSuccess) return hip_status(e);
   // candidates are usually a little over k' (the keys of the bins down to
   // the one holding rank k'): blocks for twice that, more slices are looped
@@ -312,7 +311,16 @@ int32_t pariskv_si_debug_intermediate(const pariskv_si_index* ix, int32_t k, con
   };
   switch (which) {
     case 0: return rows(L.lut, 512 * 4, 512 * 4);
-    case 1: return rows(L.fscore, (size_t)L.Epad * 4, (size_t)E * 4);
+    case 1: {
+      // recomputed from the ids and this workspace's byte table
+      uint8_t* wsb = const_cast<uint8_t*>(base);
+      if (pkv::launch_si_scores((int)BH, ix->ids, c->capacity, c->n_sink, E,
+                                (const float*)(wsb + L.tab), (float*)(wsb + L.fscore), L.Epad,
+                                nullptr) != hipSuccess ||
+          hipDeviceSynchronize() != hipSuccess)
+        return PARISKV_ERR_HIP;
+      return rows(L.fscore, (size_t)L.Epad * 4, (size_t)E * 4);
+    }
     case 2: return rows(L.meta, 16, 16);
     default: return PARISKV_ERR_INVALID_ARG;
   }

@@ -241,12 +241,23 @@ __device__ __forceinline__ uint32_t si_bin(float s, float lo, float scale) {
   return (uint32_t)fminf((s - lo) * scale, 255.0f);
 }
 
+// A key's LUT-GEMV score from its 16 id bytes and the unit's byte table
+// (LDS or global): (((0 + tab[0][byte_0]) + tab[1][byte_1]) + ...) in fp32.
+__device__ __forceinline__ float si_score(const uint4 x, const float* tab) {
+  const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s = s + tab[r * 256 + ((w4[r >> 2] >> ((r & 3) * 8)) & 0xFFu)];
+  return s;
+}
+
 // ---------------------------------------------------------------------------
 // SI7 LUT-GEMV scan ([SI] Methodology B): for keys i in [S, N)
 //   score_i = (((0 + tab[0][byte_0]) + tab[1][byte_1]) + ...) + tab[15][byte_15]
-// (fp32, 16 LDS reads per key), written as fp32 with its bin (one byte) and
-// a cumulative per-chunk row #(bin >= v) of the bins, as the vote scan does
-// for vote scores, so the threshold and compaction kernels serve both.
+// (fp32, 16 LDS reads per key); writes its bin (one byte) and a cumulative
+// per-chunk row #(bin >= v) of the bins, as the vote scan does for vote
+// scores, so the threshold and compaction kernels serve both.  The fp32 score
+// itself is not stored: the compaction recomputes it for the candidates.
 // Grid (chunks, units), KPT * NT keys per chunk.
 // ---------------------------------------------------------------------------
 template <int KPT, int NT>
@@ -254,7 +265,6 @@ __global__ __launch_bounds__(NT) void k_si_scan(const uint4* __restrict__ ids, i
                                                 int64_t S, int64_t E,
                                                 const float* __restrict__ tab,
                                                 const float* __restrict__ range,
-                                                float* __restrict__ fscore,
                                                 uint8_t* __restrict__ bins, int64_t Epad,
                                                 uint32_t* __restrict__ chist, int chunk_stride) {
   constexpr int NW = NT / 64;
@@ -284,14 +294,9 @@ __global__ __launch_bounds__(NT) void k_si_scan(const uint4* __restrict__ ids, i
   for (int t = 0; t < KPT; ++t) {
     const int64_t p = p0 + t * NT;
     const bool valid = p < E;
-    const uint32_t w4[4] = {x[t].x, x[t].y, x[t].z, x[t].w};
-    float s = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s = s + s_tab[r * 256 + ((w4[r >> 2] >> ((r & 3) * 8)) & 0xFFu)];
-    const uint32_t bn = si_bin(s, lo, scale);
+    const uint32_t bn = si_bin(si_score(x[t], s_tab), lo, scale);
     zeros += (uint32_t)__popcll(__ballot(valid && bn == 0));
     if (valid) {
-      fscore[(int64_t)u * Epad + p] = s;
       bins[(int64_t)u * Epad + p] = (uint8_t)bn;
       if (bn != 0) atomicAdd(&s_hist[wv][bn], 1u);
     }
@@ -327,12 +332,15 @@ __global__ __launch_bounds__(NT) void k_si_scan(const uint4* __restrict__ ids, i
 // SI8 candidates of two consecutive chunks: every key whose bin is >= T (the
 // bin holding rank k', found by the threshold kernel with all of T's keys
 // kept), listed in ascending position order at the chunk's offset with its
-// fp32 score; plus the block's score range (order keys) for the top-k.
+// fp32 score (recomputed from the key's ids and the byte table in global
+// memory, the scan's order of additions); plus the block's score range
+// (order keys) for the top-k.
 // Grid (ceil(chunks / 2), units), 256 threads, KPT keys per thread.
 // ---------------------------------------------------------------------------
 template <int KPT>
 __global__ __launch_bounds__(256) void k_si_compact(const uint8_t* __restrict__ bins,
-                                                    const float* __restrict__ fscore,
+                                                    const uint4* __restrict__ ids, int64_t cap,
+                                                    const float* __restrict__ tab,
                                                     int64_t Epad, int64_t S, int64_t E,
                                                     const int32_t* __restrict__ meta,
                                                     const uint32_t* __restrict__ coff,
@@ -381,11 +389,13 @@ __global__ __launch_bounds__(256) void k_si_compact(const uint8_t* __restrict__ 
   }
   __syncthreads();
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+  const uint4* src = ids + (int64_t)u * cap + S;
+  const float* tb = tab + (int64_t)u * 4096;
   for (uint32_t j = tid; j < ntot; j += 256) {
     const uint32_t ent = s_list[j];
     const int h = (int)(ent >> 14);
     const int64_t q = (int64_t)(c0 + h) * CH + (ent & 0x3FFFu);  // eligible index
-    const float e = fscore[(int64_t)u * Epad + q];
+    const float e = si_score(src[q], tb);
     const uint32_t o = (j >= n0) ? off_c[1] + (j - n0) : off_c[0] + j;
     cand[(int64_t)u * cstride + o] = (int32_t)(S + q);
     est[(int64_t)u * cstride + o] = e;
@@ -405,6 +415,19 @@ __global__ __launch_bounds__(256) void k_si_compact(const uint8_t* __restrict__ 
     mm[((int64_t)u * chunk_stride + chunk) * 2 + 0] = min(min(s_mm[0], s_mm[1]), min(s_mm[2], s_mm[3]));
     mm[((int64_t)u * chunk_stride + chunk) * 2 + 1] = max(max(s_mm[4], s_mm[5]), max(s_mm[6], s_mm[7]));
   }
+}
+
+// Every eligible key's fp32 score, for parity introspection only (the
+// retrieval keeps bins): the scan's arithmetic from the table in global
+// memory.  Grid (ceil(E / 256), units).
+__global__ __launch_bounds__(256) void k_si_scores(const uint4* __restrict__ ids, int64_t cap,
+                                                   int64_t S, int64_t E,
+                                                   const float* __restrict__ tab,
+                                                   float* __restrict__ fscore, int64_t Epad) {
+  const int u = blockIdx.y;
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p < E) fscore[(int64_t)u * Epad + p] = si_score(ids[(int64_t)u * cap + S + p],
+                                                      tab + (int64_t)u * 4096);
 }
 
 // ---------------------------------------------------------------------------
@@ -491,15 +514,15 @@ hipError_t launch_si_lut(int dtype, const void* Q, int units, int n_kv_heads, in
 
 hipError_t launch_si_scan(int kpt, int nchunks, int units, const uint8_t* ids, int64_t cap,
                           int64_t S, int64_t E, const float* tab, const float* range,
-                          float* fscore, uint8_t* bins, int64_t Epad, uint32_t* chist,
-                          int chunk_stride, hipStream_t st, const EvPair& ev) {
+                          uint8_t* bins, int64_t Epad, uint32_t* chist, int chunk_stride,
+                          hipStream_t st, const EvPair& ev) {
   const dim3 grid(nchunks, units);
   const uint4* id4 = (const uint4*)ids;
   switch (kpt) {
 #define PKV_SS(K, NT)                                                                          \
   case K:                                                                                      \
     return launch(k_si_scan<(K * 256) / NT, NT>, grid, dim3(NT), st, ev, id4, cap, S, E, tab, \
-                  range, fscore, bins, Epad, chist, chunk_stride);
+                  range, bins, Epad, chist, chunk_stride);
     PKV_SS(1, 256) PKV_SS(2, 256) PKV_SS(4, 512) PKV_SS(8, 512) PKV_SS(16, 512)
 #undef PKV_SS
     default: return hipErrorInvalidValue;
@@ -507,20 +530,28 @@ hipError_t launch_si_scan(int kpt, int nchunks, int units, const uint8_t* ids, i
 }
 
 hipError_t launch_si_compact(int kpt, int nchunks, int units, const uint8_t* bins,
-                             const float* fscore, int64_t Epad, int64_t S, int64_t E,
-                             const int32_t* meta, const uint32_t* coff, int chunk_stride,
-                             int32_t* cand, float* est, int64_t cstride, uint32_t* mm,
-                             hipStream_t st, const EvPair& ev) {
+                             const uint8_t* ids, int64_t cap, const float* tab, int64_t Epad,
+                             int64_t S, int64_t E, const int32_t* meta, const uint32_t* coff,
+                             int chunk_stride, int32_t* cand, float* est, int64_t cstride,
+                             uint32_t* mm, hipStream_t st, const EvPair& ev) {
   const dim3 grid((nchunks + 1) / 2, units);
   switch (kpt) {
 #define PKV_SC(K)                                                                              \
   case K:                                                                                      \
-    return launch(k_si_compact<K>, grid, dim3(256), st, ev, bins, fscore, Epad, S, E, meta,   \
-                  coff, chunk_stride, nchunks, cand, est, cstride, mm);
+    return launch(k_si_compact<K>, grid, dim3(256), st, ev, bins, (const uint4*)ids, cap, tab, \
+                  Epad, S, E, meta, coff, chunk_stride, nchunks, cand, est, cstride, mm);
     PKV_SC(1) PKV_SC(2) PKV_SC(4) PKV_SC(8) PKV_SC(16)
 #undef PKV_SC
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_si_scores(int units, const uint8_t* ids, int64_t cap, int64_t S, int64_t E,
+                            const float* tab, float* fscore, int64_t Epad, hipStream_t st) {
+  if (E <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((E + 255) / 256), units);
+  return launch(k_si_scores, grid, dim3(256), st, EvPair{}, (const uint4*)ids, cap, S, E, tab,
+                fscore, Epad);
 }
 
 }  // namespace pkv

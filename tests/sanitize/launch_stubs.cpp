@@ -83,16 +83,21 @@ hipError_t launch_si_lut(int dtype, const void* Q, int units, int n_kv_heads, in
 
 hipError_t launch_si_scan(int kpt, int nchunks, int units, const uint8_t* ids, int64_t cap,
                           int64_t S, int64_t E, const float* tab, const float* range,
-                          float* fscore, uint8_t* bins, int64_t Epad, uint32_t* chist,
-                          int chunk_stride, hipStream_t st, const EvPair& ev) {
+                          uint8_t* bins, int64_t Epad, uint32_t* chist, int chunk_stride,
+                          hipStream_t st, const EvPair& ev) {
   return hipSuccess;
 }
 
 hipError_t launch_si_compact(int kpt, int nchunks, int units, const uint8_t* bins,
-                             const float* fscore, int64_t Epad, int64_t S, int64_t E,
-                             const int32_t* meta, const uint32_t* coff, int chunk_stride,
-                             int32_t* cand, float* est, int64_t cstride, uint32_t* mm,
-                             hipStream_t st, const EvPair& ev) {
+                             const uint8_t* ids, int64_t cap, const float* tab, int64_t Epad,
+                             int64_t S, int64_t E, const int32_t* meta, const uint32_t* coff,
+                             int chunk_stride, int32_t* cand, float* est, int64_t cstride,
+                             uint32_t* mm, hipStream_t st, const EvPair& ev) {
+  return hipSuccess;
+}
+
+hipError_t launch_si_scores(int units, const uint8_t* ids, int64_t cap, int64_t S, int64_t E,
+                            const float* tab, float* fscore, int64_t Epad, hipStream_t st) {
   return hipSuccess;
 }
 
