@@ -2197,8 +2197,10 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
 
 // K8 log-sum-exp merge of the split-K partials -> output row per query head.
 // One block per (b, query head).  Partials are staged in LDS 64 chunks at a
-// time (one round of 16-byte loads); threads 0..127 then combine them for
-// their output element, rescaling by the running maximum across tiles.
+// time (one round of 16-byte loads); wave 0 forms the tile's maximum and
+// each chunk's factor exp2(m_c - M) once, then threads 0..127 combine the
+// chunks for their output element in chunk order, rescaling by the running
+// maximum across tiles.
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part, int nch,
                                                     T* __restrict__ out) {
@@ -2208,6 +2210,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   const int bq = blockIdx.x, tid = threadIdx.x;
   const float* pp = part + (int64_t)bq * nch * kPartStride;
   __shared__ float4 s_p4[TILE * R4];
+  __shared__ float s_f[TILE], s_m[1];
   const float* s_p = reinterpret_cast<const float*>(s_p4);
   float o = 0.0f, l = 0.0f, M = -INFINITY;
   for (int t0 = 0; t0 < nch; t0 += TILE) {
@@ -2227,18 +2230,26 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
       if (i < n4) s_p4[i] = v[u];
     }
     __syncthreads();
-    if (tid < 128) {
-      float tm = -INFINITY;
-      for (int c = 0; c < nt; ++c) tm = fmaxf(tm, s_p[c * kPartStride + 128]);
+    if (tid < 64) {
+      // lane c: chunk c's maximum; the tile's by a wave reduction
+      const float mc = tid < nt ? s_p[tid * kPartStride + 128] : -INFINITY;
+      float tm = mc;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) tm = fmaxf(tm, __shfl_xor(tm, off));
       const float Mn = fmaxf(M, tm);
+      if (tid < nt) s_f[tid] = (Mn == -INFINITY || mc == -INFINITY) ? 0.0f : exp2f(mc - Mn);
+      if (tid == 0) s_m[0] = Mn;
+    }
+    __syncthreads();
+    if (tid < 128) {
+      const float Mn = s_m[0];
       if (Mn != -INFINITY) {
         const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
         o *= r;
         l *= r;
         M = Mn;
         for (int c = 0; c < nt; ++c) {
-          const float mc = s_p[c * kPartStride + 128];
-          const float f = (mc == -INFINITY) ? 0.0f : exp2f(mc - M);
+          const float f = s_f[c];
           o = __builtin_fmaf(f, s_p[c * kPartStride + tid], o);
           l = __builtin_fmaf(f, s_p[c * kPartStride + 129], l);
         }
