@@ -225,7 +225,8 @@ PARISKV_API int32_t pariskv_retrieve_topk_profiled(
 /* Name of retrieval stage s, or NULL. */
 PARISKV_API const char *pariskv_stage_name(int32_t stage);
 
-/* How pariskv_retrieve_topk runs on an index.
+/* How pariskv_retrieve_topk runs on an index: an execution choice for the
+ * same [TS] Core Algorithmic Innovations 2 pipeline, not a different method.
  *   PARISKV_PATH_AUTO (the default): the multi-kernel pipeline.
  *   PARISKV_PATH_PIPELINE: the multi-kernel pipeline.
  *   PARISKV_PATH_SINGLE: one kernel, one 1024-thread block per unit running
