@@ -771,15 +771,27 @@ __device__ __forceinline__ float rerank_estimate(
     wsw[2] = ww.z;
     wsw[3] = ww.w;
   }
-  float t[NB];
+  // every table value of the NB subspaces first: the 32 LDS reads are
+  // independent and all go out before the first sum waits (left to itself the
+  // compiler waits after each subspace's 8), then each subspace's sum in
+  // coordinate order
+  float v[NB][M];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     // subspace 4 q NB / 4 + i: coordinates from nibble j0 of code dword bb
     const int bb = (i * M) >> 3, j0 = (i * M) & 7;
     const float* pb = s_P + (4 * q + bb) * kPtabRow;
+#pragma unroll
+    for (int jj = 0; jj < M; ++jj)
+      v[i][jj] = pb[(j0 + jj) * 16 + ((cws[bb] >> (4 * (j0 + jj))) & 15u)];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float t[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
     float p = 0.0f;
 #pragma unroll
-    for (int jj = j0; jj < j0 + M; ++jj) p = p + pb[jj * 16 + ((cws[bb] >> (4 * jj)) & 15u)];
+    for (int jj = 0; jj < M; ++jj) p = p + v[i][jj];
     const uint16_t hb = (uint16_t)(wsw[i >> 1] >> ((i & 1) * 16));
     t[i] = (float)__builtin_bit_cast(_Float16, hb) * p;
   }
