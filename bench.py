@@ -116,9 +116,9 @@ def read_traffic(name: str, launches_bytes: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the work shards by (batch, KV head) with no exchange; see the "
-              "design notes).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the work shards by (batch, KV head) with no exchange between "
+              "GPUs).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
