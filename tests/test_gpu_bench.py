@@ -1,0 +1,45 @@
+"""The benchmark's JSON line on a short run of the tiny workload: every field
+of the contract is present and consistent (one GPU, the metric's unit, the
+roofline of the dominant kernel, the oracle's CPU baseline)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from gpu_helpers import need_gpu
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_json_line():
+    need_gpu()
+    cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--workload", "tiny",
+           "--steps", "5", "--warmup", "2", "--profile-steps", "3", "--warm-steps", "3",
+           "--cpu-steps", "1", "--layers", "2"]
+    print("bench:", " ".join(cmd[2:]), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=280, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-3000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    j = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in j, key
+    assert j["n_gpus"] == 1 and j["steps"] == 5 and j["warmup"] == 2
+    assert j["unit"] == "keys/s" and j["value"] > 0 and j["higher_is_better"] is True
+    assert j["ms_per_step"] > 0 and j["vs_baseline"] is None
+    assert j["config"]["workload"]
+    roof = j["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in roof, key
+    assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-9
+    cb = j["cpu_baseline"]
+    for key in ("value", "unit", "cores", "kind", "sample"):
+        assert key in cb, key
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
