@@ -232,9 +232,10 @@ PARISKV_API const char *pariskv_stage_name(int32_t stage);
  *   PARISKV_PATH_SINGLE: one kernel, one 1024-thread block per unit running
  *     every stage with block barriers instead of kernel boundaries; it
  *     serves units of one (b, KV head) (shared retrieval) with at most 16,384
- *     candidates, and returns UNSUPPORTED otherwise.  Measured slower than
- *     the pipeline from 4K keys per unit up (one block serialises every
- *     dependent memory round trip), so AUTO does not pick it.
+ *     candidates, and returns UNSUPPORTED otherwise.  Units of at most 8192
+ *     keys and 2048 candidates keep ids, scores and candidates in registers
+ *     and LDS.  Measured about 3% faster than the pipeline on a 4K-key unit
+ *     and slower on larger ones (one CU per unit), so AUTO does not pick it.
  * The two paths return the same bits and leave the same intermediates in
  * the workspace.  Errors: INVALID_ARG. */
 #define PARISKV_PATH_AUTO 0

@@ -123,6 +123,10 @@ constexpr int kTopkMaxMembers = 4096;
 constexpr int kTopkFusedSlices = 4;
 // the single-kernel retrieval holds up to this many slices of candidates
 constexpr int kSmallTopkSlices = 4;
+// up to these sizes per unit it keeps every key's ids and score and every
+// candidate in registers and LDS (the resident variant)
+constexpr int kTinyKeys = 8192;
+constexpr int kTinyCands = 2048;
 // up to this many slices, the select kernel loads all histogram rows at once
 constexpr int kTopkFewSlices = 16;
 // split-K attention partial per (query head, chunk): o[128], m, l, 2 unused

@@ -112,9 +112,9 @@ __device__ __forceinline__ uint32_t sign_byte_of(const SignMask& sg, int sub) {
 // the ids of subspaces 2 s (low nibble) and 2 s + 1 (high nibble) (M = 4).
 // ---------------------------------------------------------------------------
 // Encodes key row r of (b, h) = bh (16 lanes, lane `sub` = coordinates
-// 8 sub .. 8 sub + 7) into index position `pos`.
+// 8 sub .. 8 sub + 7) into index position `pos`; returns the lane's id byte.
 template <typename T, int M>
-__device__ __forceinline__ void encode_key(const T* __restrict__ K, int64_t rows_per_head,
+__device__ __forceinline__ uint32_t encode_key(const T* __restrict__ K, int64_t rows_per_head,
                                            int64_t bh, int64_t r, int64_t pos, int64_t cap,
                                            uint8_t* __restrict__ ids, uint32_t* __restrict__ rec,
                                            const SignMask& sg, float c, int sub) {
@@ -164,6 +164,7 @@ __device__ __forceinline__ void encode_key(const T* __restrict__ K, int64_t rows
     reinterpret_cast<uint16_t*>(rec)[key * 64 + 32 + sub] = (uint16_t)wpack;
   else
     rec[key * 32 + 16 + sub] = wpack;
+  return id;
 }
 
 template <typename T, int M>
@@ -335,6 +336,13 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
   const int b = bh / n_kv_heads, h = bh - b * n_kv_heads;
   const int Hq = n_kv_heads * G;
   __shared__ float s_yq[128];
+  // the codebook levels in LDS for the product table (uniform loads here; a
+  // per-lane index into the constant array would be a vector memory load)
+  __shared__ float s_lv[8];
+  if (tid == 0) {
+#pragma unroll
+    for (int l = 0; l < 8; ++l) s_lv[l] = cb_level<M>(l);
+  }
   if (tid < 16) {
     const int sub = tid;
     // all G query rows are loaded at once, then summed in head order
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
   // product table for the rerank: ptab[j][code] = fl(+-L[code & 7] yq_j), the
   // sign bit (code & 8) negating the product exactly
   for (int e = tid; e < 2048; e += 1024) {
-    const float pr = cb_level<M>(e & 7) * s_yq[e >> 4];
+    const float pr = s_lv[e & 7] * s_yq[e >> 4];
     ptab_out[(int64_t)bh * 2048 + e] = (e & 8) ? -pr : pr;
   }
   const int s = tid >> 6, l = tid & 63;
@@ -1744,6 +1752,7 @@ __global__ __launch_bounds__(1024) void k_retrieve_small(
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int b = bh / n_kv_heads, h = bh - b * n_kv_heads, Hq = n_kv_heads * G;
   __shared__ float s_yq[128];
+  __shared__ float s_lv[8];  // codebook levels for the product table
   __shared__ uint8_t s_lut[16 * 256];
   __shared__ float s_P[kPtabLds];
   __shared__ uint32_t s_wh[16][256];  // per-wave score histograms, then the top-k bins
@@ -1781,13 +1790,17 @@ __global__ __launch_bounds__(1024) void k_retrieve_small(
     reinterpret_cast<float4*>(yq_out + (int64_t)bh * 128 + sub * 8)[1] =
         make_float4(x[4], x[5], x[6], x[7]);
   }
+  if (tid == 0) {
+#pragma unroll
+    for (int l = 0; l < 8; ++l) s_lv[l] = cb_level<M>(l);
+  }
   for (int i = tid; i < 16 * 256; i += 1024) (&s_wh[0][0])[i] = 0u;
   __threadfence_block();
   __syncthreads();
   // signed product table (rows of kPtabRow floats) and the vote table, row
   // s = wave s
   for (int e = tid; e < 2048; e += 1024) {
-    const float pr = cb_level<M>(e & 7) * s_yq[e >> 4];
+    const float pr = s_lv[e & 7] * s_yq[e >> 4];
     s_P[(e >> 7) * kPtabRow + (e & 127)] = (e & 8) ? -pr : pr;
   }
   {
@@ -1934,6 +1947,7 @@ __global__ __launch_bounds__(1024) void k_retrieve_small(
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        if (j0 + r * 256 >= C) break;  // uniform: no candidates left
         const int64_t j = j0 + r * 256 + (tid >> 2);
         const float e = rerank_estimate<M>(cw[r], ww[r], s_P, q);
         if (j < C && q == 0) eb[j] = e;
@@ -2065,6 +2079,340 @@ __global__ __launch_bounds__(1024) void k_retrieve_small(
       }
     }
     done += tot.x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The single-kernel retrieval for tiny units (E <= kTinyKeys eligible keys,
+// C <= kTinyCands candidates): as k_retrieve_small, with everything resident.
+// The ids are loaded into registers at the start (8 keys per thread, the
+// keys appended by this call patched in from the encoding lanes through
+// LDS), and scores, candidates and estimates stay in LDS, so the record
+// gathers are the only global round trip after the query.  The workspace
+// receives the same intermediates.  The top-k ranks every member of the
+// threshold bin exactly (at most C of them, all in LDS).
+// ---------------------------------------------------------------------------
+template <typename T, int M>
+__global__ __launch_bounds__(1024) void k_retrieve_tiny(
+    const T* __restrict__ Q, int n_kv_heads, int G, float invG, SignMask sg, float c, int rho,
+    Tiers tw, AppendJob app, const uint4* __restrict__ ids, const uint32_t* __restrict__ rec,
+    int64_t cap, int64_t S, int64_t E, int64_t C, int kprime, int k, int nbins,
+    uint8_t* __restrict__ lut_out, float* __restrict__ yq_out, uint8_t* __restrict__ scores,
+    int64_t Epad, int32_t* __restrict__ meta, int32_t* __restrict__ cand, float* __restrict__ est,
+    int64_t cstride, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
+  constexpr int U = kTinyKeys / 1024;  // keys per thread
+  constexpr int CM = kTinyCands;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = bh / n_kv_heads, h = bh - b * n_kv_heads, Hq = n_kv_heads * G;
+  const int Ei = (int)E, Ci = (int)C;
+  __shared__ float s_yq[128];
+  __shared__ float s_lv[8];  // codebook levels for the product table
+  __shared__ uint8_t s_lut[16 * 256];
+  __shared__ float s_P[kPtabLds];
+  __shared__ uint32_t s_wh[16][256];  // per-wave score histograms, then the top-k bins
+  __shared__ uint32_t s_ge[257];
+  __shared__ __align__(16) uint8_t s_sc[kTinyKeys];
+  __shared__ int32_t s_cand[CM];
+  __shared__ float s_est[CM];
+  __shared__ uint64_t s_mem[CM];
+  __shared__ uint32_t s_bits[CM / 32];
+  __shared__ __align__(16) uint8_t s_app[64 * 16];
+  __shared__ uint2 s_w[16];
+  __shared__ uint32_t s_sel[4];
+  __shared__ uint32_t s_r[32];
+
+  // (1) every eligible key's ids first (unconditional loads at clamped
+  // positions), then the appended keys' encode, whose lanes also leave the
+  // id bytes in LDS, and the query
+  const uint4* src = ids + (int64_t)bh * cap + S;
+  uint4 x[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int p = u * 1024 + tid;
+    x[u] = src[p < Ei ? p : Ei - 1];
+  }
+  if ((tid >> 4) < app.n)
+    s_app[tid] = (uint8_t)encode_key<T, M>((const T*)app.K, app.rows_per_head, bh, tid >> 4,
+                                           app.lo + (tid >> 4), app.cap, app.ids, app.rec, sg, c,
+                                           tid & 15);
+  if (tid < 16) {
+    const int sub = tid;
+    const T* q0 = Q + ((int64_t)(b * Hq + h * G) << 7) + sub * 8;
+    float xq[8];
+    load8(q0, xq);
+    for (int g = 1; g < G; ++g) {
+      float xg[8];
+      load8(q0 + ((int64_t)g << 7), xg);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xq[j] = xq[j] + xg[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xq[j] = xq[j] * invG;
+    srht16(xq, sign_byte_of(sg, sub), sub, c);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_yq[sub * 8 + j] = xq[j];
+    reinterpret_cast<float4*>(yq_out + (int64_t)bh * 128 + sub * 8)[0] =
+        make_float4(xq[0], xq[1], xq[2], xq[3]);
+    reinterpret_cast<float4*>(yq_out + (int64_t)bh * 128 + sub * 8)[1] =
+        make_float4(xq[4], xq[5], xq[6], xq[7]);
+  }
+  if (tid == 0) {
+#pragma unroll
+    for (int l = 0; l < 8; ++l) s_lv[l] = cb_level<M>(l);
+  }
+  for (int i = tid; i < 16 * 256; i += 1024) (&s_wh[0][0])[i] = 0u;
+  __threadfence_block();
+  __syncthreads();
+  // keys appended by this call: their ids from the encoding lanes
+  if (app.n > 0) {
+    const int64_t a0 = app.lo - S;  // eligible index of the first appended key
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t p = u * 1024 + tid;
+      if (p >= a0 && p < a0 + app.n)
+        x[u] = reinterpret_cast<const uint4*>(s_app)[p - a0];
+    }
+  }
+  // (2) signed product table and vote table (row s = wave s)
+  for (int e = tid; e < 2048; e += 1024) {
+    const float pr = s_lv[e & 7] * s_yq[e >> 4];
+    s_P[(e >> 7) * kPtabRow + (e & 127)] = (e & 8) ? -pr : pr;
+  }
+  {
+    const uint32_t word = vote_table_word<M>(s_yq, wv, lane, rho, tw);
+    reinterpret_cast<uint32_t*>(s_lut)[wv * 64 + lane] = word;
+    reinterpret_cast<uint32_t*>(lut_out + (int64_t)bh * 4096)[wv * 64 + lane] = word;
+  }
+  __syncthreads();
+
+  // (3) vote scan from registers: scores into LDS (and the workspace)
+  uint8_t* dst = scores + (int64_t)bh * Epad;
+  {
+    uint32_t zeros = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u * 1024 >= Ei) break;  // uniform: the rest of the key slots are empty
+      const int p = u * 1024 + tid;
+      const bool valid = p < Ei;
+      const uint32_t w4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+      uint32_t sc = 0;
+#pragma unroll
+      for (int bb = 0; bb < 16; ++bb)
+        sc += s_lut[bb * 256 + ((w4[bb >> 2] >> ((bb & 3) * 8)) & 0xFFu)];
+      zeros += (uint32_t)__popcll(__ballot(valid && sc == 0));
+      s_sc[p] = valid ? (uint8_t)sc : (uint8_t)0;
+      if (valid) {
+        dst[p] = (uint8_t)sc;
+        if (sc != 0) atomicAdd(&s_wh[wv][sc], 1u);
+      }
+    }
+    if (lane == 0) s_wh[wv][0] = zeros;
+  }
+  __syncthreads();
+
+  // (4) threshold: Tv = the largest v with #(score >= v) >= C
+  if (tid < 256) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) a += s_wh[w][tid];
+    s_ge[tid] = a;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    uint32_t hc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) hc[r] = s_ge[4 * lane + r];
+    const uint32_t loc = hc[0] + hc[1] + hc[2] + hc[3];
+    uint32_t inc = loc;  // sum over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t t = __shfl_down(inc, off);
+      if (lane + off < 64) inc += t;
+    }
+    const uint32_t g3 = inc - loc + hc[3], g2 = g3 + hc[2], g1 = g2 + hc[1], g0 = g1 + hc[0];
+    s_ge[4 * lane + 0] = g0;
+    s_ge[4 * lane + 1] = g1;
+    s_ge[4 * lane + 2] = g2;
+    s_ge[4 * lane + 3] = g3;
+    if (lane == 0) s_ge[256] = 0u;
+  }
+  __syncthreads();
+  if (tid < 256 && (int)s_ge[tid] >= Ci && (int)s_ge[tid + 1] < Ci) s_sel[0] = (uint32_t)tid;
+  __syncthreads();
+  const int Tv = (int)s_sel[0];
+  const int n_gt = (int)s_ge[Tv + 1];
+  const int Qt = Ci - n_gt;
+  if (tid == 0) {
+    meta[bh * 4 + 0] = Tv;
+    meta[bh * 4 + 1] = n_gt;
+    meta[bh * 4 + 2] = Qt;
+    meta[bh * 4 + 3] = Ci;
+  }
+
+  // (5) candidates in index order: thread t owns keys 8 t .. 8 t + 7
+  int32_t* cb = cand + (int64_t)bh * cstride;
+  {
+    const int p0 = tid * 8;
+    const int rem = Ei - p0;
+    const int nval = rem <= 0 ? 0 : (rem >= 8 ? 8 : rem);
+    const uint2 raw = reinterpret_cast<const uint2*>(s_sc)[tid];
+    uint8_t sc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) sc[t] = (uint8_t)(((t < 4) ? raw.x : raw.y) >> ((t & 3) * 8));
+    uint32_t gtm, eqm;
+    score_masks<8>(sc, raw, Tv, nval, nbins <= 128, gtm, eqm);
+    uint2 tot;
+    const uint2 ex = block_exscan2<1024>(
+        make_uint2((uint32_t)__popc(gtm), (uint32_t)__popc(eqm)), s_w, tot);
+    const int mine = Qt - (int)ex.y;  // ties of this thread still within the quota
+    const uint32_t r = mine <= 0 ? 0u : (uint32_t)(mine < 32 ? mine : 32);
+    uint32_t sel = gtm | lowest_bits(eqm, r);
+    int o = (int)ex.x + ((int)ex.y < Qt ? (int)ex.y : (Qt > 0 ? Qt : 0));
+    while (sel) {
+      const int t = __builtin_ctz(sel);
+      if (o < Ci) {
+        s_cand[o] = (int32_t)(S + p0 + t);
+        cb[o] = (int32_t)(S + p0 + t);
+      }
+      ++o;
+      sel &= sel - 1u;
+    }
+  }
+  __syncthreads();
+
+  // (6) RSQ-IP estimates, 4 lanes per candidate, 4 candidates per lane group
+  // fetched before any is used
+  float* eb = est + (int64_t)bh * cstride;
+  {
+    using WT = typename std::conditional<M == 8, uint2, uint4>::type;
+    const int q = tid & 3;
+    const uint32_t* rq = rec + (int64_t)bh * cap * 32;
+    for (int j0 = 0; j0 < Ci; j0 += 1024) {
+      int32_t pi[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + r * 256 + (tid >> 2);
+        pi[r] = s_cand[j < Ci ? j : Ci - 1];
+      }
+      uint4 cw[4];
+      WT ww[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t* rp = rq + (int64_t)pi[r] * 32;
+        cw[r] = reinterpret_cast<const uint4*>(rp)[q];
+        ww[r] = reinterpret_cast<const WT*>(rp + 16)[q];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (j0 + r * 256 >= Ci) break;  // uniform: no candidates left
+        const int j = j0 + r * 256 + (tid >> 2);
+        const float e = rerank_estimate<M>(cw[r], ww[r], s_P, q);
+        if (j < Ci && q == 0) {
+          s_est[j] = e;
+          eb[j] = e;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // (7) exact top-k' by (est desc, position asc)
+  int32_t* oi = out_idx + (int64_t)bh * k;
+  float* oe = out_est ? out_est + (int64_t)bh * kprime : nullptr;
+  // linear 2048-bin histogram between the estimates' extremes, the bin b1
+  // holding rank k', exact ranks of b1's members; thread t owns candidates
+  // 2 t and 2 t + 1
+  uint32_t* s_hist = &s_wh[0][0];
+  float f[2];
+  bool has[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int cc = 2 * tid + r;
+    has[r] = cc < Ci;
+    f[r] = has[r] ? s_est[cc] : 0.0f;
+  }
+  for (int i = tid; i < 2049; i += 1024) s_hist[i] = 0u;
+  if (tid < CM / 32) s_bits[tid] = 0u;
+  if (tid < 4) s_sel[tid] = 0u;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (has[r]) {
+      const uint32_t ok = order_key(f[r]);
+      kmin = min(kmin, ok);
+      kmax = max(kmax, ok);
+    }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  if (lane == 0) { s_r[wv] = kmin; s_r[16 + wv] = kmax; }
+  __syncthreads();
+  kmin = s_r[0];
+  kmax = s_r[16];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) { kmin = min(kmin, s_r[w]); kmax = max(kmax, s_r[16 + w]); }
+  float fmin, scale;
+  range_scale(kmin, kmax, fmin, scale);
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (has[r]) atomicAdd(&s_hist[est_bin(f[r], fmin, scale)], 1u);
+  __syncthreads();
+  {
+    // cumulative #(bin >= b); thread t owns bins 2047 - 2t and 2046 - 2t
+    const uint32_t hh = s_hist[2047 - 2 * tid], hl = s_hist[2046 - 2 * tid];
+    uint2 tot;
+    const uint2 ex = block_exscan2<1024>(make_uint2(hh + hl, 0), s_w, tot);
+    s_hist[2047 - 2 * tid] = ex.x + hh;
+    s_hist[2046 - 2 * tid] = ex.x + hh + hl;
+  }
+  __syncthreads();
+  for (int bn = tid; bn < 2048; bn += 1024)
+    if (s_hist[bn] >= (uint32_t)kprime && s_hist[bn + 1] < (uint32_t)kprime) s_sel[0] = bn;
+  __syncthreads();
+  const uint32_t b1 = s_sel[0];
+  const uint32_t above_tot = s_hist[b1 + 1];
+  const uint32_t Mb = s_hist[b1] - above_tot;
+  const uint32_t remaining = (uint32_t)kprime - above_tot;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int cc = 2 * tid + r;
+    if (has[r] && est_bin(f[r], fmin, scale) == b1) {
+      const uint32_t slot = atomicAdd(&s_sel[2], 1u);
+      s_mem[slot] = member_key(order_key(f[r]), (uint32_t)cc);
+    }
+  }
+  __syncthreads();
+  for (uint32_t j = tid; j < Mb; j += 1024) {
+    const uint64_t mj = s_mem[j];
+    const uint32_t cj = ~(uint32_t)mj;
+    uint32_t rank = 0;
+#pragma unroll 8
+    for (uint32_t qq = 0; qq < Mb; ++qq) rank += (s_mem[qq] > mj) ? 1u : 0u;
+    if (rank < remaining) atomicOr(&s_bits[cj >> 5], 1u << (cj & 31));
+  }
+  __syncthreads();
+  for (int t = tid; t < (int)S; t += 1024) oi[t] = t;
+  uint32_t selm = 0;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int cc = 2 * tid + r;
+    if (has[r]) {
+      const uint32_t bn = est_bin(f[r], fmin, scale);
+      if (bn > b1 || (bn == b1 && ((s_bits[cc >> 5] >> (cc & 31)) & 1u))) selm |= 1u << r;
+    }
+  }
+  uint2 tot;
+  const uint2 ex = block_exscan2<1024>(make_uint2((uint32_t)__popc(selm), 0u), s_w, tot);
+  uint32_t pos = ex.x;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (((selm >> r) & 1u) && pos < (uint32_t)kprime) {  // bound holds by construction
+      oi[S + pos] = s_cand[2 * tid + r];
+      if (oe) oe[pos] = f[r];
+      ++pos;
+    }
   }
 }
 
@@ -2511,10 +2859,16 @@ hipError_t launch_retrieve_small(int m, int dtype, const void* Q, int BH, int n_
     return hipErrorInvalidValue;
   const float invG = 1.0f / (float)G;
   const uint4* id4 = (const uint4*)ids;
+  const bool tiny = E <= kTinyKeys && C <= kTinyCands;
 #define PKV_RS(TT, MM)                                                                          \
-  return launch(k_retrieve_small<TT, MM>, dim3(BH), dim3(1024), st, ev, (const TT*)Q, n_kv_heads, \
-                G, invG, sg, c, rho, tw, app, id4, rec, cap, S, E, C, kprime, k, nbins, lut, yq,  \
-                scores, Epad, meta, cand, est, cstride, out_idx, out_est)
+  return tiny ? launch(k_retrieve_tiny<TT, MM>, dim3(BH), dim3(1024), st, ev, (const TT*)Q,     \
+                       n_kv_heads, G, invG, sg, c, rho, tw, app, id4, rec, cap, S, E, C, kprime, \
+                       k, nbins, lut, yq, scores, Epad, meta, cand, est, cstride, out_idx,       \
+                       out_est)                                                                 \
+              : launch(k_retrieve_small<TT, MM>, dim3(BH), dim3(1024), st, ev, (const TT*)Q,    \
+                       n_kv_heads, G, invG, sg, c, rho, tw, app, id4, rec, cap, S, E, C, kprime, \
+                       k, nbins, lut, yq, scores, Epad, meta, cand, est, cstride, out_idx,       \
+                       out_est)
   if (m == 8) {
     if (dtype == 0) PKV_RS(uint16_t, 8);
     PKV_RS(float, 8);

@@ -57,6 +57,10 @@ SMALL = {
                  tiers=(7, 6, 5, 4, 3, 2, 1, 1), k=512, seed=24),
     # degenerate sizes: one key to select, one eligible key, E a whole number
     # of 256-key chunks (no partial chunk) and one key more (a 1-key chunk)
+    # 1600 candidates of 8000 keys: the resident single kernel near its
+    # limits (8192 keys, 2048 candidates)
+    "cands_1600": W("8000 keys, 20% candidates", 1, 2, 8, 128, 8000, "bf16", cand_num=1,
+                    cand_den=5, k=512, seed=38),
     "kprime_one": W("k' = 1", 1, 2, 8, 128, 700, "bf16", k=33, sinks=32, seed=25),
     "e_one": W("E = 1", 1, 1, 4, 128, 17, "bf16", k=17, sinks=16, seed=26),
     "e_chunks_exact": W("E = 16 chunks", 1, 1, 4, 128, 4096, "bf16", k=64, seed=27),
