@@ -28,6 +28,30 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// Streaming loads (the `nt` bit: no retention in L2 or the Infinity Cache),
+// for data a decode step reads once: the id plane in the scans and the
+// gathered K/V rows in the attention.  On the million-token layer (its ids
+// do not fit the Infinity Cache) they keep the scores, records and partials
+// that the next kernels read in the caches.
+typedef uint32_t stream_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const stream_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const stream_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void load8_stream(const uint16_t* p, float (&x)[8]) {
+  const uint4 v = load_stream(reinterpret_cast<const uint4*>(p));
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+__device__ __forceinline__ void load8_stream(const float* p, float (&x)[8]) {
+  const uint4 a = load_stream(reinterpret_cast<const uint4*>(p));
+  const uint4 b = load_stream(reinterpret_cast<const uint4*>(p) + 1);
+  x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+  x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+  x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+  x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+}
+
 // Order key of an estimate: unsigned order == (est desc) order, -0 == +0.
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);

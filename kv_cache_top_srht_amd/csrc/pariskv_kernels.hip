@@ -403,7 +403,7 @@ __device__ __forceinline__ void scan_keys(const uint4* __restrict__ src, int chu
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
     const int64_t p = p0 + t * NT;
-    x[t] = src[(FULL || p < E) ? p : E - 1];
+    x[t] = load_stream(&src[(FULL || p < E) ? p : E - 1]);
   }
   __builtin_amdgcn_sched_barrier(0);
   // the LUT store waits for the LUT load alone (issued before the keys)
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(NT) void k_scan_group(const uint4* __restrict__ ids
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
     const int64_t p = p0 + t * NT;
-    x[t] = src[p < E ? p : E - 1];
+    x[t] = load_stream(&src[p < E ? p : E - 1]);
   }
   // interleave: entry 4 q + e gets byte e of head g's word in byte g % 4
 #pragma unroll
@@ -2498,8 +2498,8 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
   float kx[4][8], vx[4][8];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    load8((near[it] ? Kn : Kf) + (row[it] << 7), kx[it]);
-    load8((near[it] ? Vn : Vf) + (row[it] << 7), vx[it]);
+    load8_stream((near[it] ? Kn : Kf) + (row[it] << 7), kx[it]);
+    load8_stream((near[it] ? Vn : Vf) + (row[it] << 7), vx[it]);
   }
   float lg[4][G];
 #pragma unroll

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(NT) void k_si_scan(const uint4* __restrict__ ids, i
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
     const int64_t p = p0 + t * NT;
-    x[t] = src[p < E ? p : E - 1];
+    x[t] = load_stream(&src[p < E ? p : E - 1]);
   }
 #pragma unroll
   for (int i = 0; i < 4096 / 4 / NT; ++i) reinterpret_cast<float4*>(s_tab)[tid + i * NT] = tv[i];
