@@ -29,14 +29,19 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
 }
 
 // Streaming loads (the `nt` bit: no retention in L2 or the Infinity Cache),
-// for data a decode step reads once: the id plane in the scans and the
-// gathered K/V rows in the attention.  On the million-token layer (its ids
+// for data a decode step reads once: the id plane in the scans, the score
+// bytes in the compaction and the gathered K/V rows in the attention.  On the million-token layer (its ids
 // do not fit the Infinity Cache) they keep the scores, records and partials
 // that the next kernels read in the caches.
 typedef uint32_t stream_u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   const stream_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const stream_u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+typedef uint32_t stream_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+  const stream_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const stream_u32x2*>(p));
+  return make_uint2(v.x, v.y);
 }
 __device__ __forceinline__ void load8_stream(const uint16_t* p, float (&x)[8]) {
   const uint4 v = load_stream(reinterpret_cast<const uint4*>(p));

@@ -856,7 +856,7 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
     }
     const uint8_t* sp = scores + bh * Epad + (int64_t)chunk * CH + tid * KPT;
     if constexpr (KPT == 8) {
-      raw[h] = *reinterpret_cast<const uint2*>(sp);
+      raw[h] = load_stream(reinterpret_cast<const uint2*>(sp));
 #pragma unroll
       for (int t = 0; t < 8; ++t) sc[h][t] = (uint8_t)(((t < 4) ? raw[h].x : raw[h].y) >> ((t & 3) * 8));
     } else {
