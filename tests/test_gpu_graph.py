@@ -25,6 +25,12 @@ CASES = {
     # the single-kernel retrieval (resident variant for these sizes)
     "single_kernel": (W("2 heads x 6K", 1, 2, 8, 128, 6000, "bf16", k=128, seed=43),
                       "single"),
+    # unshared retrieval: one unit per query head, the grouped scan
+    "per_query_head": (W("per query head, 2 x 4 heads x 30K", 1, 2, 8, 128, 30000, "bf16",
+                         k=256, per_query_head=True, seed=44), "pipeline"),
+    # the Self-Indexing index and its retrieval
+    "self_indexing": (W("Self-Indexing, 4 heads x 100K", 1, 4, 16, 128, 100000, "bf16",
+                        k=512, sinks=16, seed=45), "si"),
 }
 STEPS = 4
 REPLAYS = 3
@@ -53,13 +59,18 @@ def test_graph_replays_equal_eager(name):
     Q = lay["Q"]
     Qs = [(Q.float() + 0.05 * torch.randn(Q.shape, generator=g, device="cuda")).to(Q.dtype)
           for _ in range(STEPS)]
-    U = w.batch * w.n_kv_heads
+    U = w.batch * (w.n_q_heads if w.per_query_head else w.n_kv_heads)
     scale = w.d ** -0.5
-    mode = pk.PATH_SINGLE if path == "single" else pk.PATH_PIPELINE
+
+    def new_layer():
+        if path == "si":
+            return pk.SiLayer(pk.si_config_for(w, capacity=w.N + 8), lay["K"], n0, k=w.k)
+        L = pk.Layer(cfg, lay["signs"], lay["K"], n0, k=w.k)
+        L.set_path(pk.PATH_SINGLE if path == "single" else pk.PATH_PIPELINE)
+        return L
 
     # eager reference on one index
-    A = pk.Layer(cfg, lay["signs"], lay["K"], n0, k=w.k)
-    A.set_path(mode)
+    A = new_layer()
     idx_e = [torch.empty(U, w.k, dtype=torch.int32, device="cuda") for _ in range(STEPS)]
     out_e = [torch.empty_like(Q) for _ in range(STEPS)]
     run_steps(A, lay, Qs, n0, idx_e, out_e, scale)
@@ -68,8 +79,7 @@ def test_graph_replays_equal_eager(name):
     ref_out = [x.view(torch.int16).cpu().numpy() for x in out_e]
 
     # the same steps captured on an identical index
-    B = pk.Layer(cfg, lay["signs"], lay["K"], n0, k=w.k)
-    B.set_path(mode)
+    B = new_layer()
     idx_g = [torch.empty(U, w.k, dtype=torch.int32, device="cuda") for _ in range(STEPS)]
     out_g = [torch.empty_like(Q) for _ in range(STEPS)]
     torch.cuda.synchronize()
