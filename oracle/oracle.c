@@ -207,6 +207,43 @@ int orc_codebook_f32(int m, float *L32, float *tau32)
 /* with (a, b) -> (a + b, a - b) for the pair (j, j + h), then * c.          */
 /* ------------------------------------------------------------------------ */
 
+/* The diagonal D from a seed: D_j = -1 when bit 63 of the j-th output    */
+/* (j = 0 .. d-1) of SplitMix64 seeded with `seed` is set, else +1.       */
+/* SplitMix64 (Steele, Lea and Flood, "Fast Splittable Pseudorandom       */
+/* Number Generators", OOPSLA 2014): the state advances by the odd        */
+/* constant 0x9e3779b97f4a7c15; each output is the state passed through   */
+/* two xor-shift-multiply rounds (shifts 30 and 27, multipliers            */
+/* 0xbf58476d1ce4e5b9 and 0x94d049bb133111eb) and a final xor-shift by 31. */
+int orc_srht_signs(uint64_t seed, int d, int8_t *D)
+{
+    if (d < 1) return ORC_EINVAL;
+    uint64_t state = seed;
+    for (int j = 0; j < d; j++) {
+        state += 0x9e3779b97f4a7c15ull;
+        uint64_t z = state;
+        z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+        z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+        z = z ^ (z >> 31);
+        D[j] = (z >> 63) ? -1 : 1;
+    }
+    return ORC_OK;
+}
+
+/* Raw SplitMix64 outputs (the generator's known-answer pin). */
+int orc_splitmix64(uint64_t seed, int n, uint64_t *out)
+{
+    if (n < 0) return ORC_EINVAL;
+    uint64_t state = seed;
+    for (int j = 0; j < n; j++) {
+        state += 0x9e3779b97f4a7c15ull;
+        uint64_t z = state;
+        z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+        z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+        out[j] = z ^ (z >> 31);
+    }
+    return ORC_OK;
+}
+
 float orc_rot_scale(int d)
 {
     return (float)(1.0 / sqrt((double)d));
@@ -718,22 +755,17 @@ int orc_si_lut(int d, int G, const float *Q, const float *cb, float *lut)
 }
 
 /* [SI] Methodology B, the approximate score of a key: the sum of its LUT   */
-/* entries.  Reading of the fp32 order: the sub-vectors are taken in pairs  */
-/* (2t, 2t + 1), each pair summed first, and the pair sums added in order:  */
-/* s = 0; for t: s = s + (lut[2t][id_2t] + lut[2t+1][id_2t+1]).  Scores of  */
+/* entries, one per sub-vector, written out as that sum: fp32, sub-vectors  */
+/* in order, s = 0; for b = 0 .. d/4 - 1: s = s + lut[b][id_b].  Scores of  */
 /* keys [S, n).                                                              */
 int orc_si_scores(int d, int64_t n, int64_t S, const uint8_t *ids,
                   const float *lut, float *scores)
 {
-    if (d < 8 || d % 8 || S < 0) return ORC_EINVAL;
+    if (d < 4 || d % 4 || S < 0) return ORC_EINVAL;
     int B = d / 4;
     for (int64_t i = S; i < n; i++) {
         float s = 0.0f;
-        for (int t = 0; t < B / 2; t++) {
-            float pr = lut[(2 * t) * 16 + ids[i * B + 2 * t]] +
-                       lut[(2 * t + 1) * 16 + ids[i * B + 2 * t + 1]];
-            s = s + pr;
-        }
+        for (int b = 0; b < B; b++) s = s + lut[b * 16 + ids[i * B + b]];
         scores[i - S] = s;
     }
     return ORC_OK;

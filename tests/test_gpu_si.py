@@ -1,11 +1,24 @@
 """Self-Indexing workload ("Self-Indexing KVCache: Predicting Sparse
 Attention from Compressed Keys", Methodology A-C) on the GPU against the
-oracle: means, centroids and sign ids bit-exact (both sides accumulate in
-fp64 and round once to fp32), LUT, scores and top-k bit-exact, attention over
-the selection within the bf16 bar."""
+oracle: means, centroids, sign ids and the LUT bit-exact (both sides
+accumulate the build in fp64 and round once to fp32; the LUT follows one
+stated fp32 order), attention over the selection within the bf16 bar.
+
+Scores: the oracle sums a key's 32 LUT entries in sub-vector order, the
+kernel sums them in byte pairs (the order of its byte-indexed table).  Any
+fp32 summation of n terms lies within gamma_{n-1} * sum|terms| of the exact
+sum (Higham, Accuracy and Stability, 4.2), so the two differ by at most
+tol = 2 gamma_31 sum|terms| per key, which the tests assert.  The top-k
+then agrees except across the selection boundary: a key the GPU took and
+the oracle did not (e) and one the oracle took and the GPU did not (m) are
+allowed only when o_m - o_e <= tol_e + tol_m (GPU order puts e first, so
+g_e >= g_m), and every such pair is reported."""
 import numpy as np
 import pytest
 import torch
+
+U32 = 2.0 ** -24
+GAMMA31 = 31 * U32 / (1 - 31 * U32)
 
 from gpu_helpers import ATTN_TOL_BF16, ATTN_TOL_FP32, case, host_f32, need_gpu, pk, synth
 
@@ -71,15 +84,37 @@ def check_head(orc, w, n0, lay, g, bh, Kh, Qh, Vh):
     assert np.array_equal(ids[bh], ids_o), bh
     ref = orc.si_retrieve_head(Qh[b, h * G:(h + 1) * G], ids_o, cb_o, S=S, k=w.k)
     assert np.array_equal(g["lut"][bh].view(np.uint32), ref["lut"].view(np.uint32)), bh
-    assert np.array_equal(g["scores"][bh].view(np.uint32), ref["scores"].view(np.uint32)), bh
-    assert np.array_equal(g["idx"][bh], ref["idx"]), bh
-    assert np.array_equal(g["sc"][bh].view(np.uint32), ref["est"].view(np.uint32)), bh
+    # per-key bound on |kernel score - oracle score| from the LUT terms
+    lut64 = ref["lut"].astype(np.float64)
+    B = lut64.shape[0]
+    terms = np.abs(lut64[np.arange(B)[None], ids_o[S:].astype(np.int64)])
+    tol = 2 * GAMMA31 * terms.sum(axis=1)
+    o = ref["scores"].astype(np.float64)
+    gsc = g["scores"][bh].astype(np.float64)
+    assert np.all(np.abs(gsc - o) <= tol), (bh, float(np.max(np.abs(gsc - o) - tol)))
+    gi, oi = g["idx"][bh], ref["idx"]
+    # the selection is exact for the kernel's own scores: (score desc, position asc)
+    own = np.sort(np.lexsort((np.arange(len(gsc)), -g["scores"][bh]))[:w.k - S] + S)
+    assert np.array_equal(gi, np.concatenate([np.arange(S), own])), bh
+    extra = np.setdiff1d(gi[S:], oi[S:]) - S
+    miss = np.setdiff1d(oi[S:], gi[S:]) - S
+    assert len(extra) == len(miss), bh
+    for e in extra:
+        for m in miss:
+            assert o[m] - o[e] <= tol[e] + tol[m], (bh, e + S, m + S)
+    if len(extra):
+        case("head %d: %d boundary swaps within tolerance: %s" % (
+            bh, len(extra), ", ".join("%d<->%d (oracle %.9g vs %.9g)" % (
+                e + S, m + S, o[e], o[m]) for e, m in zip(extra, miss))))
+    # scores reported for the selection, aligned with idx[S:]
+    gs = g["sc"][bh].astype(np.float64)
+    assert np.all(np.abs(gs - o[gi[S:] - S]) <= tol[gi[S:] - S]), bh
     T, gt, eq, Cn = g["meta"][bh]
     assert gt + eq == Cn and gt < w.k - S <= Cn
-    tol = ATTN_TOL_BF16 if w.dtype == "bf16" else ATTN_TOL_FP32
+    atol = ATTN_TOL_BF16 if w.dtype == "bf16" else ATTN_TOL_FP32
     ref_o = orc.attention(Qh[b, h * G:(h + 1) * G], Kh[b, h], Vh[b, h], g["idx"][bh],
                           w.d ** -0.5)
-    assert np.max(np.abs(g["out"][b, h * G:(h + 1) * G] - ref_o)) <= tol, bh
+    assert np.max(np.abs(g["out"][b, h * G:(h + 1) * G] - ref_o)) <= atol, bh
 
 
 @pytest.mark.parametrize("name", list(CASES))

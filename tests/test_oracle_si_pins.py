@@ -166,3 +166,27 @@ def test_si_retrieval_prefers_high_inner_products(orc):
     assert np.array_equal(np.sort(order), sel)
     truth = X[S:].astype(np.float64) @ Q.astype(np.float64).mean(axis=0)
     assert np.corrcoef(sc, truth)[0, 1] > 0.7
+
+
+def test_si_score_is_the_sum_of_its_lut_entries(orc):
+    """[SI] Methodology B defines a key's score as the sum of its LUT entries.
+    Dyadic entries (small integers times 2^-6) make every fp32 sum exact, so
+    the oracle must equal the exact sum; for arbitrary entries it must lie
+    within the forward-error bound of a sequential fp32 sum of B terms,
+    gamma_{B-1} * sum |entries| (Higham, Accuracy and Stability, 4.2)."""
+    r = rng(11)
+    B, n = D // 4, 3000
+    ids = r.integers(0, 16, (n, B)).astype(np.uint8)
+    lut = (r.integers(-512, 513, (B, 16)) * 2.0 ** -6).astype(np.float32)
+    terms = lut.astype(np.float64)[np.arange(B)[None], ids.astype(np.int64)]
+    sc = orc.si_scores(ids, lut, 5)
+    assert np.array_equal(sc.astype(np.float64), terms[5:].sum(axis=1))
+    lut = r.standard_normal((B, 16)).astype(np.float32)
+    terms = lut.astype(np.float64)[np.arange(B)[None], ids.astype(np.int64)]
+    sc = orc.si_scores(ids, lut, 0)
+    u = 2.0 ** -24
+    gamma = (B - 1) * u / (1 - (B - 1) * u)
+    assert np.all(np.abs(sc - terms.sum(axis=1)) <= gamma * np.abs(terms).sum(axis=1))
+    # a term left out or taken from the wrong sub-vector breaks the bound
+    assert np.any(np.abs(terms[:, 1:].sum(axis=1) - terms.sum(axis=1)) >
+                  gamma * np.abs(terms).sum(axis=1))
