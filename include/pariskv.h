@@ -162,10 +162,12 @@ PARISKV_API int32_t pariskv_build_index(const pariskv_config *cfg,
  *                for r < n_new (a pointer into the KV cache at row N with
  *                new_rows_per_head = the cache's rows per head works).
  * A decode step's few keys (n_new <= 48) are encoded lazily: by the first
- * kernel of the next pariskv_retrieve_topk on the same stream, or, if
- * something else comes first (another append, a retrieval on another stream,
- * pariskv_debug_export, pariskv_index_destroy), by a kernel launched then on
- * this call's stream.  K_new must stay valid and unmodified until then.
+ * kernel of the next pariskv_retrieve_topk, on that call's stream (which the
+ * caller orders after the writes of K_new, as any retrieval that must see the
+ * new keys requires, whether or not it is the append's stream), or, if
+ * something else comes first (another append, pariskv_debug_export,
+ * pariskv_index_destroy), by a kernel launched then on this call's stream.
+ * K_new must stay valid and unmodified until then.
  * Larger appends are encoded at once on `stream`.
  * Errors: INVALID_ARG, CAPACITY (N + n_new > capacity), HIP. */
 PARISKV_API int32_t pariskv_append_keys(pariskv_index *index,
@@ -341,7 +343,9 @@ PARISKV_API int32_t pariskv_window_create(pariskv_index *index,
 /* Appends one token per (b, h) (rows K_new/V_new[(b * n_kv_heads + h) *
  * new_rows_per_head], device-accessible) to the update buffer; when that
  * fills the buffer, moves the U oldest local tokens to the retrieval region
- * (far-store copies and an index encode, asynchronous on `stream`).
+ * (far-store copies and an index encode, asynchronous on `stream`).  Their
+ * ring rows start at S + R % (L + U) and wrap to row S when they pass the
+ * ring's end, so R needs no alignment to U.
  * Errors: INVALID_ARG, CAPACITY (the index cannot take U more keys), HIP. */
 PARISKV_API int32_t pariskv_window_append(pariskv_window *w, const void *K_new,
                                           const void *V_new,
@@ -552,6 +556,18 @@ PARISKV_API int32_t pariskv_retrieve_sizes(const pariskv_index *index,
  * thresholds tau[7]) and its rotation scale fp32(1/sqrt(d)).  Host-only. */
 PARISKV_API int32_t pariskv_codebook(int32_t m, float *L, float *tau);
 PARISKV_API float pariskv_rot_scale(int32_t head_dim);
+
+/* The rotation's random diagonal D from a 64-bit seed, for callers that
+ * keep a seed rather than the signs ([TS] Core Algorithmic Innovations 1:
+ * one random rotation, implemented via SRHT, shared by keys and queries):
+ * signs[j] = -1 when bit 63 of the j-th output (j = 0 .. head_dim - 1) of
+ * SplitMix64 seeded with `seed` is set, else +1 (Steele, Lea and Flood,
+ * "Fast Splittable Pseudorandom Number Generators", OOPSLA 2014).  The
+ * result can be passed as pariskv_build_index's srht_signs.  Host-only.
+ *   signs   host int8 [head_dim], written.
+ * Errors: INVALID_ARG (null signs, head_dim < 1 or > 1024). */
+PARISKV_API int32_t pariskv_srht_signs_from_seed(uint64_t seed, int32_t head_dim,
+                                                 int8_t *signs);
 
 /* Human-readable text for a status code (static storage). */
 PARISKV_API const char *pariskv_status_string(int32_t status);

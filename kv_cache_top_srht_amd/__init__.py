@@ -100,6 +100,7 @@ def lib():
             "pariskv_retrieval_path": (i32, [P, i32]),
             "pariskv_codebook": (i32, [i32, P, P]),
             "pariskv_rot_scale": (C.c_float, [i32]),
+            "pariskv_srht_signs_from_seed": (i32, [C.c_uint64, i32, P]),
             "pariskv_status_string": (C.c_char_p, [i32]),
             "pariskv_sparse_attn_per_query_head": (i32, [P, P, P, i64, P, i32, i32, i32,
                                                          i32, i32, i32, C.c_float, P, P,
@@ -396,6 +397,14 @@ def pariskv_codebook(m: int):
 
 def pariskv_rot_scale(d: int) -> np.float32:
     return np.float32(lib().pariskv_rot_scale(d))
+
+
+def pariskv_srht_signs_from_seed(seed: int, d: int) -> np.ndarray:
+    """The rotation's signs (int8 +-1, [d]) from a 64-bit seed."""
+    out = np.zeros(d, np.int8)
+    _check(lib().pariskv_srht_signs_from_seed(int(seed) & (2 ** 64 - 1), int(d),
+                                              out.ctypes.data_as(C.c_void_p)))
+    return out
 
 
 # ------------------------------------------------------ convenience holder --

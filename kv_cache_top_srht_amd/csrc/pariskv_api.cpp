@@ -206,16 +206,14 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   hipStream_t st = (hipStream_t)stream;
   pariskv_index* mix = const_cast<pariskv_index*>(ix);
   mix->last = st;
-  // deferred appends: encoded by the query-prep kernel when they were
-  // appended on this stream, else first on their own stream
+  // deferred appends: encoded by this retrieval's first kernel, on its own
+  // stream, which the caller has ordered after the appended rows were
+  // written (whichever stream the append was issued on), so the scan that
+  // follows on this stream sees them
   pkv::AppendJob app;
   if (mix->pending.n > 0) {
-    if (mix->pending_stream == st) {
-      app = mix->pending;
-      mix->pending.n = 0;
-    } else if (int32_t rc = flush_pending(mix)) {
-      return rc;
-    }
+    app = mix->pending;
+    mix->pending.n = 0;
   }
   const int BH = (int)units_of(c);  // retrieval units
   const int udiv = unit_div_of(c);
@@ -682,22 +680,30 @@ int32_t pariskv_window_append(pariskv_window* w, const void* K_new, const void* 
   if (e != hipSuccess) return PARISKV_ERR_HIP;
   if (++w->u < w->U) return PARISKV_OK;
   // update buffer full: the U oldest local tokens [S + R, S + R + U) move to the
-  // retrieval region.  Their ring slots are contiguous (R and ring are
-  // multiples of U); their rows are copied to the far store and their keys
-  // encoded into the index now (the next token reuses the first slot).
-  const int64_t pos0 = w->S + w->R, slot0 = w->S + w->R % w->ring;
+  // retrieval region: their rows are copied to the far store and their keys
+  // encoded into the index now (the next token reuses the first slot).  Their
+  // ring slots start at S + R % ring and wrap to S at the end of the ring, so
+  // the copy and the encode run in at most two contiguous pieces.
+  const int64_t pos0 = w->S + w->R, r0 = w->R % w->ring;
+  const int64_t n1 = (w->U < w->ring - r0) ? w->U : w->ring - r0;
   const size_t far_pitch = (size_t)w->far_rows * rb;
-  e = hipMemcpy2DAsync(w->Kf + pos0 * rb, far_pitch, w->Kn + slot0 * rb, near_pitch, w->U * rb,
-                       BH, hipMemcpyDefault, st);
-  if (e == hipSuccess)
-    e = hipMemcpy2DAsync(w->Vf + pos0 * rb, far_pitch, w->Vn + slot0 * rb, near_pitch,
-                         w->U * rb, BH, hipMemcpyDefault, st);
-  if (e != hipSuccess) return PARISKV_ERR_HIP;
   if (int32_t rc = flush_pending(ix)) return rc;
-  e = pkv::launch_encode(m_of(&ix->cfg), ix->cfg.key_dtype, w->Kn + slot0 * rb, w->S + w->ring,
-                         ix->n, w->U, (int)BH, ix->cfg.capacity, ix->ids, ix->rec, ix->signs,
-                         ix->rot_c, st, pkv::EvPair{});
-  if (e != hipSuccess) return PARISKV_ERR_HIP;
+  for (int piece = 0; piece < 2; ++piece) {
+    const int64_t cnt = piece ? w->U - n1 : n1;
+    if (cnt == 0) continue;
+    const int64_t slot0 = w->S + (piece ? 0 : r0), pos = pos0 + (piece ? n1 : 0);
+    e = hipMemcpy2DAsync(w->Kf + pos * rb, far_pitch, w->Kn + slot0 * rb, near_pitch, cnt * rb,
+                         BH, hipMemcpyDefault, st);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(w->Vf + pos * rb, far_pitch, w->Vn + slot0 * rb, near_pitch,
+                           cnt * rb, BH, hipMemcpyDefault, st);
+    if (e == hipSuccess)
+      e = pkv::launch_encode(m_of(&ix->cfg), ix->cfg.key_dtype, w->Kn + slot0 * rb,
+                             w->S + w->ring, ix->n + (piece ? n1 : 0), cnt, (int)BH,
+                             ix->cfg.capacity, ix->ids, ix->rec, ix->signs, ix->rot_c, st,
+                             pkv::EvPair{});
+    if (e != hipSuccess) return PARISKV_ERR_HIP;
+  }
   ix->n += w->U;
   ix->last = st;
   w->R += w->U;
@@ -767,6 +773,21 @@ int32_t pariskv_codebook(int32_t m, float* L, float* tau) {
 }
 
 float pariskv_rot_scale(int32_t head_dim) { return head_dim > 0 ? rot_scale(head_dim) : 0.0f; }
+
+int32_t pariskv_srht_signs_from_seed(uint64_t seed, int32_t head_dim, int8_t* signs) {
+  if (!signs || head_dim < 1 || head_dim > 1024) return PARISKV_ERR_INVALID_ARG;
+  // SplitMix64: Weyl-sequence state, output mixed by two multiply rounds
+  constexpr uint64_t kGamma = 0x9e3779b97f4a7c15ull;
+  constexpr uint64_t kMul1 = 0xbf58476d1ce4e5b9ull, kMul2 = 0x94d049bb133111ebull;
+  for (int32_t j = 0; j < head_dim; ++j) {
+    uint64_t x = seed + kGamma * (uint64_t)(j + 1);
+    x = (x ^ (x >> 30)) * kMul1;
+    x = (x ^ (x >> 27)) * kMul2;
+    x ^= x >> 31;
+    signs[j] = (int8_t)(1 - 2 * (int)(x >> 63));
+  }
+  return PARISKV_OK;
+}
 
 const char* pariskv_status_string(int32_t s) {
   switch (s) {

@@ -55,6 +55,8 @@ def lib():
             "orc_codebook": (i32, [i32, P, P]),
             "orc_codebook_f32": (i32, [i32, P, P]),
             "orc_rot_scale": (f32, [i32]),
+            "orc_srht_signs": (i32, [C.c_uint64, i32, P]),
+            "orc_splitmix64": (i32, [C.c_uint64, i32, P]),
             "orc_rotate": (i32, [i32, P, P, P]),
             "orc_encode_keys": (i32, [i32, i32, P, i64, P, P, P, P]),
             "orc_query_prep": (i32, [i32, i32, i32, P, P, i32, P, P, P, P]),
@@ -117,6 +119,19 @@ def codebook_f32(m: int):
     t = np.zeros(7, np.float32)
     _ok(lib().orc_codebook_f32(m, _p(L), _p(t)))
     return L, t
+
+
+def srht_signs(seed: int, d: int) -> np.ndarray:
+    """The rotation's signs D from a seed (SplitMix64 top bits), int8 [d]."""
+    D = np.zeros(d, np.int8)
+    _ok(lib().orc_srht_signs(int(seed), int(d), _p(D)))
+    return D
+
+
+def splitmix64(seed: int, n: int) -> np.ndarray:
+    out = np.zeros(n, np.uint64)
+    _ok(lib().orc_splitmix64(int(seed), int(n), _p(out)))
+    return out
 
 
 def rot_scale(d: int) -> np.float32:

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <vector>
 
+#include "launch_stubs.h"
 #include "pariskv.h"
 
 namespace {
@@ -112,11 +113,91 @@ void run_index(const pariskv_config& c, int32_t k) {
   pariskv_index_destroy(ix);
 }
 
+// A window whose retrieval region R0 is not a multiple of the update buffer
+// U: promotions take ring rows that wrap past the ring's end.  Host buffers
+// stand in for the near and far stores (the copy stub copies host memory and
+// aborts on any access outside a registered buffer); every row carries its
+// (head, position) tag, so the far store and the encoded rows can be checked
+// position by position.
+void run_window_wrap() {
+  pariskv_config c = base_cfg();
+  c.capacity = 4096;
+  const int64_t S = c.n_sink, L = 64, U = 32, ring = L + U, N0 = 2013;
+  const int64_t R0 = N0 - S, BH = (int64_t)c.batch * c.n_kv_heads, d = 128;
+  EXPECT(R0 % U != 0 && R0 % ring + U > ring);
+  size_t ib = 0;
+  EXPECT(pariskv_index_bytes(&c, &ib) == PARISKV_OK);
+  std::vector<int8_t> signs(128, 1);
+  pariskv_index* ix = nullptr;
+  EXPECT(pariskv_build_index(&c, signs.data(), dev(1), ib, dev(2), c.capacity, N0, nullptr,
+                             &ix) == PARISKV_OK);
+  if (!ix) return;
+  auto tag = [&](uint16_t* row, int64_t h, int64_t p) {
+    row[0] = (uint16_t)h;
+    row[1] = (uint16_t)(p & 0xFFFF);
+    row[2] = (uint16_t)(p >> 16);
+  };
+  auto has_tag = [&](const uint16_t* row, int64_t h, int64_t p) {
+    return row[0] == (uint16_t)h && row[1] == (uint16_t)(p & 0xFFFF) &&
+           row[2] == (uint16_t)(p >> 16);
+  };
+  const int64_t nrows = S + ring;
+  std::vector<uint16_t> Kn(BH * nrows * d, 0xFFFF), Vn(Kn), Kf(BH * c.capacity * d, 0xFFFF),
+      Vf(Kf), Kx(BH * d), Vx(BH * d);
+  for (auto* v : {&Kn, &Vn, &Kf, &Vf, &Kx, &Vx}) stub_track(v->data(), v->size() * 2);
+  for (int64_t h = 0; h < BH; ++h) {
+    for (int64_t p = 0; p < S; ++p) tag(&Kn[(h * nrows + p) * d], h, p);
+    for (int64_t p = S + R0; p < S + R0 + L; ++p)
+      tag(&Kn[(h * nrows + S + (p - S) % ring) * d], h, p);
+  }
+  Vn = Kn;
+  pariskv_window* w = nullptr;
+  EXPECT(pariskv_window_create(ix, L, U, Kn.data(), Vn.data(), Kf.data(), Vf.data(), c.capacity,
+                               &w) == PARISKV_OK);
+  if (!w) return;
+  stub_clear_encodes();
+  int promotions = 0;
+  size_t seen = 0;
+  int64_t next = S + R0, pieces = 0;
+  for (int64_t t = 0; t < 100; ++t) {
+    const int64_t p = S + R0 + L + t;
+    for (int64_t h = 0; h < BH; ++h) tag(&Kx[h * d], h, p);
+    Vx = Kx;
+    EXPECT(pariskv_window_append(w, Kx.data(), Vx.data(), 1, nullptr) == PARISKV_OK);
+    int64_t nt = 0, R = 0, tail = 0;
+    EXPECT(pariskv_window_state(w, &nt, &R, &tail) == PARISKV_OK && nt == p + 1);
+    if (R == R0 + (promotions + 1) * U) ++promotions;
+    EXPECT(pariskv_index_size(ix) == S + R);
+    // encodes issued by this call: each reads its own tokens' ring rows
+    for (; seen < stub_encodes().size(); ++seen) {
+      const StubEncode& e = stub_encodes()[seen];
+      EXPECT(e.lo == next && e.rows_per_head == nrows);
+      const int64_t r0 = ((const uint16_t*)e.K - Kn.data()) / d;
+      for (int64_t h = 0; h < BH; ++h)
+        for (int64_t i = 0; i < e.n; ++i) EXPECT(has_tag(&Kn[(h * nrows + r0 + i) * d], h, e.lo + i));
+      next += e.n;
+      ++pieces;
+    }
+  }
+  EXPECT(promotions == 3);
+  EXPECT(next == S + R0 + 3 * U && pieces == 4);  // the first promotion in two pieces
+  // the far store holds positions [S + R0, S + R0 + 3U) of every head
+  for (int64_t h = 0; h < BH; ++h)
+    for (int64_t p = S + R0; p < S + R0 + 3 * U; ++p) {
+      EXPECT(has_tag(&Kf[(h * c.capacity + p) * d], h, p));
+      EXPECT(has_tag(&Vf[(h * c.capacity + p) * d], h, p));
+    }
+  pariskv_window_destroy(w);
+  pariskv_index_destroy(ix);
+  stub_untrack_all();
+}
+
 }  // namespace
 
 int main() {
   pariskv_config c = base_cfg();
   run_index(c, 1024);
+  run_window_wrap();
   c.n_subspaces = 32;  // subspaces of 4
   run_index(c, 300);
   c = base_cfg();

@@ -2,17 +2,79 @@
 // C-ABI sources (pariskv_api.cpp, si_api.cpp) build with g++ under the
 // address and undefined-behaviour sanitizers and their validation, layout,
 // handle and error paths run without a GPU.  Every launcher succeeds
-// without touching memory.  Test infrastructure only.
+// without touching memory.  Host buffers the driver registers with
+// stub_track() are checked: a 2-D copy (hipMemcpy2DAsync, replaced here by
+// a host memcpy) or an encode that reads rows of such a buffer must stay
+// inside it, and every encode is recorded.  Test infrastructure only.
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
 #include "codebook_tables.h"
+#include "launch_stubs.h"
 #include "pariskv_internal.h"
+
+namespace {
+struct Tracked {
+  const uint8_t* p;
+  size_t n;
+};
+std::vector<Tracked> g_tracked;
+std::vector<StubEncode> g_encodes;
+
+// the tracked buffer holding [p, p + n), or null when p is in none
+const Tracked* find_tracked(const void* p) {
+  const uint8_t* b = (const uint8_t*)p;
+  for (const Tracked& t : g_tracked)
+    if (b >= t.p && b < t.p + t.n) return &t;
+  return nullptr;
+}
+void check_range(const void* p, size_t n, const char* what) {
+  const Tracked* t = find_tracked(p);
+  if (!t) return;
+  if ((const uint8_t*)p + n > t->p + t->n) {
+    std::printf("out of bounds: %s reads/writes %zu bytes past its buffer\n", what,
+                (size_t)((const uint8_t*)p + n - (t->p + t->n)));
+    std::abort();
+  }
+}
+}  // namespace
+
+void stub_track(const void* p, size_t bytes) { g_tracked.push_back({(const uint8_t*)p, bytes}); }
+void stub_untrack_all() { g_tracked.clear(); }
+const std::vector<StubEncode>& stub_encodes() { return g_encodes; }
+void stub_clear_encodes() { g_encodes.clear(); }
+
+extern "C" hipError_t hipMemcpy2DAsync(void* dst, size_t dpitch, const void* src, size_t spitch,
+                                       size_t width, size_t height, hipMemcpyKind kind,
+                                       hipStream_t stream) {
+  (void)kind;
+  (void)stream;
+  if (height == 0 || width == 0) return hipSuccess;
+  if (!find_tracked(dst) || !find_tracked(src)) return hipErrorInvalidValue;
+  check_range(dst, (height - 1) * dpitch + width, "copy destination");
+  check_range(src, (height - 1) * spitch + width, "copy source");
+  for (size_t r = 0; r < height; ++r)
+    std::memmove((uint8_t*)dst + r * dpitch, (const uint8_t*)src + r * spitch, width);
+  return hipSuccess;
+}
 
 namespace pkv {
 
 hipError_t launch_encode(int m, int dtype, const void* K, int64_t rows_per_head, int64_t lo,
                          int64_t n, int BH, int64_t cap, uint8_t* ids, uint32_t* rec,
                          const SignMask& sg, float c, hipStream_t st, const EvPair& ev) {
+  const size_t rb = (dtype == 0 ? 2 : 4) * 128;  // d = 128 rows of bf16 or fp32
+  if (lo < 0 || n < 0 || lo + n > cap) {
+    std::printf("encode past the index capacity: [%lld, %lld) of %lld\n", (long long)lo,
+                (long long)(lo + n), (long long)cap);
+    std::abort();
+  }
+  if (n > 0) check_range(K, ((size_t)(BH - 1) * rows_per_head + n) * rb, "encode");
+  g_encodes.push_back({K, rows_per_head, lo, n});
   return hipSuccess;
 }
 

@@ -58,6 +58,18 @@ def test_rot_scale_matches_oracle(pk, orc):
         assert pk.pariskv_rot_scale(d) == orc.rot_scale(d)
 
 
+def test_seeded_signs_match_oracle(pk, orc):
+    """The library's seed -> signs helper and the oracle's own SplitMix64
+    give the same rotation diagonal (the generator itself is pinned by its
+    known answers in the oracle's tests)."""
+    for seed in (0, 1, 2 ** 63 + 12345, 2 ** 64 - 1):
+        for d in (1, 64, 128, 1024):
+            assert np.array_equal(pk.pariskv_srht_signs_from_seed(seed, d),
+                                  orc.srht_signs(seed, d))
+    with pytest.raises(Exception):
+        pk.pariskv_srht_signs_from_seed(1, 0)
+
+
 def test_sizes(pk):
     c = pk.make_config(capacity=1 << 20, batch=1, n_kv_heads=8, n_q_heads=32)
     # ids 16 B + a 128-byte record (codes 64 B + w 32 B) per key and head

@@ -24,14 +24,18 @@ def _gpu():
     need_gpu()
 
 
-@pytest.mark.parametrize("far", ["device", "host"])
-def test_window_sequence(orc, far):
+# (far store, prefill tokens N0).  With N0 = 2000 the retrieval region starts
+# at R0 = 1920, a multiple of the ring (96 slots), so every promotion takes
+# contiguous slots; with N0 = 2013, R0 = 1933 and the third promotion (step
+# 95) takes slots 77..95 and then 0..12 of the ring.
+@pytest.mark.parametrize("far,N0", [("device", 2000), ("host", 2000), ("device", 2013)])
+def test_window_sequence(orc, far, N0):
     S, L, U = 16, 64, 32
     B, Hkv, G, d = 1, 2, 4, 128
-    N0, steps, k = 2000, 100, 160
+    steps, k = 100, 160
     cap = N0 + steps + 64
     w = W("window", B, Hkv, Hkv * G, d, cap, "bf16", k=k, sinks=S, seed=61)
-    case("window S=%d L=%d U=%d far store in %s memory" % (S, L, U, far))
+    case("window S=%d L=%d U=%d N0=%d far store in %s memory" % (S, L, U, N0, far))
     lay = synth.make_layer(w, "cuda")
     K, V, Q = lay["K"], lay["V"], lay["Q"]        # logical rows, position p at row p
     BH = B * Hkv

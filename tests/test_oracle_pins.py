@@ -524,3 +524,20 @@ def test_tiny_workload_planted_keys_found(orc):
     exact = orc.exact_topk(Q, K, 0, 64)
     recall = len(set(exact.tolist()) & set(res["idx"].tolist())) / 64
     assert recall > 0.5
+
+
+def test_splitmix64_known_answers(orc):
+    """The generator behind seeded rotation signs against its published
+    known answers (tests/golden/splitmix64_known_answers.txt), and the signs
+    as the top bits of those outputs."""
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "splitmix64_known_answers.txt"))
+            if l.strip() and not l.startswith("#")]
+    for seed, i, hexv in rows:
+        out = orc.splitmix64(int(seed), int(i) + 1)
+        assert int(out[int(i)]) == int(hexv, 16)
+    D = orc.srht_signs(0, 3)
+    assert list(D) == [-1, 1, 1]          # top bits of e220..., 6e78..., 06c4...
+    # 4096 signs: a fair coin, and consecutive seeds give different draws
+    D = orc.srht_signs(7, 4096).astype(np.int64)
+    assert set(np.unique(D)) == {-1, 1} and abs(int(D.sum())) < 4 * 64
+    assert not np.array_equal(orc.srht_signs(7, 128), orc.srht_signs(8, 128))
