@@ -256,25 +256,43 @@ def main():
         step(t)
     torch.cuda.synchronize()
 
-    # timed region: K steps, captured as one HIP graph, replayed once
+    # timed region: exactly K distinct steps, split into R consecutive parts
+    # (R = min(10, K), sizes differing by at most one step); each part is
+    # captured as one HIP graph, and the graphs are replayed back to back
+    # between two synchronisations, with an event recorded between replays
+    # (outside the graphs), so that each part's per-step time is known
     E_of.clear()
     mode = "eager" if args.eager else "hip-graph"
-    g = None
+    R = max(1, min(10, K_steps))
+    part = [K_steps // R + (1 if r < K_steps % R else 0) for r in range(R)]
+    graphs = []
     if not args.eager:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
-            for t in range(K_steps):
-                step(W_steps + t)
+        t = W_steps
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                for _ in range(part[r]):
+                    step(t)
+                    t += 1
+            graphs.append(g)
         torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    if g is None:
-        for t in range(K_steps):
-            step(W_steps + t)
-    else:
-        g.replay()
+    t = W_steps
+    marks[0].record()
+    for r in range(R):
+        if graphs:
+            graphs[r].replay()
+        else:
+            for _ in range(part[r]):
+                step(t)
+                t += 1
+        marks[r + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    part_us = np.array([marks[r].elapsed_time(marks[r + 1]) * 1e3 / part[r]
+                        for r in range(R)])
     E_timed = list(E_of)
 
     # kernel durations: the next P steps launched with dispatch-stamped
@@ -402,6 +420,13 @@ def main():
             "unit": "GB/s", "algorithmic_bytes_per_launch": rerank_bytes,
             "avg_launch_us": rerank_us,
         },
+        "timed_step_us": {"parts": R, "steps_per_part": part,
+                          "median": float(np.median(part_us)),
+                          "p90": float(np.percentile(part_us, 90)),
+                          "mean": float(part_us.mean()),
+                          "note": "per-step time of each graph-replayed part of the "
+                                  "timed region, from events recorded between "
+                                  "replays"},
         "stage_us": stage_us,
         "kernel_timing": "%d further steps, each kernel bracketed by start/stop "
                          "events stamped by its own dispatch" % P,
@@ -486,12 +511,29 @@ def recall_at_k(pk, torch, np, w, layer, idx, cap):
     torch.cuda.synchronize()
     exact = exact_topk_rows(torch, w, lay, L.size)
     S, kp = w.sinks, w.k - w.sinks
-    rec = []
+    # candidate lists of the same retrieval (vote stage), for the ParisKV path
+    cand = None
+    if isinstance(L, pk.Layer):
+        cand = torch.from_numpy(pk.pariskv_debug_intermediate(
+            L.handle, L.k, L.ws, pk.DEBUG_CAND, len(exact))).to(idx.device).long()
+    rec, crec = [], []
     for bh, ex in enumerate(exact):
         got = idx[bh, S:].long()
         rec.append(float(torch.isin(got, ex).sum().item()) / kp)
+        if cand is not None:
+            crec.append(float(torch.isin(ex, cand[bh]).sum().item()) / kp)
+    stages = None
+    if crec:
+        # the exact top-k' kept by the vote stage (inside the candidate set),
+        # and the share of those the rerank then keeps in the top-k'
+        stages = {"candidate_recall_mean": float(np.mean(crec)),
+                  "candidate_recall_min": float(np.min(crec)),
+                  "rerank_keeps_mean": float(np.mean([r / c if c else 1.0
+                                                      for r, c in zip(rec, crec)])),
+                  "per_head": [{"recall": r, "candidate_recall": c}
+                               for r, c in zip(rec, crec)]}
     return {"k": w.k, "mean": float(np.mean(rec)), "min": float(np.min(rec)),
-            "heads": len(rec), "context": int(L.size),
+            "heads": len(rec), "context": int(L.size), "stages": stages,
             "reference": ("exact top-k' of each query head's logits <q_h, k_i>"
                           if w.per_query_head else
                           "exact top-k' of the group-summed logits sum_g <q_g, k_i>")
@@ -676,13 +718,20 @@ def cpu_baseline(w, lay, steps):
     t1 = time.perf_counter()
     one(0, 0)
     single = time.perf_counter() - t1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
     return {"value": keys / dt, "unit": "keys/s", "cores": nthreads,
+            "threads": nthreads, "host_cores": os.cpu_count() or 1,
+            "host_cores_usable": usable,
             "kind": "oracle",
             "us_per_step_per_layer": dt / steps * 1e6,
             "single_thread_us_per_head_step": single * 1e6,
             "sample": "all %d (batch, KV head) pairs of one %s layer, %d decode "
                       "steps (append + retrieve + attention), index prefill "
-                      "untimed" % (BH, w.name, steps)}
+                      "untimed; a thread per (batch, KV head), at most %d "
+                      "threads" % (BH, w.name, steps, nthreads)}
 
 
 if __name__ == "__main__":

@@ -40,6 +40,15 @@ def test_bench_json_line():
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-9
     cb = j["cpu_baseline"]
-    for key in ("value", "unit", "cores", "kind", "sample"):
+    for key in ("value", "unit", "cores", "threads", "host_cores", "kind", "sample"):
         assert key in cb, key
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    assert cb["threads"] == cb["cores"] and cb["host_cores"] == os.cpu_count()
+    # the timed region: 5 graph-replayed parts of one step, median and p90
+    ts = j["timed_step_us"]
+    assert ts["parts"] == 5 and sum(ts["steps_per_part"]) == 5
+    assert 0 < ts["median"] <= ts["p90"]
+    # recall split by stage: the vote stage's candidates, then the rerank
+    st = j["recall"]["stages"]
+    assert 0.0 <= st["candidate_recall_min"] <= st["candidate_recall_mean"] <= 1.0
+    assert j["recall"]["mean"] <= st["candidate_recall_mean"] + 1e-12
