@@ -210,6 +210,31 @@ PARISKV_API int32_t pariskv_retrieve_topk(const pariskv_index *index,
                                           void *ws, size_t ws_bytes,
                                           void *stream);
 
+/* Bytes of the library's own device scratch per GPU, used by
+ * pariskv_retrieve_topk_noalloc. */
+#define PARISKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): pariskv_retrieve_topk with the workspace taken from a
+ * library-owned device array of PARISKV_NOALLOC_SCRATCH_BYTES on the device
+ * current on the calling thread (the index's device).  The array is loaded
+ * with the library and held by each GPU it runs on until the process ends;
+ * its address is resolved on the first call on a device.  No hipMalloc,
+ * hipFree or other allocating call is made.  Every call on one GPU shares
+ * that GPU's array and leaves its contents behind (the retrieval needs none
+ * of it initialised), so calls that overlap on one GPU -- on different
+ * streams, or from different threads without ordering -- race and must not
+ * be issued.  Same arguments, outputs and errors as pariskv_retrieve_topk,
+ * plus WORKSPACE when pariskv_retrieve_workspace_bytes(k) for this index
+ * exceeds PARISKV_NOALLOC_SCRATCH_BYTES (the 1M-key x 8-head layer at
+ * k = 4096 needs about 25 MiB). */
+PARISKV_API int32_t pariskv_retrieve_topk_noalloc(const pariskv_index *index,
+                                                  const void *Q, int32_t k,
+                                                  int32_t *out_idx,
+                                                  float *out_est,
+                                                  void *stream);
+
 /* Same as pariskv_retrieve_topk, and times each stage's kernel: events
  * holds 2 * PARISKV_RETRIEVE_STAGES caller-created hipEvent_t (timing
  * enabled); events[2s] and events[2s+1] are stamped by the dispatch of stage

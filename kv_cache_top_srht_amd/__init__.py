@@ -17,6 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 SO_PATH = os.path.join(_PKG, "libpariskv.so")
 
 PARISKV_OK = 0
+(PARISKV_ERR_INVALID_ARG, PARISKV_ERR_UNSUPPORTED, PARISKV_ERR_CAPACITY,
+ PARISKV_ERR_WORKSPACE, PARISKV_ERR_HIP, PARISKV_ERR_NOMEM) = range(-1, -7, -1)
 PARISKV_DTYPE_BF16 = 0
 PARISKV_DTYPE_FP32 = 1
 PARISKV_RETRIEVE_STAGES = 6
@@ -24,6 +26,7 @@ PARISKV_RETRIEVE_STAGES = 6
 DEBUG_LUT, DEBUG_YQ, DEBUG_SCORES, DEBUG_CAND, DEBUG_EST, DEBUG_THRESH = range(6)
 # retrieval paths (pariskv_set_retrieval_path)
 PATH_AUTO, PATH_PIPELINE, PATH_SINGLE = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PARISKV_NOALLOC_SCRATCH_BYTES
 
 
 class PariskvError(RuntimeError):
@@ -85,6 +88,7 @@ def lib():
             "pariskv_index_size": (i64, [P]),
             "pariskv_index_destroy": (None, [P]),
             "pariskv_retrieve_topk": (i32, [P, P, i32, P, P, P, sz, P]),
+            "pariskv_retrieve_topk_noalloc": (i32, [P, P, i32, P, P, P]),
             "pariskv_retrieve_topk_profiled": (i32, [P, P, i32, P, P, P, sz, P,
                                                      C.POINTER(P)]),
             "pariskv_stage_name": (C.c_char_p, [i32]),
@@ -250,6 +254,11 @@ def pariskv_retrieve_topk(handle, Q, k, out_idx, out_est, ws, stream=None):
     _check(lib().pariskv_retrieve_topk(handle, _ptr(Q), int(k), _ptr(out_idx),
                                        _ptr(out_est), _ptr(ws), _nbytes(ws),
                                        _stream(stream)))
+
+
+def pariskv_retrieve_topk_noalloc(handle, Q, k, out_idx, out_est, stream=None):
+    _check(lib().pariskv_retrieve_topk_noalloc(handle, _ptr(Q), int(k), _ptr(out_idx),
+                                               _ptr(out_est), _stream(stream)))
 
 
 def pariskv_retrieve_topk_profiled(handle, Q, k, out_idx, out_est, ws, events,

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SO = os.path.join(PKG, "libpariskv.so")
-SOURCES = ["pariskv_kernels.hip", "si_kernels.hip", "pariskv_api.cpp", "si_api.cpp"]
+SOURCES = ["pariskv_kernels.hip", "si_kernels.hip", "scratch.hip", "pariskv_api.cpp",
+           "si_api.cpp"]
 HEADERS = ["pariskv_internal.h", "pariskv_device.h", "codebook_tables.h"]
 
 HIPCC_FLAGS = [

@@ -467,6 +467,18 @@ int32_t pariskv_retrieve_topk(const pariskv_index* ix, const void* Q, int32_t k,
   return retrieve_impl(ix, Q, k, out_idx, out_est, ws, ws_bytes, stream, nullptr);
 }
 
+int32_t pariskv_retrieve_topk_noalloc(const pariskv_index* ix, const void* Q, int32_t k,
+                                      int32_t* out_idx, float* out_est, void* stream) {
+  if (!ix || !Q || !out_idx) return PARISKV_ERR_INVALID_ARG;
+  size_t need = 0;
+  if (int32_t rc = pariskv_retrieve_workspace_bytes(&ix->cfg, k, &need)) return rc;
+  if (need > pkv::kNoAllocScratchBytes) return PARISKV_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (pkv::noalloc_scratch(&scratch) != hipSuccess) return PARISKV_ERR_HIP;
+  return retrieve_impl(ix, Q, k, out_idx, out_est, scratch, pkv::kNoAllocScratchBytes, stream,
+                       nullptr);
+}
+
 int32_t pariskv_retrieve_topk_profiled(const pariskv_index* ix, const void* Q, int32_t k,
                                        int32_t* out_idx, float* out_est, void* ws,
                                        size_t ws_bytes, void* stream, void** events) {

@@ -155,6 +155,12 @@ hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs
 hipError_t launch_attn_merge(int dtype, const float* part, int nch, int rows, void* out,
                              hipStream_t st,
                          const EvPair& ev);
+// Device scratch of the entry point that allocates nothing: a file-scope
+// array of this many bytes per GPU; noalloc_scratch() returns its address on
+// the current device (resolved once per device, then kept).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void** out);
+
 void codebook_m8(float* L, float* tau);
 void codebook_m4(float* L, float* tau);
 

@@ -68,6 +68,14 @@ void run_index(const pariskv_config& c, int32_t k) {
                                nullptr) == PARISKV_ERR_INVALID_ARG);
   EXPECT(pariskv_retrieve_topk(ix, dev(4), c.n_sink, (int32_t*)dev(5), nullptr, dev(7), ws,
                                nullptr) == PARISKV_ERR_INVALID_ARG);
+  // the entry point that allocates nothing: this workspace fits its scratch
+  EXPECT(ws <= PARISKV_NOALLOC_SCRATCH_BYTES);
+  EXPECT(pariskv_retrieve_topk_noalloc(ix, dev(4), k, (int32_t*)dev(5), (float*)dev(6),
+                                       nullptr) == PARISKV_OK);
+  EXPECT(pariskv_retrieve_topk_noalloc(ix, dev(4), c.n_sink, (int32_t*)dev(5), nullptr,
+                                       nullptr) == PARISKV_ERR_INVALID_ARG);
+  EXPECT(pariskv_retrieve_topk_noalloc(nullptr, dev(4), k, (int32_t*)dev(5), nullptr,
+                                       nullptr) == PARISKV_ERR_INVALID_ARG);
   int64_t E = 0, C = 0;
   EXPECT(pariskv_retrieve_sizes(ix, k, &E, &C) == PARISKV_OK && E == 50104 - c.n_sink && C > 0);
   // retrieval paths: the pipeline by default; the single kernel, when asked
@@ -203,6 +211,24 @@ int main() {
   c = base_cfg();
   c.per_query_head = 1;
   run_index(c, 512);
+  // a retrieval workspace beyond the no-alloc scratch is refused before any launch
+  {
+    pariskv_config big = base_cfg();
+    big.capacity = 2000000;  // 8 heads x 2M keys: about 45 MiB of workspace at k = 1024
+    size_t ib = 0, ws = 0;
+    EXPECT(pariskv_index_bytes(&big, &ib) == PARISKV_OK);
+    EXPECT(pariskv_retrieve_workspace_bytes(&big, 1024, &ws) == PARISKV_OK &&
+           ws > PARISKV_NOALLOC_SCRATCH_BYTES);
+    std::vector<int8_t> signs(128, 1);
+    pariskv_index* ix = nullptr;
+    EXPECT(pariskv_build_index(&big, signs.data(), dev(1), ib, dev(2), big.capacity, 5000,
+                               nullptr, &ix) == PARISKV_OK);
+    if (ix) {
+      EXPECT(pariskv_retrieve_topk_noalloc(ix, dev(4), 1024, (int32_t*)dev(5), nullptr,
+                                           nullptr) == PARISKV_ERR_WORKSPACE);
+      pariskv_index_destroy(ix);
+    }
+  }
   // configuration errors
   c = base_cfg();
   size_t n = 0;
