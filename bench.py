@@ -81,6 +81,10 @@ def parse():
     ap.add_argument("--si", action="store_true",
                     help="the Self-Indexing workload instead: sign-VQ index with "
                          "LUT-GEMV scores over every key, exact top-k, same attention")
+    ap.add_argument("--separate", action="store_true",
+                    help="run retrieval and attention as separate calls "
+                         "(pariskv_retrieve_topk + pariskv_sparse_attn) instead of "
+                         "pariskv_retrieve_attend")
     ap.add_argument("--uva", choices=["none", "v", "kv"], default="none",
                     help="keep V (v) or K and V (kv) of every layer in pinned host "
                          "memory, read by the kernels over the host link")
@@ -238,6 +242,16 @@ def main():
         n = L.size
         L.append(lay["K"][:, :, n:], 1, rows_per_head=cap)
         E_of.append(L.size - w.sinks)
+        if not args.si and not args.separate:
+            # retrieval and attention in one call; ev: the 6 retrieval stages,
+            # then the attention split and merge
+            if ev is None:
+                L.retrieve_attend(lay["Q"], lay["K"], lay["V"], idx, out, scale=scale)
+            else:
+                pk.pariskv_retrieve_attend_profiled(L.handle, lay["Q"], lay["K"], lay["V"],
+                                                    cap, w.k, scale, idx, None, out,
+                                                    L.attend_workspace(), ev[0:16])
+            return
         if ev is None:
             L.retrieve(lay["Q"], idx)
             L.attend(lay["Q"], lay["K"], lay["V"], idx, out, scale)
@@ -389,6 +403,9 @@ def main():
             "parallelism": "single GPU", "launch": mode,
             "retrieval_path": ("Self-Indexing kernels" if args.si else
                                "single kernel" if single else "multi-kernel pipeline"),
+            "attention": ("pariskv_retrieve_attend (one call)"
+                          if not (args.si or args.separate or args.window)
+                          else "separate calls"),
             "kv_placement": {"none": "HBM", "v": "V in pinned host memory",
                              "kv": "K and V in pinned host memory"}[args.uva],
             "window": ({"sinks": w.sinks, "local": win_L, "update_buffer": win_U,

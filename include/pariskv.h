@@ -249,6 +249,48 @@ PARISKV_API int32_t pariskv_retrieve_topk_profiled(
     const pariskv_index *index, const void *Q, int32_t k, int32_t *out_idx,
     float *out_est, void *ws, size_t ws_bytes, void *stream, void **events);
 
+/* ---------------------------------------------------------------------- */
+/* Retrieval and sparse attention in one call.                             */
+/* [TS] Core Algorithmic Innovations 2 (the two-stage retrieval) followed  */
+/* by System-Level Innovations 1: only the selected Top-k rows of K and V  */
+/* are fetched and attended.  The retrieval kernels, then the split-K      */
+/* attention and its merge, queued by one call on one stream.  The results */
+/* are those of pariskv_retrieve_topk followed by pariskv_sparse_attn (or  */
+/* its per-query-head form) with the same arguments: identical out_idx,    */
+/* out_est and attention output.                                           */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of the workspace pariskv_retrieve_attend needs for k. */
+PARISKV_API int32_t pariskv_retrieve_attend_workspace_bytes(const pariskv_config *cfg,
+                                                            int32_t k, size_t *bytes);
+
+/* Retrieval as pariskv_retrieve_topk (out_idx, optional out_est), then the
+ * attention of every query head over its selected rows into `out`.
+ *   K, V             device-accessible, key_dtype, [b][H_kv][kv_rows_per_head][d]
+ *                    (kv_rows_per_head >= the index size).
+ *   scale            softmax scale (normally 1/sqrt(d)), finite.
+ *   out              device, key_dtype, [b][H_q][d].
+ *   ws               >= pariskv_retrieve_attend_workspace_bytes(k), 256-byte
+ *                    aligned; contents need not be initialised.
+ * No host synchronisation and no allocation: capturable in a HIP graph.
+ * Errors: as pariskv_retrieve_topk, plus INVALID_ARG for null K, V or out, a
+ * non-finite scale or kv_rows_per_head below the index size. */
+PARISKV_API int32_t pariskv_retrieve_attend(const pariskv_index *index, const void *Q,
+                                            const void *K, const void *V,
+                                            int64_t kv_rows_per_head, int32_t k,
+                                            float scale, int32_t *out_idx,
+                                            float *out_est, void *out, void *ws,
+                                            size_t ws_bytes, void *stream);
+
+/* Same, timing its kernels: events holds 2 * PARISKV_RETRIEVE_STAGES + 4
+ * caller-created events, the retrieval stages as for
+ * pariskv_retrieve_topk_profiled, then the attention split and merge.
+ * Not for use under stream capture. */
+PARISKV_API int32_t pariskv_retrieve_attend_profiled(
+    const pariskv_index *index, const void *Q, const void *K, const void *V,
+    int64_t kv_rows_per_head, int32_t k, float scale, int32_t *out_idx, float *out_est,
+    void *out, void *ws, size_t ws_bytes, void *stream, void **events);
+
 /* Name of retrieval stage s, or NULL. */
 PARISKV_API const char *pariskv_stage_name(int32_t stage);
 

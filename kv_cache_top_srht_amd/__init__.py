@@ -89,6 +89,11 @@ def lib():
             "pariskv_index_destroy": (None, [P]),
             "pariskv_retrieve_topk": (i32, [P, P, i32, P, P, P, sz, P]),
             "pariskv_retrieve_topk_noalloc": (i32, [P, P, i32, P, P, P]),
+            "pariskv_retrieve_attend_workspace_bytes": (i32, [cfgp, i32, C.POINTER(sz)]),
+            "pariskv_retrieve_attend": (i32, [P, P, P, P, i64, i32, C.c_float, P, P, P, P, sz,
+                                              P]),
+            "pariskv_retrieve_attend_profiled": (i32, [P, P, P, P, i64, i32, C.c_float, P, P,
+                                                       P, P, sz, P, P]),
             "pariskv_retrieve_topk_profiled": (i32, [P, P, i32, P, P, P, sz, P,
                                                      C.POINTER(P)]),
             "pariskv_stage_name": (C.c_char_p, [i32]),
@@ -254,6 +259,28 @@ def pariskv_retrieve_topk(handle, Q, k, out_idx, out_est, ws, stream=None):
     _check(lib().pariskv_retrieve_topk(handle, _ptr(Q), int(k), _ptr(out_idx),
                                        _ptr(out_est), _ptr(ws), _nbytes(ws),
                                        _stream(stream)))
+
+
+def pariskv_retrieve_attend_workspace_bytes(cfg, k) -> int:
+    n = C.c_size_t(0)
+    _check(lib().pariskv_retrieve_attend_workspace_bytes(C.byref(cfg), int(k), C.byref(n)))
+    return n.value
+
+
+def pariskv_retrieve_attend(handle, Q, K, V, kv_rows_per_head, k, scale, out_idx, out_est,
+                            out, ws, stream=None):
+    _check(lib().pariskv_retrieve_attend(handle, _ptr(Q), _ptr(K), _ptr(V),
+                                         int(kv_rows_per_head), int(k), float(scale),
+                                         _ptr(out_idx), _ptr(out_est), _ptr(out), _ptr(ws),
+                                         _nbytes(ws), _stream(stream)))
+
+
+def pariskv_retrieve_attend_profiled(handle, Q, K, V, kv_rows_per_head, k, scale, out_idx,
+                                     out_est, out, ws, events, stream=None):
+    _check(lib().pariskv_retrieve_attend_profiled(
+        handle, _ptr(Q), _ptr(K), _ptr(V), int(kv_rows_per_head), int(k), float(scale),
+        _ptr(out_idx), _ptr(out_est), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream),
+        _events(events)))
 
 
 def pariskv_retrieve_topk_noalloc(handle, Q, k, out_idx, out_est, stream=None):
@@ -461,6 +488,22 @@ class Layer:
     def retrieve(self, Q, out_idx, out_est=None, stream=None):
         pariskv_retrieve_topk(self.handle, Q, self.k, out_idx, out_est, self.ws,
                               stream)
+
+    def attend_workspace(self):
+        """The workspace of retrieve_attend (allocated on first use)."""
+        import torch
+        if getattr(self, "ra_ws", None) is None:
+            self.ra_ws = torch.empty(pariskv_retrieve_attend_workspace_bytes(self.cfg, self.k),
+                                     dtype=torch.uint8, device=self.ws.device)
+        return self.ra_ws
+
+    def retrieve_attend(self, Q, K, V, out_idx, out, out_est=None, scale=None, stream=None):
+        """Retrieval and the attention over the selected rows in one call."""
+        self.attend_workspace()
+        c = self.cfg
+        pariskv_retrieve_attend(self.handle, Q, K, V, K.shape[2], self.k,
+                                scale if scale is not None else c.head_dim ** -0.5,
+                                out_idx, out_est, out, self.ra_ws, stream)
 
     def attend(self, Q, K, V, idx, out, scale=None, stream=None):
         c = self.cfg

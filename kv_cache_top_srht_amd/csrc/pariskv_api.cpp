@@ -163,6 +163,26 @@ int pick_kpt(int64_t E, int64_t BH) {
 
 float rot_scale(int d) { return (float)(1.0L / std::sqrt((long double)d)); }
 
+// Split-K partial slots per query head of a retrieval + attention: the
+// attention's 64-row chunks.
+int64_t attend_part_chunks(int64_t k) { return ceil_div(k, 64); }
+size_t attend_part_bytes(const pariskv_config* c, int64_t k) {
+  return align_up((size_t)c->batch * c->n_q_heads * attend_part_chunks(k) * pkv::kPartStride * 4,
+                  kAlign);
+}
+
+// Attention after a retrieval: K, V ([kv heads][rows][d], key_dtype), the
+// output [b][H_q][d] and the split-K partial buffer.
+struct AttnSpec {
+  const void* K = nullptr;
+  const void* V = nullptr;
+  int64_t rows = 0;
+  float scale = 0.0f;
+  void* out = nullptr;
+  float* part = nullptr;
+  int64_t part_chunks = 0;  // partial slots per query head
+};
+
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? PARISKV_OK : PARISKV_ERR_HIP; }
 
 // Encodes deferred appended keys now, on the stream they were appended on.
@@ -188,8 +208,38 @@ int32_t choose_path(const pariskv_index* ix, int64_t C) {
   return fits ? PARISKV_PATH_SINGLE : PARISKV_ERR_UNSUPPORTED;
 }
 
+int32_t attn_core(const void* Q, const pkv::AttnRows& rs, const int32_t* idx, int32_t k,
+                  int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                  int32_t dtype, float scale, void* out, void* ws, size_t ws_bytes, void* stream,
+                  void** events);
+
+// Split-K attention over the k selected rows of every unit, with the partial
+// buffer of a retrieval + attention call; events (optional) as
+// retrieve_impl's, the attention pairs after the retrieval stages.
+int32_t attend_selected(const pariskv_index* ix, const void* Q, int32_t k, const int32_t* idx,
+                        const AttnSpec& att, hipStream_t st, void** events) {
+  const pariskv_config* c = &ix->cfg;
+  pkv::AttnRows rs;
+  rs.K = att.K;
+  rs.V = att.V;
+  rs.rows = att.rows;
+  rs.K_near = att.K;
+  rs.V_near = att.V;
+  rs.near_rows = att.rows;
+  rs.unit_div = unit_div_of(c);
+  const int Hu = c->per_query_head ? c->n_q_heads : c->n_kv_heads;
+  // the partial buffer as the workspace reserves it (256-byte aligned size)
+  const size_t bytes =
+      align_up((size_t)c->batch * c->n_q_heads * att.part_chunks * pkv::kPartStride * 4, kAlign);
+  return attn_core(Q, rs, idx, k, c->batch, c->n_q_heads, Hu, c->head_dim, c->key_dtype,
+                   att.scale, att.out, att.part, bytes, st,
+                   events ? events + 2 * PARISKV_RETRIEVE_STAGES : nullptr);
+}
+
+// events: 2 per retrieval stage; with attention 4 more (split, merge)
 int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t* out_idx,
-                      float* out_est, void* ws, size_t ws_bytes, void* stream, void** events) {
+                      float* out_est, void* ws, size_t ws_bytes, void* stream, void** events,
+                      const AttnSpec* att = nullptr) {
   if (!ix || !Q || !out_idx || !ws) return PARISKV_ERR_INVALID_ARG;
   const pariskv_config* c = &ix->cfg;
   const int64_t N = ix->n, S = c->n_sink;
@@ -260,10 +310,12 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
       if (p.start && (e = hipEventRecord(p.start, st)) != hipSuccess) return hip_status(e);
       if (p.stop && (e = hipEventRecord(p.stop, st)) != hipSuccess) return hip_status(e);
     }
-    return hip_status(pkv::launch_retrieve_small(
+    e = pkv::launch_retrieve_small(
         m_of(c), c->key_dtype, Q, BH, units_per_batch, G, ix->signs, ix->rot_c, c->rho, tw, app,
         ix->ids, ix->rec, c->capacity, S, E, C, (int)kp, k, L.nbins, lut, yq, scores, L.Epad,
-        meta, cand, est, L.cstride, out_idx, out_est, st, ev(1)));
+        meta, cand, est, L.cstride, out_idx, out_est, st, ev(1));
+    if (e != hipSuccess || !att) return hip_status(e);
+    return attend_selected(ix, Q, k, out_idx, *att, st, events);
   }
   e = pkv::launch_qprep(m_of(c), c->key_dtype, Q, BH, units_per_batch, G, ix->signs, ix->rot_c,
                         c->rho, tw, lut, yq, ptab, app, udiv, st, ev(0));
@@ -292,7 +344,8 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
                        (int)L.nchunks_max, nch, range, rows, tkmeta, sorted, out_idx, out_est, st,
                        ev(4), ev(5));
   if (e != hipSuccess) return hip_status(e);
-  return PARISKV_OK;
+  if (!att) return PARISKV_OK;
+  return attend_selected(ix, Q, k, out_idx, *att, st, events);
 }
 
 // Split-K attention over k listed rows plus rs.tail_n tail rows.
@@ -465,6 +518,55 @@ void pariskv_index_destroy(pariskv_index* ix) {
 int32_t pariskv_retrieve_topk(const pariskv_index* ix, const void* Q, int32_t k, int32_t* out_idx,
                               float* out_est, void* ws, size_t ws_bytes, void* stream) {
   return retrieve_impl(ix, Q, k, out_idx, out_est, ws, ws_bytes, stream, nullptr);
+}
+
+int32_t pariskv_retrieve_attend_workspace_bytes(const pariskv_config* cfg, int32_t k,
+                                                size_t* bytes) {
+  size_t r = 0;
+  if (int32_t rc = pariskv_retrieve_workspace_bytes(cfg, k, &r)) return rc;
+  *bytes = align_up(r, kAlign) + align_up(attend_part_bytes(cfg, k), kAlign);
+  return PARISKV_OK;
+}
+
+static int32_t retrieve_attend_impl(const pariskv_index* ix, const void* Q, const void* K,
+                                    const void* V, int64_t kv_rows_per_head, int32_t k,
+                                    float scale, int32_t* out_idx, float* out_est, void* out,
+                                    void* ws, size_t ws_bytes, void* stream, void** events) {
+  if (!ix || !Q || !K || !V || !out || !out_idx || !ws) return PARISKV_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || kv_rows_per_head < ix->n) return PARISKV_ERR_INVALID_ARG;
+  const pariskv_config* c = &ix->cfg;
+  size_t need = 0;
+  if (int32_t rc = pariskv_retrieve_attend_workspace_bytes(c, k, &need)) return rc;
+  if (ws_bytes < need) return PARISKV_ERR_WORKSPACE;
+  AttnSpec att;
+  att.K = K;
+  att.V = V;
+  att.rows = kv_rows_per_head;
+  att.scale = scale;
+  att.out = out;
+  att.part = (float*)((uint8_t*)ws + align_up(ws_layout(c, k).total, kAlign));
+  att.part_chunks = attend_part_chunks(k);
+  return retrieve_impl(ix, Q, k, out_idx, out_est, ws, ws_bytes, stream, events, &att);
+}
+
+int32_t pariskv_retrieve_attend(const pariskv_index* ix, const void* Q, const void* K,
+                                const void* V, int64_t kv_rows_per_head, int32_t k, float scale,
+                                int32_t* out_idx, float* out_est, void* out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return retrieve_attend_impl(ix, Q, K, V, kv_rows_per_head, k, scale, out_idx, out_est, out, ws,
+                              ws_bytes, stream, nullptr);
+}
+
+int32_t pariskv_retrieve_attend_profiled(const pariskv_index* ix, const void* Q, const void* K,
+                                         const void* V, int64_t kv_rows_per_head, int32_t k,
+                                         float scale, int32_t* out_idx, float* out_est,
+                                         void* out, void* ws, size_t ws_bytes, void* stream,
+                                         void** events) {
+  if (!events) return PARISKV_ERR_INVALID_ARG;
+  for (int s = 0; s < 2 * PARISKV_RETRIEVE_STAGES + 4; ++s)
+    if (!events[s]) return PARISKV_ERR_INVALID_ARG;
+  return retrieve_attend_impl(ix, Q, K, V, kv_rows_per_head, k, scale, out_idx, out_est, out, ws,
+                              ws_bytes, stream, events);
 }
 
 int32_t pariskv_retrieve_topk_noalloc(const pariskv_index* ix, const void* Q, int32_t k,

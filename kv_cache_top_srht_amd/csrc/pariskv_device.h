@@ -90,7 +90,8 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 template <int NT>
 __device__ __forceinline__ uint2 block_exscan2(uint2 v, uint2* s_warp, uint2& total) {
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // the wave index as a scalar, so the per-wave tests below are scalar
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t ix = wave_incl_scan(v.x), iy = wave_incl_scan(v.y);
   if (lane == 63) s_warp[wv] = make_uint2(ix, iy);
   __syncthreads();
@@ -112,7 +113,7 @@ __device__ __forceinline__ uint2 block_exscan2(uint2 v, uint2* s_warp, uint2& to
 template <int NT>
 __device__ __forceinline__ uint2 block_exscan_packed(uint2 v, uint2* s_warp, uint2& total) {
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t ix = wave_incl_scan(v.x), iy = wave_incl_scan(v.y);
   if (lane == 63) s_warp[wv] = make_uint2(ix, iy);
   __syncthreads();
