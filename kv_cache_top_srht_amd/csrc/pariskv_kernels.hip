@@ -312,37 +312,38 @@ __device__ __forceinline__ uint32_t vote_table_word(const float* s_yq, int s, in
   return lv[0] | (lv[1] << 8) | (lv[2] << 16) | (lv[3] << 24);
 }
 
+// One 64-thread block per (retrieval unit, vote-table row s): its 16 lanes
+// 0..15 form the unit's mean query and rotate it (every block of the unit
+// the same fp32 operations, so the same yq), then the block writes row s of
+// the vote table, the product-table entries of coordinates 8 s .. 8 s + 7
+// and (lanes s) those 8 coordinates of yq.  Short blocks that start at once
+// on idle CUs, rather than a long one per unit.
 template <typename T, int G, int M>
-__global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_kv_heads,
-                                                float invG, SignMask sg, float c, int rho, Tiers tw,
-                                                uint8_t* __restrict__ lut_out, float* __restrict__ yq_out,
-                                                float* __restrict__ ptab_out, AppendJob app,
-                                                int unit_div, int n_units) {
-  // one block per retrieval unit: a (b, KV head), or a (b, query head) with
-  // unit_div = G units per KV head (then G = 1 here and n_kv_heads counts
-  // units per batch entry); blocks n_units.. encode appended keys
-  const int bh = blockIdx.x;
+__global__ __launch_bounds__(64) void k_qprep(const T* __restrict__ Q, int n_kv_heads,
+                                              float invG, SignMask sg, float c, int rho, Tiers tw,
+                                              uint8_t* __restrict__ lut_out, float* __restrict__ yq_out,
+                                              float* __restrict__ ptab_out, AppendJob app,
+                                              int unit_div, int n_units) {
+  // blocks 16 u + s: retrieval unit u, a (b, KV head), or a (b, query head)
+  // with unit_div = G units per KV head (then G = 1 here and n_kv_heads
+  // counts units per batch entry); blocks 16 n_units.. encode appended keys
+  const int blk = blockIdx.x;
   const int tid = threadIdx.x;
-  if (bh >= n_units) {
+  if (blk >= 16 * n_units) {
     // blocks past the units encode the keys appended since the last
-    // retrieval (16 lanes per (KV head, key)), so the vote scan sees them
-    const int pair = (bh - n_units) * 64 + (tid >> 4);
+    // retrieval (16 lanes per (KV head, key), 4 per block), so the vote scan
+    // sees them
+    const int pair = (blk - 16 * n_units) * 4 + (tid >> 4);
     const int kvh = pair / app.n, r = pair - kvh * app.n;
     if (kvh < n_units / unit_div)
       encode_key<T, M>((const T*)app.K, app.rows_per_head, kvh, r, app.lo + r, app.cap, app.ids,
                        app.rec, sg, c, tid & 15);
     return;
   }
+  const int bh = blk >> 4, s = blk & 15;
   const int b = bh / n_kv_heads, h = bh - b * n_kv_heads;
   const int Hq = n_kv_heads * G;
   __shared__ float s_yq[128];
-  // the codebook levels in LDS for the product table (uniform loads here; a
-  // per-lane index into the constant array would be a vector memory load)
-  __shared__ float s_lv[8];
-  if (tid == 0) {
-#pragma unroll
-    for (int l = 0; l < 8; ++l) s_lv[l] = cb_level<M>(l);
-  }
   if (tid < 16) {
     const int sub = tid;
     // all G query rows are loaded at once, then summed in head order
@@ -362,21 +363,25 @@ __global__ __launch_bounds__(1024) void k_qprep(const T* __restrict__ Q, int n_k
     srht16(x, sign_byte_of(sg, sub), sub, c);
 #pragma unroll
     for (int j = 0; j < 8; ++j) s_yq[sub * 8 + j] = x[j];
-    reinterpret_cast<float4*>(yq_out + (int64_t)bh * 128 + sub * 8)[0] =
-        make_float4(x[0], x[1], x[2], x[3]);
-    reinterpret_cast<float4*>(yq_out + (int64_t)bh * 128 + sub * 8)[1] =
-        make_float4(x[4], x[5], x[6], x[7]);
+    if (sub == s) {
+      reinterpret_cast<float4*>(yq_out + (int64_t)bh * 128 + sub * 8)[0] =
+          make_float4(x[0], x[1], x[2], x[3]);
+      reinterpret_cast<float4*>(yq_out + (int64_t)bh * 128 + sub * 8)[1] =
+          make_float4(x[4], x[5], x[6], x[7]);
+    }
   }
   __syncthreads();
   // product table for the rerank: ptab[j][code] = fl(+-L[code & 7] yq_j), the
-  // sign bit (code & 8) negating the product exactly
-  for (int e = tid; e < 2048; e += 1024) {
-    const float pr = s_lv[e & 7] * s_yq[e >> 4];
+  // sign bit (code & 8) negating the product exactly; entries 128 s ..
+  // 128 s + 127 are coordinates 8 s .. 8 s + 7
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = 128 * s + tid + 64 * i;
+    const float pr = cb_level<M>(e & 7) * s_yq[e >> 4];
     ptab_out[(int64_t)bh * 2048 + e] = (e & 8) ? -pr : pr;
   }
-  const int s = tid >> 6, l = tid & 63;
-  reinterpret_cast<uint32_t*>(lut_out + ((int64_t)bh * 16 + s) * 256)[l] =
-      vote_table_word<M>(s_yq, s, l, rho, tw);
+  reinterpret_cast<uint32_t*>(lut_out + ((int64_t)bh * 16 + s) * 256)[tid] =
+      vote_table_word<M>(s_yq, s, tid, rho, tw);
 }
 
 // ---------------------------------------------------------------------------
@@ -2662,11 +2667,11 @@ static hipError_t launch_qprep_m(int dtype, const void* Q, int BH, int n_kv_head
                                  uint8_t* lut, float* yq, float* ptab, const AppendJob& app,
                                  int unit_div, hipStream_t st, const EvPair& ev) {
   const float invG = 1.0f / (float)G;
-  // encode blocks: 64 (KV head, key) pairs each
-  const int nenc = app.n > 0 ? (int)(((int64_t)(BH / unit_div) * app.n + 63) / 64) : 0;
+  // encode blocks: 4 (KV head, key) pairs each
+  const int nenc = app.n > 0 ? (int)(((int64_t)(BH / unit_div) * app.n + 3) / 4) : 0;
 #define PKV_QP(T, GG)                                                                           \
-  return launch(k_qprep<T, GG, M>, dim3(BH + nenc), dim3(1024), st, ev, (const T*)Q, n_kv_heads, \
-                invG, sg, c, rho, tw, lut, yq, ptab, app, unit_div, BH)
+  return launch(k_qprep<T, GG, M>, dim3(16 * BH + nenc), dim3(64), st, ev, (const T*)Q,         \
+                n_kv_heads, invG, sg, c, rho, tw, lut, yq, ptab, app, unit_div, BH)
   if (dtype == 0) {
     switch (G) {
       case 1: PKV_QP(uint16_t, 1);
