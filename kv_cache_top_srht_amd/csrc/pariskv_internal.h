@@ -131,6 +131,11 @@ constexpr int kTinyCands = 2048;
 constexpr int kTopkFewSlices = 16;
 // split-K attention partial per (query head, chunk): o[128], m, l, 2 unused
 constexpr int kPartStride = 132;
+// rows per lane of a split-attention block (16 row slots), and the selected
+// rows of one block: one split-K partial per query head and chunk of
+// kAttnChunkRows rows
+constexpr int kAttnRowsPerLane = 2;
+constexpr int kAttnChunkRows = 16 * kAttnRowsPerLane;
 // Where attention rows come from.  Listed positions p (from idx) are read
 // from the near store when p < n_near_head, else from the far store; the
 // tail_n rows after the list are positions tail_lo + t, read from the near

@@ -2423,9 +2423,9 @@ __global__ __launch_bounds__(1024) void k_retrieve_tiny(
 
 // ---------------------------------------------------------------------------
 // K7 split-K sparse attention ([TS] Problem Statement; System-Level
-// Innovations 1: only the selected rows are fetched).  Block = 64 selected
-// rows of one (b, h); 16 lanes per row (16 B of K and of V per lane), 16 row
-// slots x 4 rows.  The G query heads of the KV head are held in registers
+// Innovations 1: only the selected rows are fetched).  Block = kAttnChunkRows
+// (32) selected rows of one (b, h); 16 lanes per row (16 B of K and of V per
+// lane), 16 row slots x kAttnRowsPerLane rows.  The G query heads of the KV head are held in registers
 // (pre-multiplied by scale * log2 e), logits summed across the 16 lanes of a
 // row with DPP, softmax statistics per slot; the 16 slots are combined in
 // LDS (wave 0, one row of 16 lanes per query head, forms each slot's factor
@@ -2457,6 +2457,7 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
                                                     const int32_t* __restrict__ idx, int k,
                                                     int n_kv_heads, float qscale,
                                                     float* __restrict__ part, int nch) {
+  constexpr int RPL = kAttnRowsPerLane;
   const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   const int b = bh / n_kv_heads, h = bh - b * n_kv_heads;
   const int Hq = n_kv_heads * G;
@@ -2470,11 +2471,11 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
   // positions tail_lo + (r - k), in the near store's ring
   const int n_rows = k + rs.tail_n;
   const int32_t* ib = idx + (int64_t)bh * k;
-  int64_t row[4];
-  bool valid[4], near[4];
+  int64_t row[RPL];
+  bool valid[RPL], near[RPL];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int r = chunk * 64 + slot + 16 * it;
+  for (int it = 0; it < RPL; ++it) {
+    const int r = chunk * kAttnChunkRows + slot + 16 * it;
     valid[it] = r < n_rows;
     const bool listed = r < k;
     const int64_t p = listed ? (int64_t)ib[r < k ? r : k - 1]  // unconditional load
@@ -2500,15 +2501,15 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
   const T* Vf = (const T*)rs.V + ((int64_t)kvh * rs.rows << 7) + sub * 8;
   const T* Kn = (const T*)rs.K_near + ((int64_t)kvh * rs.near_rows << 7) + sub * 8;
   const T* Vn = (const T*)rs.V_near + ((int64_t)kvh * rs.near_rows << 7) + sub * 8;
-  float kx[4][8], vx[4][8];
+  float kx[RPL][8], vx[RPL][8];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
+  for (int it = 0; it < RPL; ++it) {
     load8_stream((near[it] ? Kn : Kf) + (row[it] << 7), kx[it]);
     load8_stream((near[it] ? Vn : Vf) + (row[it] << 7), vx[it]);
   }
-  float lg[4][G];
+  float lg[RPL][G];
 #pragma unroll
-  for (int it = 0; it < 4; ++it)
+  for (int it = 0; it < RPL; ++it)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float sdot = 0.0f;
@@ -2521,11 +2522,11 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
   for (int g = 0; g < G; ++g) {
     float m = lg[0][g];
 #pragma unroll
-    for (int it = 1; it < 4; ++it) m = fmaxf(m, lg[it][g]);
+    for (int it = 1; it < RPL; ++it) m = fmaxf(m, lg[it][g]);
     float l = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (m != -INFINITY) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
+      for (int it = 0; it < RPL; ++it) {
         const float pw = exp2f(lg[it][g] - m);
         l += pw;
 #pragma unroll
@@ -2561,75 +2562,76 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
 }
 
 // K8 log-sum-exp merge of the split-K partials -> output row per query head.
-// One block per (b, query head).  Partials are staged in LDS 64 chunks at a
-// time (one round of 16-byte loads); wave 0 forms the tile's maximum and
-// each chunk's factor exp2(m_c - M) once, then threads 0..127 combine the
-// chunks for their output element in chunk order, rescaling by the running
-// maximum across tiles.
+// Four blocks per (b, query head), block q for output coordinates 32 q ..
+// 32 q + 31: thread (g = tid / 32, j = tid % 32) takes chunks g, g + 8, ...
+// of coordinate 32 q + j, up to 16 of them (m, l and o) loaded in one round;
+// the block's maximum M by wave reductions, then each thread's sum of
+// exp2(m_c - M) o_c and exp2(m_c - M) l_c over its chunks (rescaled by the
+// running maximum from one round of 16 chunks to the next), and the 8 chunk
+// groups added in group order.
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part, int nch,
                                                     T* __restrict__ out) {
-  constexpr int R4 = kPartStride / 4;  // float4 per partial record
-  constexpr int TILE = 64;
-  constexpr int NLD = (TILE * R4 + 255) / 256;
-  const int bq = blockIdx.x, tid = threadIdx.x;
+  constexpr int NB = 16;
+  const int bq = blockIdx.x, q = blockIdx.y, tid = threadIdx.x;
+  const int j = tid & 31, g = tid >> 5, lane = tid & 63, wv = tid >> 6;
+  const int d = 32 * q + j;
   const float* pp = part + (int64_t)bq * nch * kPartStride;
-  __shared__ float4 s_p4[TILE * R4];
-  __shared__ float s_f[TILE], s_m[1];
-  const float* s_p = reinterpret_cast<const float*>(s_p4);
-  float o = 0.0f, l = 0.0f, M = -INFINITY;
-  for (int t0 = 0; t0 < nch; t0 += TILE) {
-    const int nt = min(TILE, nch - t0);
-    const int n4 = nt * R4;
-    const float4* src = reinterpret_cast<const float4*>(pp + (int64_t)t0 * kPartStride);
-    float4 v[NLD];
+  __shared__ float s_w[4], s_a[8][32], s_l[8];
+  float M = -INFINITY, acc = 0.0f, lac = 0.0f;
+  for (int c0 = 0; c0 < nch; c0 += 8 * NB) {
+    float mv[NB], lv[NB], ov[NB];
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int i = tid + 256 * u;
-      v[u] = (i < n4) ? src[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int u = 0; u < NB; ++u) {
+      const int c = c0 + g + 8 * u;
+      const int cc = c < nch ? c : nch - 1;  // in the buffer; masked below
+      const float* pc = pp + (int64_t)cc * kPartStride;
+      mv[u] = pc[128];
+      lv[u] = pc[129];
+      ov[u] = pc[d];
+      if (c >= nch) mv[u] = -INFINITY;
     }
-    __syncthreads();  // the previous tile has been consumed
+    float bm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int i = tid + 256 * u;
-      if (i < n4) s_p4[i] = v[u];
-    }
+    for (int u = 0; u < NB; ++u) bm = fmaxf(bm, mv[u]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
+    __syncthreads();  // s_w of the previous batch has been read
+    if (lane == 0) s_w[wv] = bm;
     __syncthreads();
-    if (tid < 64) {
-      // lane c: chunk c's maximum; the tile's by a wave reduction
-      const float mc = tid < nt ? s_p[tid * kPartStride + 128] : -INFINITY;
-      float tm = mc;
+    bm = fmaxf(fmaxf(s_w[0], s_w[1]), fmaxf(s_w[2], s_w[3]));
+    const float Mn = fmaxf(M, bm);
+    if (Mn != -INFINITY) {
+      const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+      acc *= r;
+      lac *= r;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) tm = fmaxf(tm, __shfl_xor(tm, off));
-      const float Mn = fmaxf(M, tm);
-      if (tid < nt) s_f[tid] = (Mn == -INFINITY || mc == -INFINITY) ? 0.0f : exp2f(mc - Mn);
-      if (tid == 0) s_m[0] = Mn;
-    }
-    __syncthreads();
-    if (tid < 128) {
-      const float Mn = s_m[0];
-      if (Mn != -INFINITY) {
-        const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
-        o *= r;
-        l *= r;
-        M = Mn;
-        for (int c = 0; c < nt; ++c) {
-          const float f = s_f[c];
-          o = __builtin_fmaf(f, s_p[c * kPartStride + tid], o);
-          l = __builtin_fmaf(f, s_p[c * kPartStride + 129], l);
-        }
+      for (int u = 0; u < NB; ++u) {
+        const float f = (mv[u] == -INFINITY) ? 0.0f : exp2f(mv[u] - Mn);
+        acc = __builtin_fmaf(f, ov[u], acc);
+        lac = __builtin_fmaf(f, lv[u], lac);
       }
+      M = Mn;
     }
   }
-  if (tid < 128) {
-    const float r = o / l;
+  s_a[g][j] = acc;
+  if (j == 0) s_l[g] = lac;
+  __syncthreads();
+  if (g == 0) {
+    float A = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      A += s_a[t][j];
+      L += s_l[t];
+    }
+    const float r = A / L;
     if constexpr (sizeof(T) == 2) {
       // fp32 -> bf16, round to nearest even
       uint32_t u = __float_as_uint(r);
       u += 0x7FFFu + ((u >> 16) & 1u);
-      out[(int64_t)bq * 128 + tid] = (T)(u >> 16);
+      out[(int64_t)bq * 128 + d] = (T)(u >> 16);
     } else {
-      out[(int64_t)bq * 128 + tid] = r;
+      out[(int64_t)bq * 128 + d] = r;
     }
   }
 }
@@ -2915,9 +2917,9 @@ hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs
 hipError_t launch_attn_merge(int dtype, const float* part, int nch, int rows, void* out,
                              hipStream_t st, const EvPair& ev) {
   if (dtype == 0)
-    return launch(k_attn_merge<uint16_t>, dim3(rows), dim3(256), st, ev, part, nch,
+    return launch(k_attn_merge<uint16_t>, dim3(rows, 4), dim3(256), st, ev, part, nch,
                   (uint16_t*)out);
-  return launch(k_attn_merge<float>, dim3(rows), dim3(256), st, ev, part, nch, (float*)out);
+  return launch(k_attn_merge<float>, dim3(rows, 4), dim3(256), st, ev, part, nch, (float*)out);
 }
 
 void codebook_m8(float* L, float* tau) {

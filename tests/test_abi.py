@@ -76,7 +76,8 @@ def test_sizes(pk):
     assert pk.pariskv_index_bytes(c) == 8 * (1 << 20) * 144
     ws = pk.pariskv_retrieve_workspace_bytes(c, 4096)
     assert 8 * (1 << 20) < ws < 64 * (1 << 20)
-    assert pk.pariskv_attn_workspace_bytes(1, 32, 4096, 128) == 32 * 64 * 132 * 4
+    # one 132-float partial per query head and 32-row chunk of the k rows
+    assert pk.pariskv_attn_workspace_bytes(1, 32, 4096, 128) == 32 * 128 * 132 * 4
 
 
 @pytest.mark.parametrize("field,value,rc", [

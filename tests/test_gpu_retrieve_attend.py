@@ -34,8 +34,8 @@ CASES = {
     "tied_copies": (W("ties", 1, 1, 4, 128, 40000, "bf16", cand_num=1, cand_den=5, k=1024,
                       seed=108), 5000),
     "tiny_k": (W("k = S + 1", 1, 2, 8, 128, 3000, "bf16", k=17, sinks=16, seed=109), 0),
-    # one 64-row chunk: a partial buffer of 528 bytes, below the 256-byte
-    # multiple the attention asks for
+    # k = 64, two 32-row chunks: a partial buffer of 1056 bytes, not the
+    # 256-byte multiple the attention's workspace size is rounded to
     "one_chunk": (W("one chunk", 1, 1, 1, 128, 4096, "fp32", cand_num=1, cand_den=10, k=64,
                     seed=110), 0),
 }
