@@ -146,7 +146,7 @@ WsLayout ws_layout(const pariskv_config* c, int64_t k) {
   L.mmc = off;    off += align_up((size_t)BH * L.nchunks_max * 8, kAlign);
   L.range = off;  off += align_up((size_t)BH * 8, kAlign);
   L.tkmeta = off; off += align_up((size_t)BH * 16, kAlign);
-  L.rows = off;   off += align_up((size_t)BH * L.tk_blocks_max * 2048 * 4, kAlign);
+  L.rows = off;   off += align_up((size_t)BH * L.tk_blocks_max * 2048 * 2, kAlign);
   L.sorted = off; off += align_up((size_t)BH * L.tk_blocks_max * pkv::kTopkSlice * 8, kAlign);
   L.total = off;
   return L;
@@ -286,7 +286,7 @@ int32_t retrieve_impl(const pariskv_index* ix, const void* Q, int32_t k, int32_t
   uint32_t* mmc = (uint32_t*)(base + L.mmc);
   uint32_t* range = (uint32_t*)(base + L.range);
   int32_t* tkmeta = (int32_t*)(base + L.tkmeta);
-  uint32_t* rows = (uint32_t*)(base + L.rows);
+  uint16_t* rows = (uint16_t*)(base + L.rows);
   uint2* sorted = (uint2*)(base + L.sorted);
   pkv::Tiers tw;
   for (int s = 0; s < 8; ++s) tw.w[s] = c->tier_w[s];
@@ -425,8 +425,8 @@ int32_t pariskv_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t k
                                      int32_t head_dim, size_t* bytes) {
   if (!bytes || batch < 1 || n_q_heads < 1 || k < 1 || head_dim < 1)
     return PARISKV_ERR_INVALID_ARG;
-  *bytes = align_up((size_t)batch * n_q_heads * (size_t)ceil_div(k, pkv::kAttnChunkRows) * (head_dim + 4) * 4,
-                    kAlign);
+  const size_t chunks = (size_t)ceil_div(k, pkv::kAttnChunkRows);
+  *bytes = align_up((size_t)batch * n_q_heads * chunks * (head_dim + 4) * 4, kAlign);
   return PARISKV_OK;
 }
 

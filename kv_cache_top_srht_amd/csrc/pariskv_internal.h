@@ -67,7 +67,7 @@ hipError_t launch_compact_rerank(int m, int kpt, int nchunks, int BH, const uint
                                  int32_t* meta_out, hipStream_t st, const EvPair& ev);
 hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cstride, int C,
                        int kprime, int S, int k, int P, const uint32_t* mmc, int chunk_stride,
-                       int nchunks, uint32_t* range, uint32_t* rows, int32_t* tkmeta,
+                       int nchunks, uint32_t* range, uint16_t* rows, int32_t* tkmeta,
                        uint2* sorted, int32_t* out_idx, float* out_est, hipStream_t st,
                        const EvPair& ev_hist, const EvPair& ev_select);
 // top-k with per-unit candidate counts read from cmeta[unit * 4 + 3] on the
@@ -86,7 +86,7 @@ hipError_t launch_topk_counted(int BH, const float* est, const int32_t* cand, in
                                const int32_t* cmeta, int Cmax, int grid_slices, int kprime,
                                int S, int k,
                                const uint32_t* mmc, int chunk_stride, int nchunks,
-                               uint32_t* range, uint32_t* rows, int32_t* tkmeta, uint2* sorted,
+                               uint32_t* range, uint16_t* rows, int32_t* tkmeta, uint2* sorted,
                                int32_t* out_idx, float* out_est, hipStream_t st,
                                const EvPair& ev_hist, const EvPair& ev_select);
 

@@ -1065,7 +1065,8 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
 //    K4b+K5 wrote to this (b, h)'s minimum and maximum, bins its candidates
 //    linearly between them (fp32: bin = min(2047, trunc((e - min) * 2047 /
 //    (max - min))), monotone non-decreasing in e, -0 and +0 alike) and writes
-//    a cumulative row #(bin >= b).
+//    a cumulative row #(bin >= b) of 16-bit entries (a block holds at most
+//    TK_SL candidates).
 //  * k_topk_select: every block sums the rows, finds the bin b1 holding rank
 //    k', gathers b1's members (usually a few dozen; the counting sort in
 //    k_topk_hist left each block's members contiguous), ranks them exactly
@@ -1164,7 +1165,7 @@ __device__ void topk_radix_block(const float* __restrict__ e, const int32_t* __r
 __device__ __forceinline__ void topk_hist_slice(
     const float* __restrict__ est, int64_t cstride, int C, int P,
     const uint32_t* __restrict__ mmc, int chunk_stride, int nchunks,
-    uint32_t* __restrict__ rows, uint32_t* __restrict__ range, uint2* __restrict__ sorted,
+    uint16_t* __restrict__ rows, uint32_t* __restrict__ range, uint2* __restrict__ sorted,
     int p) {
   const int bh = blockIdx.y, tid = threadIdx.x;
   const float* e = est + bh * cstride;
@@ -1207,9 +1208,10 @@ __device__ __forceinline__ void topk_hist_slice(
   const uint32_t hh = s_hist[2047 - 2 * tid], hl = s_hist[2046 - 2 * tid];
   uint2 tot;
   const uint2 ex = block_exscan2<1024>(make_uint2(hh + hl, 0), s_w, tot);
-  uint32_t* row = rows + ((int64_t)bh * P + p) * 2048;
-  row[2047 - 2 * tid] = ex.x + hh;
-  row[2046 - 2 * tid] = ex.x + hh + hl;
+  // 16-bit entries: a slice holds at most TK_SL candidates
+  uint16_t* row = rows + ((int64_t)bh * P + p) * 2048;
+  row[2047 - 2 * tid] = (uint16_t)(ex.x + hh);
+  row[2046 - 2 * tid] = (uint16_t)(ex.x + hh + hl);
   // counting sort of the block's candidates by bin, descending: bin b's
   // entries start at #(bin > b), so a bin's members are contiguous
   s_hist[2047 - 2 * tid] = ex.x;
@@ -1231,7 +1233,7 @@ __device__ __forceinline__ void topk_hist_slice(
 __global__ __launch_bounds__(1024) void k_topk_hist(
     const float* __restrict__ est, int64_t cstride, int C, int P,
     const uint32_t* __restrict__ mmc, int chunk_stride, int nchunks,
-    uint32_t* __restrict__ rows, uint32_t* __restrict__ range, uint2* __restrict__ sorted,
+    uint16_t* __restrict__ rows, uint32_t* __restrict__ range, uint2* __restrict__ sorted,
     const int32_t* __restrict__ cmeta) {
   int Pu = P;
   if (cmeta) {
@@ -1247,7 +1249,7 @@ __global__ __launch_bounds__(1024) void k_topk_hist(
 __device__ __forceinline__ void topk_select_slice(
     const float* __restrict__ est, const int32_t* __restrict__ cand, int64_t cstride, int C,
     int kprime, int S, int k, int P, int Pu, const uint32_t* __restrict__ range,
-    const uint32_t* __restrict__ rows, const uint2* __restrict__ sorted,
+    const uint16_t* __restrict__ rows, const uint2* __restrict__ sorted,
     int32_t* __restrict__ tkmeta, int32_t* __restrict__ out_idx, float* __restrict__ out_est,
     int p) {
   // rows are laid out for P slices; Pu of them are this unit's
@@ -1271,7 +1273,7 @@ __device__ __forceinline__ void topk_select_slice(
   const int32_t ci[4] = {cv.x, cv.y, cv.z, cv.w};
   // resolve (every block of this (b, h) does it, identically): the bin b1
   // holding rank k' and the kept members of b1
-  const uint32_t* rb = rows + (int64_t)bh * P * 2048;
+  const uint16_t* rb = rows + (int64_t)bh * P * 2048;
   for (int b = tid; b < 2048; b += 1024) {
     uint32_t acc = 0;
     for (int q0 = 0; q0 < Pu; q0 += 8) {  // 8 rows in flight
@@ -1388,7 +1390,7 @@ __device__ __forceinline__ void topk_select_slice(
 __global__ __launch_bounds__(1024) void k_topk_select(
     const float* __restrict__ est, const int32_t* __restrict__ cand, int64_t cstride, int C,
     int kprime, int S, int k, int P, const uint32_t* __restrict__ range,
-    const uint32_t* __restrict__ rows, const uint2* __restrict__ sorted,
+    const uint16_t* __restrict__ rows, const uint2* __restrict__ sorted,
     int32_t* __restrict__ tkmeta, int32_t* __restrict__ out_idx, float* __restrict__ out_est,
     const int32_t* __restrict__ cmeta) {
   int Pu = P;
@@ -1412,7 +1414,7 @@ template <int MAXP>
 __global__ __launch_bounds__(1024) void k_topk_select_few(
     const float* __restrict__ est, const int32_t* __restrict__ cand, int64_t cstride, int C,
     int kprime, int S, int k, int P, const uint32_t* __restrict__ range,
-    const uint32_t* __restrict__ rows, const uint2* __restrict__ sorted,
+    const uint16_t* __restrict__ rows, const uint2* __restrict__ sorted,
     int32_t* __restrict__ tkmeta, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
   const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const float* e = est + bh * cstride;
@@ -1427,11 +1429,12 @@ __global__ __launch_bounds__(1024) void k_topk_select_few(
   // All loads are unconditional (one wait covers them all): rows past P
   // re-read row P - 1 and are masked; this block's candidates are read 4 at
   // a time at an index clamped into the row of cstride (a multiple of 64).
-  const uint32_t* rb = rows + (int64_t)bh * P * 2048;
-  uint2 rv[MAXP];
+  const uint16_t* rb = rows + (int64_t)bh * P * 2048;
+  // rows of 16-bit entries: thread t holds bins 2t (low half) and 2t + 1
+  uint32_t rv[MAXP];
 #pragma unroll
   for (int q = 0; q < MAXP; ++q)
-    rv[q] = reinterpret_cast<const uint2*>(rb + (int64_t)(q < P ? q : P - 1) * 2048)[tid];
+    rv[q] = reinterpret_cast<const uint32_t*>(rb + (int64_t)(q < P ? q : P - 1) * 2048)[tid];
   const int c0 = p * TK_SL + tid * 4;
   const int cl = min(c0, (int)cstride - 4);
   const float4 fv = *reinterpret_cast<const float4*>(e + cl);
@@ -1442,7 +1445,7 @@ __global__ __launch_bounds__(1024) void k_topk_select_few(
   uint32_t a0 = 0, a1 = 0;
 #pragma unroll
   for (int q = 0; q < MAXP; ++q) {
-    if (q < P) { a0 += rv[q].x; a1 += rv[q].y; }
+    if (q < P) { a0 += rv[q] & 0xFFFFu; a1 += rv[q] >> 16; }
   }
   s_hist[2 * tid] = a0;
   s_hist[2 * tid + 1] = a1;
@@ -1476,11 +1479,11 @@ __global__ __launch_bounds__(1024) void k_topk_select_few(
     if (b1 & 1u) {
 #pragma unroll
       for (int q = 0; q < MAXP; ++q)
-        if (q < P) s_cnt[q] = rv[q].y;
+        if (q < P) s_cnt[q] = rv[q] >> 16;
     } else {
 #pragma unroll
       for (int q = 0; q < MAXP; ++q)
-        if (q < P) s_cnt[q] = rv[q].x;
+        if (q < P) s_cnt[q] = rv[q] & 0xFFFFu;
     }
   }
   if (b1 + 1 < 2048u) {
@@ -1488,11 +1491,11 @@ __global__ __launch_bounds__(1024) void k_topk_select_few(
       if ((b1 + 1) & 1u) {
 #pragma unroll
         for (int q = 0; q < MAXP; ++q)
-          if (q < P) s_start[q] = rv[q].y;
+          if (q < P) s_start[q] = rv[q] >> 16;
       } else {
 #pragma unroll
         for (int q = 0; q < MAXP; ++q)
-          if (q < P) s_start[q] = rv[q].x;
+          if (q < P) s_start[q] = rv[q] & 0xFFFFu;
       }
     }
   } else if (tid < P) {
@@ -2798,7 +2801,7 @@ hipError_t launch_compact_rerank(int m, int kpt, int nchunks, int BH, const uint
 
 hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cstride, int C,
                        int kprime, int S, int k, int P, const uint32_t* mmc, int chunk_stride,
-                       int nchunks, uint32_t* range, uint32_t* rows, int32_t* tkmeta,
+                       int nchunks, uint32_t* range, uint16_t* rows, int32_t* tkmeta,
                        uint2* sorted, int32_t* out_idx, float* out_est, hipStream_t st,
                        const EvPair& ev_hist, const EvPair& ev_select) {
   const dim3 grid(P, BH);
@@ -2826,17 +2829,17 @@ hipError_t launch_topk(int BH, const float* est, const int32_t* cand, int64_t cs
   if (e != hipSuccess) return e;
   if (P <= kTopkFewSlices)
     return launch(k_topk_select_few<kTopkFewSlices>, grid, dim3(1024), st, ev_select, est, cand,
-                  cstride, C, kprime, S, k, P, (const uint32_t*)range, (const uint32_t*)rows,
+                  cstride, C, kprime, S, k, P, (const uint32_t*)range, (const uint16_t*)rows,
                   (const uint2*)sorted, tkmeta, out_idx, out_est);
   return launch(k_topk_select, grid, dim3(1024), st, ev_select, est, cand, cstride, C, kprime, S,
-                k, P, (const uint32_t*)range, (const uint32_t*)rows, (const uint2*)sorted, tkmeta,
+                k, P, (const uint32_t*)range, (const uint16_t*)rows, (const uint2*)sorted, tkmeta,
                 out_idx, out_est, (const int32_t*)nullptr);
 }
 
 hipError_t launch_topk_counted(int BH, const float* est, const int32_t* cand, int64_t cstride,
                                const int32_t* cmeta, int Cmax, int grid_slices, int kprime,
                                int S, int k, const uint32_t* mmc, int chunk_stride, int nchunks,
-                               uint32_t* range, uint32_t* rows, int32_t* tkmeta, uint2* sorted,
+                               uint32_t* range, uint16_t* rows, int32_t* tkmeta, uint2* sorted,
                                int32_t* out_idx, float* out_est, hipStream_t st,
                                const EvPair& ev_hist, const EvPair& ev_select) {
   // per-unit candidate counts known on the device only: rows laid out for
@@ -2848,7 +2851,7 @@ hipError_t launch_topk_counted(int BH, const float* est, const int32_t* cand, in
                         chunk_stride, nchunks, rows, range, sorted, cmeta);
   if (e != hipSuccess) return e;
   return launch(k_topk_select, grid, dim3(1024), st, ev_select, est, cand, cstride, Cmax, kprime,
-                S, k, P, (const uint32_t*)range, (const uint32_t*)rows, (const uint2*)sorted,
+                S, k, P, (const uint32_t*)range, (const uint16_t*)rows, (const uint2*)sorted,
                 tkmeta, out_idx, out_est, cmeta);
 }
 

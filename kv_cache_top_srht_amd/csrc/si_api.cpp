@@ -95,7 +95,7 @@ SiWsLayout si_ws_layout(const pariskv_si_config* c) {
   L.mmc = off;    off += align_up(BH * (size_t)L.nchunks_max * 2 * 4, kAlign);
   L.tkrange = off; off += align_up(BH * 2 * 4, kAlign);
   L.tkmeta = off; off += align_up(BH * 4 * 4, kAlign);
-  L.rows = off;   off += align_up(BH * (size_t)L.pmax * 2048 * 4, kAlign);
+  L.rows = off;   off += align_up(BH * (size_t)L.pmax * 2048 * 2, kAlign);
   L.sorted = off; off += align_up(BH * (size_t)L.pmax * pkv::kTopkSlice * 8, kAlign);
   L.total = off;
   return L;
@@ -134,7 +134,7 @@ int32_t si_retrieve_impl(const pariskv_si_index* ix, const void* Q, int32_t k, i
   uint32_t* mmc = (uint32_t*)(base + L.mmc);
   uint32_t* tkrange = (uint32_t*)(base + L.tkrange);
   int32_t* tkmeta = (int32_t*)(base + L.tkmeta);
-  uint32_t* rows = (uint32_t*)(base + L.rows);
+  uint16_t* rows = (uint16_t*)(base + L.rows);
   uint2* sorted = (uint2*)(base + L.sorted);
   auto ev = [&](int s) {
     pkv::EvPair p;
