@@ -164,8 +164,8 @@ int pick_kpt(int64_t E, int64_t BH) {
 float rot_scale(int d) { return (float)(1.0L / std::sqrt((long double)d)); }
 
 // Split-K partial slots per query head of a retrieval + attention: the
-// attention's chunks of kAttnChunkRows rows.
-int64_t attend_part_chunks(int64_t k) { return ceil_div(k, pkv::kAttnChunkRows); }
+// attention's chunks, at their smallest.
+int64_t attend_part_chunks(int64_t k) { return ceil_div(k, pkv::kAttnChunkRowsMin); }
 size_t attend_part_bytes(const pariskv_config* c, int64_t k) {
   return align_up((size_t)c->batch * c->n_q_heads * attend_part_chunks(k) * pkv::kPartStride * 4,
                   kAlign);
@@ -368,7 +368,8 @@ int32_t attn_core(const void* Q, const pkv::AttnRows& rs, const int32_t* idx, in
   pariskv_attn_workspace_bytes(batch, n_q_heads, (int32_t)rows, head_dim, &need);
   if (ws_bytes < need) return PARISKV_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  const int nch = (int)ceil_div(rows, pkv::kAttnChunkRows);
+  const int rpl = pkv::attn_rows_per_lane(rows, (int64_t)batch * n_kv_heads);
+  const int nch = (int)ceil_div(rows, 16 * rpl);
   const float qscale = scale * 1.4426950408889634f;
   pkv::EvPair e0, e1;
   if (events) {
@@ -378,8 +379,8 @@ int32_t attn_core(const void* Q, const pkv::AttnRows& rs, const int32_t* idx, in
     e1.stop = (hipEvent_t)events[3];
   }
   (void)hipGetLastError();
-  hipError_t e = pkv::launch_attn_split(dtype, G, Q, rs, idx, k, batch, n_kv_heads, qscale,
-                                        (float*)ws, nch, st, e0);
+  hipError_t e = pkv::launch_attn_split(dtype, G, rpl, Q, rs, idx, k, batch, n_kv_heads,
+                                        qscale, (float*)ws, nch, st, e0);
   if (e != hipSuccess) return hip_status(e);
   e = pkv::launch_attn_merge(dtype, (const float*)ws, nch, batch * n_q_heads, out, st, e1);
   if (e != hipSuccess) return hip_status(e);
@@ -425,7 +426,7 @@ int32_t pariskv_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t k
                                      int32_t head_dim, size_t* bytes) {
   if (!bytes || batch < 1 || n_q_heads < 1 || k < 1 || head_dim < 1)
     return PARISKV_ERR_INVALID_ARG;
-  const size_t chunks = (size_t)ceil_div(k, pkv::kAttnChunkRows);
+  const size_t chunks = (size_t)ceil_div(k, pkv::kAttnChunkRowsMin);
   *bytes = align_up((size_t)batch * n_q_heads * chunks * (head_dim + 4) * 4, kAlign);
   return PARISKV_OK;
 }

@@ -131,11 +131,18 @@ constexpr int kTinyCands = 2048;
 constexpr int kTopkFewSlices = 16;
 // split-K attention partial per (query head, chunk): o[128], m, l, 2 unused
 constexpr int kPartStride = 132;
-// rows per lane of a split-attention block (16 row slots), and the selected
-// rows of one block: one split-K partial per query head and chunk of
-// kAttnChunkRows rows
-constexpr int kAttnRowsPerLane = 2;
-constexpr int kAttnChunkRows = 16 * kAttnRowsPerLane;
+// Split attention: a block of 16 row slots takes rpl rows per slot, a chunk
+// of 16 rpl selected rows (one split-K partial per query head and chunk).
+// rpl = 2 (32-row chunks) when the grid of 64-row chunks would hold fewer
+// than kAttnSmallGrid blocks, else 4; workspaces are sized for the smaller
+// chunk.
+constexpr int kAttnChunkRowsMin = 32;
+constexpr int64_t kAttnSmallGrid = 1024;
+inline int attn_rows_per_lane(int64_t rows, int64_t units) {
+  return units * ((rows + 63) / 64) < kAttnSmallGrid ? 2 : 4;
+}
+// the merge takes four blocks per (b, query head) below this many of them
+constexpr int kMergeSplitRows = 128;
 // Where attention rows come from.  Listed positions p (from idx) are read
 // from the near store when p < n_near_head, else from the far store; the
 // tail_n rows after the list are positions tail_lo + t, read from the near
@@ -154,7 +161,7 @@ struct AttnRows {
   int tail_n = 0;
   int unit_div = 1;              // attention units (blocks.y) per KV head of K and V
 };
-hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs,
+hipError_t launch_attn_split(int dtype, int G, int rpl, const void* Q, const AttnRows& rs,
                              const int32_t* idx, int k, int batch, int n_kv_heads, float qscale,
                              float* part, int nch, hipStream_t st, const EvPair& ev);
 hipError_t launch_attn_merge(int dtype, const float* part, int nch, int rows, void* out,

@@ -2426,9 +2426,9 @@ __global__ __launch_bounds__(1024) void k_retrieve_tiny(
 
 // ---------------------------------------------------------------------------
 // K7 split-K sparse attention ([TS] Problem Statement; System-Level
-// Innovations 1: only the selected rows are fetched).  Block = kAttnChunkRows
-// (32) selected rows of one (b, h); 16 lanes per row (16 B of K and of V per
-// lane), 16 row slots x kAttnRowsPerLane rows.  The G query heads of the KV head are held in registers
+// Innovations 1: only the selected rows are fetched).  Block = a chunk of
+// 16 RPL selected rows of one (b, h) (RPL = 2 or 4: attn_rows_per_lane); 16
+// lanes per row (16 B of K and of V per lane), 16 row slots x RPL rows.  The G query heads of the KV head are held in registers
 // (pre-multiplied by scale * log2 e), logits summed across the 16 lanes of a
 // row with DPP, softmax statistics per slot; the 16 slots are combined in
 // LDS (wave 0, one row of 16 lanes per query head, forms each slot's factor
@@ -2455,12 +2455,11 @@ __device__ __forceinline__ float row_max16(float v) {
   return v;
 }
 
-template <typename T, int G>
+template <typename T, int G, int RPL>
 __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, AttnRows rs,
                                                     const int32_t* __restrict__ idx, int k,
                                                     int n_kv_heads, float qscale,
                                                     float* __restrict__ part, int nch) {
-  constexpr int RPL = kAttnRowsPerLane;
   const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   const int b = bh / n_kv_heads, h = bh - b * n_kv_heads;
   const int Hq = n_kv_heads * G;
@@ -2478,7 +2477,7 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
   bool valid[RPL], near[RPL];
 #pragma unroll
   for (int it = 0; it < RPL; ++it) {
-    const int r = chunk * kAttnChunkRows + slot + 16 * it;
+    const int r = chunk * (16 * RPL) + slot + 16 * it;
     valid[it] = r < n_rows;
     const bool listed = r < k;
     const int64_t p = listed ? (int64_t)ib[r < k ? r : k - 1]  // unconditional load
@@ -2564,8 +2563,9 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
   }
 }
 
-// K8 log-sum-exp merge of the split-K partials -> output row per query head.
-// Four blocks per (b, query head), block q for output coordinates 32 q ..
+// K8 log-sum-exp merge of the split-K partials -> output row per query head,
+// for fewer than kMergeSplitRows (b, query head) pairs.  Four blocks per
+// (b, query head), block q for output coordinates 32 q ..
 // 32 q + 31: thread (g = tid / 32, j = tid % 32) takes chunks g, g + 8, ...
 // of coordinate 32 q + j, up to 16 of them (m, l and o) loaded in one round;
 // the block's maximum M by wave reductions, then each thread's sum of
@@ -2635,6 +2635,80 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
       out[(int64_t)bq * 128 + d] = (T)(u >> 16);
     } else {
       out[(int64_t)bq * 128 + d] = r;
+    }
+  }
+}
+
+// K8 for many query heads (kMergeSplitRows or more): one block per (b, query
+// head).  Partials are staged in LDS 64 chunks at a time (one round of
+// 16-byte loads); wave 0 forms the tile's maximum and each chunk's factor
+// exp2(m_c - M) once, then threads 0..127 combine the chunks for their
+// output element in chunk order, rescaling by the running maximum across
+// tiles.
+template <typename T>
+__global__ __launch_bounds__(256) void k_attn_merge_row(const float* __restrict__ part, int nch,
+                                                        T* __restrict__ out) {
+  constexpr int R4 = kPartStride / 4;  // float4 per partial record
+  constexpr int TILE = 64;
+  constexpr int NLD = (TILE * R4 + 255) / 256;
+  const int bq = blockIdx.x, tid = threadIdx.x;
+  const float* pp = part + (int64_t)bq * nch * kPartStride;
+  __shared__ float4 s_p4[TILE * R4];
+  __shared__ float s_f[TILE], s_m[1];
+  const float* s_p = reinterpret_cast<const float*>(s_p4);
+  float o = 0.0f, l = 0.0f, M = -INFINITY;
+  for (int t0 = 0; t0 < nch; t0 += TILE) {
+    const int nt = min(TILE, nch - t0);
+    const int n4 = nt * R4;
+    const float4* src = reinterpret_cast<const float4*>(pp + (int64_t)t0 * kPartStride);
+    float4 v[NLD];
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int i = tid + 256 * u;
+      v[u] = (i < n4) ? src[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    __syncthreads();  // the previous tile has been consumed
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int i = tid + 256 * u;
+      if (i < n4) s_p4[i] = v[u];
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane c: chunk c's maximum; the tile's by a wave reduction
+      const float mc = tid < nt ? s_p[tid * kPartStride + 128] : -INFINITY;
+      float tm = mc;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) tm = fmaxf(tm, __shfl_xor(tm, off));
+      const float Mn = fmaxf(M, tm);
+      if (tid < nt) s_f[tid] = (Mn == -INFINITY || mc == -INFINITY) ? 0.0f : exp2f(mc - Mn);
+      if (tid == 0) s_m[0] = Mn;
+    }
+    __syncthreads();
+    if (tid < 128) {
+      const float Mn = s_m[0];
+      if (Mn != -INFINITY) {
+        const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+        o *= r;
+        l *= r;
+        M = Mn;
+        for (int c = 0; c < nt; ++c) {
+          const float f = s_f[c];
+          o = __builtin_fmaf(f, s_p[c * kPartStride + tid], o);
+          l = __builtin_fmaf(f, s_p[c * kPartStride + 129], l);
+        }
+      }
+    }
+  }
+  if (tid < 128) {
+    const float r = o / l;
+    if constexpr (sizeof(T) == 2) {
+      // fp32 -> bf16, round to nearest even
+      uint32_t u = __float_as_uint(r);
+      u += 0x7FFFu + ((u >> 16) & 1u);
+      out[(int64_t)bq * 128 + tid] = (T)(u >> 16);
+    } else {
+      out[(int64_t)bq * 128 + tid] = r;
     }
   }
 }
@@ -2891,13 +2965,16 @@ hipError_t launch_retrieve_small(int m, int dtype, const void* Q, int BH, int n_
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs,
+hipError_t launch_attn_split(int dtype, int G, int rpl, const void* Q, const AttnRows& rs,
                              const int32_t* idx, int k, int batch, int n_kv_heads, float qscale,
                              float* part, int nch, hipStream_t st, const EvPair& ev) {
   const dim3 grid(nch, batch * n_kv_heads);
-#define PKV_AS(T, GG)                                                                         \
-  return launch(k_attn_split<T, GG>, grid, dim3(256), st, ev, (const T*)Q, rs, idx, k,      \
-                n_kv_heads, qscale, part, nch)
+  if (rpl != 2 && rpl != 4) return hipErrorInvalidValue;
+#define PKV_AS(T, GG)                                                                          \
+  return rpl == 2 ? launch(k_attn_split<T, GG, 2>, grid, dim3(256), st, ev, (const T*)Q, rs,   \
+                           idx, k, n_kv_heads, qscale, part, nch)                              \
+                  : launch(k_attn_split<T, GG, 4>, grid, dim3(256), st, ev, (const T*)Q, rs,   \
+                           idx, k, n_kv_heads, qscale, part, nch)
   if (dtype == 0) {
     switch (G) {
       case 1: PKV_AS(uint16_t, 1);
@@ -2919,10 +2996,17 @@ hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs
 
 hipError_t launch_attn_merge(int dtype, const float* part, int nch, int rows, void* out,
                              hipStream_t st, const EvPair& ev) {
+  // four blocks per (b, query head) while they are few, else one
+  if (rows < kMergeSplitRows) {
+    if (dtype == 0)
+      return launch(k_attn_merge<uint16_t>, dim3(rows, 4), dim3(256), st, ev, part, nch,
+                    (uint16_t*)out);
+    return launch(k_attn_merge<float>, dim3(rows, 4), dim3(256), st, ev, part, nch, (float*)out);
+  }
   if (dtype == 0)
-    return launch(k_attn_merge<uint16_t>, dim3(rows, 4), dim3(256), st, ev, part, nch,
+    return launch(k_attn_merge_row<uint16_t>, dim3(rows), dim3(256), st, ev, part, nch,
                   (uint16_t*)out);
-  return launch(k_attn_merge<float>, dim3(rows, 4), dim3(256), st, ev, part, nch, (float*)out);
+  return launch(k_attn_merge_row<float>, dim3(rows), dim3(256), st, ev, part, nch, (float*)out);
 }
 
 void codebook_m8(float* L, float* tau) {

@@ -163,7 +163,7 @@ hipError_t launch_si_scores(int units, const uint8_t* ids, int64_t cap, int64_t 
   return hipSuccess;
 }
 
-hipError_t launch_attn_split(int dtype, int G, const void* Q, const AttnRows& rs,
+hipError_t launch_attn_split(int dtype, int G, int rpl, const void* Q, const AttnRows& rs,
                              const int32_t* idx, int k, int batch, int n_kv_heads, float qscale,
                              float* part, int nch, hipStream_t st, const EvPair& ev) {
   return hipSuccess;

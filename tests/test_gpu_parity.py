@@ -330,6 +330,37 @@ def test_attention_dense_and_sparse(orc, G, dtype, k, N):
         assert np.max(np.abs(oh[b, h * G:(h + 1) * G] - ref)) <= tol
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_attention_large_grid(orc, dtype):
+    """The attention's other launch shapes: 16 x 8 KV heads with k = 512 make
+    1024 blocks of 64-row chunks (the split's 4-rows-per-lane form) and 512
+    (b, query head) pairs (the one-block merge); sampled heads against fp64
+    softmax attention."""
+    B, Hkv, G, k, N = 16, 8, 4, 512, 2048
+    case("attention large grid %s B=%d Hkv=%d G=%d k=%d N=%d" % (dtype, B, Hkv, G, k, N))
+    w = W("attn grid", B, Hkv, Hkv * G, 128, N, dtype, k=k, seed=43)
+    lay = synth.make_layer(w, "cuda")
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    idx = torch.stack([torch.sort(torch.randperm(N, generator=gen)[:k]).values
+                       for _ in range(B * Hkv)]).to(torch.int32).cuda()
+    ws = torch.empty(pk.pariskv_attn_workspace_bytes(B, Hkv * G, k, 128),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full_like(lay["Q"], float("nan"))
+    pk.pariskv_sparse_attn(lay["Q"], lay["K"], lay["V"], N, idx, k, B, Hkv * G,
+                           Hkv, 128, pk.PARISKV_DTYPE_BF16 if dtype == "bf16"
+                           else pk.PARISKV_DTYPE_FP32, 128 ** -0.5, out, ws)
+    torch.cuda.synchronize()
+    Qh, Kh, Vh = host_f32(lay["Q"]), host_f32(lay["K"]), host_f32(lay["V"])
+    ih, oh = idx.cpu().numpy(), host_f32(out)
+    assert not np.isnan(oh).any()
+    tol = ATTN_TOL_BF16 if dtype == "bf16" else ATTN_TOL_FP32
+    for bh in (0, 37, 64, 127):
+        b, h = divmod(bh, Hkv)
+        ref = orc.attention(Qh[b, h * G:(h + 1) * G], Kh[b, h], Vh[b, h], ih[bh],
+                            128 ** -0.5)
+        assert np.max(np.abs(oh[b, h * G:(h + 1) * G] - ref)) <= tol
+
+
 def test_append_to_capacity(orc):
     """Appends fill the index exactly to its capacity (then one more key is
     refused on the host); the full index retrieves as the oracle does."""
