@@ -1217,14 +1217,19 @@ __device__ __forceinline__ void topk_hist_slice(
   s_hist[2047 - 2 * tid] = ex.x;
   s_hist[2046 - 2 * tid] = ex.x + hh;
   __syncthreads();
-  uint2* out = sorted + ((int64_t)bh * P + p) * TK_SL;
+  // sorted in LDS, then written out coalesced
+  __shared__ uint2 s_sorted[TK_SL];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     if (c0 + r < C) {
       const uint32_t slot = atomicAdd(&s_hist[est_bin(f[r], fmin, scale)], 1u);
-      out[slot] = make_uint2(order_key(f[r]), (uint32_t)(c0 + r));
+      s_sorted[slot] = make_uint2(order_key(f[r]), (uint32_t)(c0 + r));
     }
   }
+  __syncthreads();
+  uint2* out = sorted + ((int64_t)bh * P + p) * TK_SL;
+  const int nb = min(TK_SL, C - p * TK_SL);  // the block's candidates
+  for (int i = tid; i < nb; i += 1024) out[i] = s_sorted[i];
 }
 
 // cmeta (optional): this unit's candidate count is cmeta[bh * 4 + 3], at
