@@ -386,7 +386,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (channel-scaled Gaussian keys with outlier "
                 "channels, Gaussian values; no model weights)",
         "config": {

@@ -34,6 +34,7 @@ def test_bench_json_line():
     assert j["unit"] == "keys/s" and j["value"] > 0 and j["higher_is_better"] is True
     assert j["ms_per_step"] > 0 and j["vs_baseline"] is None
     assert j["config"]["workload"]
+    assert j["dtype"] == "f32"  # the tiny workload stores and computes in fp32
     roof = j["roofline"]
     for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert key in roof, key
