@@ -757,7 +757,7 @@ __device__ __forceinline__ void score_masks(const uint8_t (&sc)[KPT], const uint
 // value of lane S of this lane's group of 4 (DPP quad permutation, no LDS)
 template <int S>
 __device__ __forceinline__ float quad_lane(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x55 * S, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x55 * S, 0xF, 0xF, true));
 }
 
 // LDS product table: subspace b's 128 entries ([j][code]) start at b * 132
@@ -788,15 +788,31 @@ __device__ __forceinline__ float rerank_estimate(
   // independent and all go out before the first sum waits (left to itself the
   // compiler waits after each subspace's 8), then each subspace's sum in
   // coordinate order
+  // byte offsets code * 4 of a dword's 8 nibbles, two masked shifts per
+  // dword: the even nibbles in the bytes of ev, the odd ones in od; each read
+  // address is then the row base plus one byte (a byte-select add)
+  uint32_t ev[4], od[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    ev[c] = (cws[c] << 2) & 0x3C3C3C3Cu;
+    od[c] = (cws[c] >> 2) & 0x3C3C3C3Cu;
+    // opaque to the optimiser, which would otherwise fold the masks back
+    // into one shift-and pair per nibble
+    asm("" : "+v"(ev[c]));
+    asm("" : "+v"(od[c]));
+  }
   float v[NB][M];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     // subspace 4 q NB / 4 + i: coordinates from nibble j0 of code dword bb
     const int bb = (i * M) >> 3, j0 = (i * M) & 7;
-    const float* pb = s_P + (4 * q + bb) * kPtabRow;
+    const char* pb = reinterpret_cast<const char*>(s_P + (4 * q + bb) * kPtabRow);
 #pragma unroll
-    for (int jj = 0; jj < M; ++jj)
-      v[i][jj] = pb[(j0 + jj) * 16 + ((cws[bb] >> (4 * (j0 + jj))) & 15u)];
+    for (int jj = 0; jj < M; ++jj) {
+      const int n = j0 + jj;
+      const uint32_t off = (((n & 1) ? od[bb] : ev[bb]) >> (8 * (n >> 1))) & 0xFFu;
+      v[i][jj] = *reinterpret_cast<const float*>(pb + n * 64 + off);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   float t[NB];
@@ -1027,17 +1043,18 @@ __global__ __launch_bounds__(256) void k_compact_rerank(
       if (j0 + r * 64 >= ntot) break;  // uniform across the block
       const uint32_t j = j0 + r * 64 + (tid >> 2);
       const float e = rerank_estimate<M>(cw[r], ww[r], s_P, q);
-      if (j < ntot) {
-        if (q == 0) {
-          const uint32_t o = (j >= nsel0) ? off_c[1] + (j - nsel0) : off_c[0] + j;
-          if ((int64_t)o < C) {  // always true when K4a and this kernel agree
-            cand[bh * cstride + o] = (int32_t)pi[r];
-            est[bh * cstride + o] = e;
-          }
+      // the range update is unconditional (masked by selects), so the sum's
+      // additions stay beside their lane moves and fold into DPP adds
+      const bool valid = j < ntot;
+      const uint32_t ok = order_key(e);
+      kmn = min(kmn, valid ? ok : 0xFFFFFFFFu);
+      kmx = max(kmx, valid ? ok : 0u);
+      if (valid && q == 0) {
+        const uint32_t o = (j >= nsel0) ? off_c[1] + (j - nsel0) : off_c[0] + j;
+        if ((int64_t)o < C) {  // always true when K4a and this kernel agree
+          cand[bh * cstride + o] = (int32_t)pi[r];
+          est[bh * cstride + o] = e;
         }
-        const uint32_t ok = order_key(e);
-        kmn = min(kmn, ok);
-        kmx = max(kmx, ok);
       }
     }
   }
