@@ -2455,11 +2455,16 @@ __global__ __launch_bounds__(1024) void k_retrieve_tiny(
 // row with DPP, softmax statistics per slot; the 16 slots are combined in
 // LDS (wave 0, one row of 16 lanes per query head, forms each slot's factor
 // and the total denominator once).  Writes per query head a partial
-// (o[128], m, l) in the log2 domain.
+// (o[128], m, l) in the log2 domain.  The weights exp2(logit - max) use the
+// hardware exp2 directly: every argument is <= 0, and a weight below 2^-126
+// (flushed to zero there) is far below the attention's tolerance.
 // ---------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  // every source lane of these patterns lies in the same row of 16, so the
+  // bound-control zero fill never applies; it lets the move fold into the
+  // add or max that consumes it
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 // sum / maximum over the 16 lanes of a row, received by all of them
 __device__ __forceinline__ float row_sum16(float v) {
@@ -2551,7 +2556,7 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
     if (m != -INFINITY) {
 #pragma unroll
       for (int it = 0; it < RPL; ++it) {
-        const float pw = exp2f(lg[it][g] - m);
+        const float pw = __builtin_amdgcn_exp2f(lg[it][g] - m);  // argument <= 0
         l += pw;
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[j] = __builtin_fmaf(pw, vx[it][j], o[j]);
@@ -2568,7 +2573,7 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
     const int g = tid >> 4, sl = tid & 15;
     const float ms = s_m[sl][g];
     const float M = row_max16(ms);
-    const float f = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
+    const float f = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
     const float lt = row_sum16(f * s_l[sl][g]);
     s_f[sl][g] = f;
     if (sl == 0) { s_M[g] = M; s_L[g] = lt; }
