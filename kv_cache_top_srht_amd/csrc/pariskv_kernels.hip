@@ -841,8 +841,10 @@ __device__ __forceinline__ float rerank_estimate(
 // unit's chunk rows, and its chunks' offsets from block scans over the rows
 // before them -- the K4a arithmetic, repeated per block (block 0 of each unit
 // also writes meta); meta and coff are then not read.
+// Held to 72 VGPRs (7 waves per SIMD, 7 blocks per CU) by the launch
+// bounds: one more resident block per CU than the 74 it would take.
 template <int KPT, int CPB, int M, bool FT>
-__global__ __launch_bounds__(256) void k_compact_rerank(
+__global__ __launch_bounds__(256, 7) void k_compact_rerank(
     const uint8_t* __restrict__ scores, int64_t Epad, int64_t S, int64_t E,
     const int32_t* __restrict__ meta, const uint32_t* __restrict__ coff, int chunk_stride,
     int nchunks, const float* __restrict__ ptab, const uint32_t* __restrict__ rec,

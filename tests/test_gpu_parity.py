@@ -198,6 +198,8 @@ def test_ties_duplicates_and_zero_keys(orc, B, path):
     (60000, 5, 2048, 8000, "pipeline"),   # 3 slices, threshold bin of 8000 equal keys
     (80000, 5, 2048, 0, "pipeline"),      # 16000 candidates: 4 slices, the one-kernel limit
     (90000, 5, 2048, 0, "pipeline"),      # 18000 candidates: 5 slices, histogram + select
+    (90000, 5, 2048, 8000, "pipeline"),   # 5 slices and the select's radix select of a tied bin
+    (327680, 5, 4096, 0, "pipeline"),     # 65536 candidates: 16 slices, every row in registers
     (150000, 2, 4096, 0, "pipeline"),     # 75000 candidates: 19 slices, generic select
     (150000, 2, 4096, 8000, "pipeline"),  # 19 slices and the radix select of a tied bin
     # the single-kernel path: its top-k over 2 and 4 slices, and its radix select
@@ -207,10 +209,11 @@ def test_ties_duplicates_and_zero_keys(orc, B, path):
 ])
 def test_topk_paths(orc, N, den, k, copies, path):
     """The top-k's paths: one kernel up to 4 slices of 4096 candidates, the
-    histogram + select pair above that (more than 16 slices: the generic
-    select), and a threshold bin holding more than 4096 members (identical
-    keys tie exactly on score and estimate; the lower positions win); the
-    single-kernel retrieval's own top-k up to 4 slices."""
+    histogram + select pair above that (up to 16 slices the select holds
+    every histogram row in registers; above, the generic select), and a
+    threshold bin holding more than 4096 members (identical keys tie exactly
+    on score and estimate; the lower positions win); the single-kernel
+    retrieval's own top-k up to 4 slices."""
     w = W("topk paths", 1, 1, 4, 128, N, "bf16", cand_num=1, cand_den=den, k=k,
           seed=33)
     case("top-k paths N=%d f=1/%d k=%d copies=%d, %s path" % (N, den, k, copies, path))
