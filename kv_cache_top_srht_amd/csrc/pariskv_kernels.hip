@@ -2484,7 +2484,9 @@ __device__ __forceinline__ float row_max16(float v) {
   return v;
 }
 
-template <typename T, int G, int RPL>
+// WIN: rows may come from the near store or its ring (a sliding window);
+// without it every row is a listed position in the far store.
+template <typename T, int G, int RPL, bool WIN>
 __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, AttnRows rs,
                                                     const int32_t* __restrict__ idx, int k,
                                                     int n_kv_heads, float qscale,
@@ -2500,7 +2502,7 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
   // rows r < k are the positions idx[r] (positions below n_near_head in the
   // near store, the rest in the far store); rows k .. k + tail_n - 1 are the
   // positions tail_lo + (r - k), in the near store's ring
-  const int n_rows = k + rs.tail_n;
+  const int n_rows = k + (WIN ? rs.tail_n : 0);
   const int32_t* ib = idx + (int64_t)bh * k;
   int64_t row[RPL];
   bool valid[RPL], near[RPL];
@@ -2508,15 +2510,20 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
   for (int it = 0; it < RPL; ++it) {
     const int r = chunk * (16 * RPL) + slot + 16 * it;
     valid[it] = r < n_rows;
-    const bool listed = r < k;
-    const int64_t p = listed ? (int64_t)ib[r < k ? r : k - 1]  // unconditional load
-                             : rs.tail_lo + (r - k);
-    if (listed) {
-      near[it] = p < rs.n_near_head;
-      row[it] = p;
+    const int32_t li = ib[r < k ? r : k - 1];  // unconditional load
+    if constexpr (WIN) {
+      const bool listed = r < k;
+      const int64_t p = listed ? (int64_t)li : rs.tail_lo + (r - k);
+      if (listed) {
+        near[it] = p < rs.n_near_head;
+        row[it] = p;
+      } else {
+        near[it] = true;
+        row[it] = rs.n_near_head + (p - rs.n_near_head) % rs.ring;
+      }
     } else {
-      near[it] = true;
-      row[it] = rs.n_near_head + (p - rs.n_near_head) % rs.ring;
+      near[it] = false;
+      row[it] = li;
     }
     if (!valid[it]) { near[it] = false; row[it] = 0; }
   }
@@ -2535,8 +2542,8 @@ __global__ __launch_bounds__(256) void k_attn_split(const T* __restrict__ Q, Att
   float kx[RPL][8], vx[RPL][8];
 #pragma unroll
   for (int it = 0; it < RPL; ++it) {
-    load8_stream((near[it] ? Kn : Kf) + (row[it] << 7), kx[it]);
-    load8_stream((near[it] ? Vn : Vf) + (row[it] << 7), vx[it]);
+    load8_stream((WIN && near[it] ? Kn : Kf) + (row[it] << 7), kx[it]);
+    load8_stream((WIN && near[it] ? Vn : Vf) + (row[it] << 7), vx[it]);
   }
   float lg[RPL][G];
 #pragma unroll
@@ -2999,11 +3006,13 @@ hipError_t launch_attn_split(int dtype, int G, int rpl, const void* Q, const Att
                              float* part, int nch, hipStream_t st, const EvPair& ev) {
   const dim3 grid(nch, batch * n_kv_heads);
   if (rpl != 2 && rpl != 4) return hipErrorInvalidValue;
-#define PKV_AS(T, GG)                                                                          \
-  return rpl == 2 ? launch(k_attn_split<T, GG, 2>, grid, dim3(256), st, ev, (const T*)Q, rs,   \
-                           idx, k, n_kv_heads, qscale, part, nch)                              \
-                  : launch(k_attn_split<T, GG, 4>, grid, dim3(256), st, ev, (const T*)Q, rs,   \
-                           idx, k, n_kv_heads, qscale, part, nch)
+  const bool win = rs.n_near_head > 0 || rs.tail_n > 0;
+#define PKV_ASW(T, GG, R)                                                                      \
+  (win ? launch(k_attn_split<T, GG, R, true>, grid, dim3(256), st, ev, (const T*)Q, rs, idx,   \
+                k, n_kv_heads, qscale, part, nch)                                              \
+       : launch(k_attn_split<T, GG, R, false>, grid, dim3(256), st, ev, (const T*)Q, rs, idx,  \
+                k, n_kv_heads, qscale, part, nch))
+#define PKV_AS(T, GG) return rpl == 2 ? PKV_ASW(T, GG, 2) : PKV_ASW(T, GG, 4)
   if (dtype == 0) {
     switch (G) {
       case 1: PKV_AS(uint16_t, 1);
@@ -3021,6 +3030,7 @@ hipError_t launch_attn_split(int dtype, int G, int rpl, const void* Q, const Att
     default: return hipErrorInvalidValue;
   }
 #undef PKV_AS
+#undef PKV_ASW
 }
 
 hipError_t launch_attn_merge(int dtype, const float* part, int nch, int rows, void* out,
