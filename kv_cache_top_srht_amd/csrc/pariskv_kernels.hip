@@ -841,10 +841,8 @@ __device__ __forceinline__ float rerank_estimate(
 // unit's chunk rows, and its chunks' offsets from block scans over the rows
 // before them -- the K4a arithmetic, repeated per block (block 0 of each unit
 // also writes meta); meta and coff are then not read.
-// Held to 72 VGPRs (7 waves per SIMD, 7 blocks per CU) by the launch
-// bounds: one more resident block per CU than the 74 it would take.
 template <int KPT, int CPB, int M, bool FT>
-__global__ __launch_bounds__(256, 7) void k_compact_rerank(
+__device__ __forceinline__ void compact_rerank(
     const uint8_t* __restrict__ scores, int64_t Epad, int64_t S, int64_t E,
     const int32_t* __restrict__ meta, const uint32_t* __restrict__ coff, int chunk_stride,
     int nchunks, const float* __restrict__ ptab, const uint32_t* __restrict__ rec,
@@ -1074,6 +1072,31 @@ __global__ __launch_bounds__(256, 7) void k_compact_rerank(
     mm[((int64_t)bh * chunk_stride + chunk) * 2 + 1] = max(max(s_mm[4], s_mm[5]), max(s_mm[6], s_mm[7]));
   }
 }
+
+// The m = 8 separate-threshold form is held to 72 VGPRs (7 waves per SIMD, 7
+// blocks per CU) by its launch bounds, one more resident block per CU than
+// the 74 it would take; the other forms keep what they need (held to 72, the
+// fused-threshold and m = 4 forms spill).
+#define PKV_CR_PARAMS                                                                          \
+  const uint8_t* __restrict__ scores, int64_t Epad, int64_t S, int64_t E,                      \
+      const int32_t* __restrict__ meta, const uint32_t* __restrict__ coff, int chunk_stride,   \
+      int nchunks, const float* __restrict__ ptab, const uint32_t* __restrict__ rec,           \
+      int64_t cap, int32_t* __restrict__ cand, float* __restrict__ est, int64_t cstride,       \
+      int64_t C, uint32_t* __restrict__ mm, int swar, int unit_div,                            \
+      const uint32_t* __restrict__ chist, int nbins, int rstride, int32_t* __restrict__ meta_out
+#define PKV_CR_ARGS                                                                            \
+  scores, Epad, S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, cand, est, cstride, C, \
+      mm, swar, unit_div, chist, nbins, rstride, meta_out
+template <int KPT, int CPB>
+__global__ __launch_bounds__(256, 7) void k_compact_rerank_m8(PKV_CR_PARAMS) {
+  compact_rerank<KPT, CPB, 8, false>(PKV_CR_ARGS);
+}
+template <int KPT, int CPB, int M, bool FT>
+__global__ __launch_bounds__(256) void k_compact_rerank(PKV_CR_PARAMS) {
+  compact_rerank<KPT, CPB, M, FT>(PKV_CR_ARGS);
+}
+#undef PKV_CR_PARAMS
+#undef PKV_CR_ARGS
 
 // ---------------------------------------------------------------------------
 // K6 exact top-k over the reranked candidates ([TS] Key Contributions 2:
@@ -2887,9 +2910,15 @@ hipError_t launch_compact_rerank(int m, int kpt, int nchunks, int BH, const uint
   const dim3 grid((nchunks + kCompactChunks - 1) / kCompactChunks, BH);
 #define PKV_CR(K, MM, FT)                                                                     \
   case K:                                                                                     \
-    return launch(k_compact_rerank<K, kCompactChunks, MM, FT>, grid, dim3(256), st, ev,       \
-                  scores, Epad, S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, cand,  \
-                  est, cstride, C, mm, swar, unit_div, chist, nbins, rstride, meta_out);
+    return (MM == 8 && !FT)                                                                   \
+               ? launch(k_compact_rerank_m8<K, kCompactChunks>, grid, dim3(256), st, ev,      \
+                        scores, Epad, S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, \
+                        cand, est, cstride, C, mm, swar, unit_div, chist, nbins, rstride,      \
+                        meta_out)                                                             \
+               : launch(k_compact_rerank<K, kCompactChunks, MM, FT>, grid, dim3(256), st, ev, \
+                        scores, Epad, S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, \
+                        cand, est, cstride, C, mm, swar, unit_div, chist, nbins, rstride,      \
+                        meta_out);
 #define PKV_CRK(MM, FT)                                                                      \
   switch (kpt) {                                                                             \
     PKV_CR(1, MM, FT) PKV_CR(2, MM, FT) PKV_CR(4, MM, FT) PKV_CR(8, MM, FT) PKV_CR(16, MM, FT) \
