@@ -55,6 +55,11 @@ SMALL = {
                        sinks=32, seed=23),
     "m4_rho8": W("m 4, rho 8", 1, 2, 8, 128, 30000, "bf16", B=32, rho=8,
                  tiers=(7, 6, 5, 4, 3, 2, 1, 1), k=512, seed=24),
+    # one head of 100K keys at m = 4: 391 chunks of 256 keys, above the
+    # fused-threshold limit, so the separate threshold and the m = 4
+    # compaction that reads it
+    "m4_many_chunks": W("m 4, 1 head, 100K keys", 1, 1, 4, 128, 100000, "bf16", B=32,
+                        k=1024, seed=39),
     # degenerate sizes: one key to select, one eligible key, E a whole number
     # of 256-key chunks (no partial chunk) and one key more (a 1-key chunk)
     # 1600 candidates of 8000 keys: the resident single kernel near its
