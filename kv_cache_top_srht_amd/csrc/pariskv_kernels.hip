@@ -2910,15 +2910,15 @@ hipError_t launch_compact_rerank(int m, int kpt, int nchunks, int BH, const uint
   const dim3 grid((nchunks + kCompactChunks - 1) / kCompactChunks, BH);
 #define PKV_CR(K, MM, FT)                                                                     \
   case K:                                                                                     \
-    return (MM == 8 && !FT)                                                                   \
-               ? launch(k_compact_rerank_m8<K, kCompactChunks>, grid, dim3(256), st, ev,      \
-                        scores, Epad, S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, \
-                        cand, est, cstride, C, mm, swar, unit_div, chist, nbins, rstride,      \
-                        meta_out)                                                             \
-               : launch(k_compact_rerank<K, kCompactChunks, MM, FT>, grid, dim3(256), st, ev, \
-                        scores, Epad, S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, \
-                        cand, est, cstride, C, mm, swar, unit_div, chist, nbins, rstride,      \
-                        meta_out);
+    if constexpr (MM == 8 && !(FT))                                                           \
+      return launch(k_compact_rerank_m8<K, kCompactChunks>, grid, dim3(256), st, ev, scores,  \
+                    Epad, S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap, cand, est, \
+                    cstride, C, mm, swar, unit_div, chist, nbins, rstride, meta_out);         \
+    else                                                                                      \
+      return launch(k_compact_rerank<K, kCompactChunks, MM, FT>, grid, dim3(256), st, ev,     \
+                    scores, Epad, S, E, meta, coff, chunk_stride, nchunks, ptab, rec, cap,    \
+                    cand, est, cstride, C, mm, swar, unit_div, chist, nbins, rstride,         \
+                    meta_out);
 #define PKV_CRK(MM, FT)                                                                      \
   switch (kpt) {                                                                             \
     PKV_CR(1, MM, FT) PKV_CR(2, MM, FT) PKV_CR(4, MM, FT) PKV_CR(8, MM, FT) PKV_CR(16, MM, FT) \
