@@ -641,21 +641,22 @@ __global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ ch
   const uint32_t* hb = chist + (int64_t)bh * chunk_stride * rstride;
   for (int v = tid; v < 260; v += 1024) s_tot[v] = 0;
   // column sums over the chunk rows: thread = (row r0, group g of 4 bins),
-  // 16-byte loads, 8 rows in flight per thread, summed in registers
+  // 16-byte loads, 16 rows in flight per thread (a million-token unit's 512
+  // rows of 65 bins in one round), summed in registers
   const int ng = rstride >> 2, rpp = 1024 / ng;
   const int g = tid % ng, r0 = tid / ng;
   uint32_t acc[4] = {0u, 0u, 0u, 0u};
   if (r0 < rpp) {
     const uint4* h4 = reinterpret_cast<const uint4*>(hb);
-    for (int rb = r0; rb < nchunks; rb += 8 * rpp) {
-      uint4 v[8];
+    for (int rb = r0; rb < nchunks; rb += 16 * rpp) {
+      uint4 v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         const int row = rb + u * rpp;
         v[u] = (row < nchunks) ? h4[(int64_t)row * ng + g] : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         acc[0] += v[u].x;
         acc[1] += v[u].y;
         acc[2] += v[u].z;
