@@ -374,6 +374,7 @@ def main():
         traffic = read_traffic("retrieve_single_%s%s_traffic.txt" % (args.workload, variant),
                                scan_bytes)
 
+    step_bytes = scan_bytes + (0.0 if (args.si or single) else rerank_bytes) + attn_bytes
     result = {
         "metric": METRIC,
         "value": value,
@@ -430,6 +431,16 @@ def main():
             "frac": attn_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_launch": attn_bytes,
             "avg_launch_us": attn_us,
+        },
+        # the whole step against the HBM peak: the bytes the method must move
+        # per step (ids of every key, the candidates' records, the selected
+        # K/V rows with q and out), over the timed per-step time
+        "step_roofline": {
+            "algorithmic_bytes_per_step": step_bytes,
+            "achieved": step_bytes / (us_per_step * 1e-6) / 1e9,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": step_bytes / (us_per_step * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "floor_us_at_peak": step_bytes / (HBM_PEAK_GBPS * 1e9) * 1e6,
         },
         "rerank_gather": None if (args.si or single) else {
             "kernel": "compact_rerank",

@@ -40,6 +40,11 @@ def test_bench_json_line():
         assert key in roof, key
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-9
+    # the whole step against the same peak
+    sr = j["step_roofline"]
+    assert sr["algorithmic_bytes_per_step"] >= roof["algorithmic_bytes_per_launch"]
+    assert abs(sr["frac"] - sr["achieved"] / sr["peak"]) < 1e-9
+    assert 0 < sr["frac"] < 1 and sr["floor_us_at_peak"] < j["ms_per_step"] * 1e3
     cb = j["cpu_baseline"]
     for key in ("value", "unit", "cores", "threads", "host_cores", "kind", "sample"):
         assert key in cb, key
