@@ -683,7 +683,10 @@ __global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ ch
   __syncthreads();
   const int T = s_T;
   const int64_t Q = (all_ties ? (int64_t)s_tot[T] : C) - (int64_t)s_tot[T + 1];
-  uint32_t carry_tie = 0, carry_off = 0;
+  // Ties are taken in position order until the quota Q is used up, so the
+  // chunks before c hold min(#ties before c, Q) of them: one scan of (ties,
+  // keys above T) gives a chunk both its ties before and its offset.
+  uint32_t carry_tie = 0, carry_gt = 0;
   for (int c0 = 0; c0 < nchunks; c0 += 1024) {
     const int c = c0 + tid;
     uint32_t gt = 0, eq = 0;
@@ -693,19 +696,15 @@ __global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ ch
       eq = hc[T] - gt;
     }
     uint2 tot;
-    const uint2 ex = block_exscan2<1024>(make_uint2(eq, 0), s_w, tot);
+    const uint2 ex = block_exscan2<1024>(make_uint2(eq, gt), s_w, tot);
     const uint32_t tie_before = carry_tie + ex.x;
-    int64_t quota = Q - (int64_t)tie_before;
-    if (quota < 0) quota = 0;
-    const uint32_t sel = gt + (uint32_t)((int64_t)eq < quota ? eq : quota);
-    uint2 tot2;
-    const uint2 ex2 = block_exscan2<1024>(make_uint2(sel, 0), s_w, tot2);
+    const int64_t taken = (int64_t)tie_before < Q ? (int64_t)tie_before : Q;
     if (c < nchunks) {
-      coff[((int64_t)bh * chunk_stride + c) * 2 + 0] = carry_off + ex2.x;
+      coff[((int64_t)bh * chunk_stride + c) * 2 + 0] = carry_gt + ex.y + (uint32_t)taken;
       coff[((int64_t)bh * chunk_stride + c) * 2 + 1] = tie_before;
     }
     carry_tie += tot.x;
-    carry_off += tot2.x;
+    carry_gt += tot.y;
   }
 }
 
@@ -947,18 +946,17 @@ __device__ __forceinline__ void compact_rerank(
       gt = (T + 1 < nbins) ? hc[T + 1] : 0u;
       eq = hc[T] - gt;
     }
+    // one scan of (ties, keys above T): the chunks before this one hold
+    // min(#ties before it, Q) of the kept ties
     uint2 tot;
-    const uint2 ex = block_exscan2<256>(make_uint2(eq, 0), s_w2, tot);
-    int64_t quota = Q - (int64_t)ex.x;
-    if (quota < 0) quota = 0;
-    const uint32_t sel = gt + (uint32_t)((int64_t)eq < quota ? eq : quota);
-    const uint2 ex2 = block_exscan2<256>(make_uint2(sel, 0), s_w2, tot);
+    const uint2 ex = block_exscan2<256>(make_uint2(eq, gt), s_w2, tot);
+    const int64_t taken = (int64_t)ex.x < Q ? (int64_t)ex.x : Q;
     // hand the two chunks' values to every thread
     __shared__ uint32_t s_co[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       if (tid == c0 + (h < nc ? h : 0)) {
-        s_co[2 * h] = ex2.x;
+        s_co[2 * h] = ex.y + (uint32_t)taken;
         s_co[2 * h + 1] = ex.x;
       }
     __syncthreads();
@@ -1470,7 +1468,7 @@ __global__ __launch_bounds__(1024) void k_topk_select_few(
   int32_t* oi = out_idx + (int64_t)bh * k;
   __shared__ uint32_t s_hist[2049];
   __shared__ uint64_t s_mem[TK_MAXMEM];
-  __shared__ uint32_t s_cnt[MAXP], s_start[MAXP], s_pref[MAXP + 1];
+  __shared__ uint32_t s_cnt[MAXP], s_start[MAXP], s_pref[MAXP + 1], s_cnt16[16];
   __shared__ uint32_t s_bits[TK_SL / 32];
   __shared__ uint2 s_w[16];
   __shared__ uint32_t s_sel[4];
@@ -1499,11 +1497,19 @@ __global__ __launch_bounds__(1024) void k_topk_select_few(
   s_hist[2 * tid + 1] = a1;
   if (tid == 0) { s_hist[2048] = 0; s_sel[3] = 0; }
   if (tid < TK_SL / 32) s_bits[tid] = 0;
+  // #(bin >= b) falls as b grows and is C >= k' at b = 0, so b1, the last
+  // bin where it is still >= k', is the number of such bins minus one:
+  // counted by ballots, summed over the waves
+  {
+    const uint32_t nge = (uint32_t)__popcll(__ballot(a0 >= (uint32_t)kprime)) +
+                         (uint32_t)__popcll(__ballot(a1 >= (uint32_t)kprime));
+    if ((tid & 63) == 0) s_cnt16[tid >> 6] = nge;
+  }
   __syncthreads();
-  for (int b = tid; b < 2048; b += 1024)
-    if (s_hist[b] >= (uint32_t)kprime && s_hist[b + 1] < (uint32_t)kprime) s_sel[0] = b;
-  __syncthreads();
-  const uint32_t b1 = s_sel[0];
+  uint32_t b1 = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) b1 += s_cnt16[w];
+  b1 -= 1u;
   const uint32_t above_tot = s_hist[b1 + 1];
   const uint32_t M = s_hist[b1] - above_tot;
   const uint32_t remaining = (uint32_t)kprime - above_tot;
@@ -1565,8 +1571,10 @@ __global__ __launch_bounds__(1024) void k_topk_select_few(
   // b1's members: slice q holds them contiguously in its sorted array from
   // #(bin > b1) on
   for (uint32_t j = tid; j < M; j += 1024) {
+    // the last slice q with s_pref[q] <= j (s_pref does not fall, s_pref[0] = 0)
     int q = 0;
-    while (q + 1 < P && s_pref[q + 1] <= j) ++q;
+#pragma unroll
+    for (int qq = 1; qq < MAXP; ++qq) q += (qq < P && s_pref[qq] <= j) ? 1 : 0;
     const uint2 pr = sorted[((int64_t)bh * P + q) * TK_SL + s_start[q] + (j - s_pref[q])];
     s_mem[j] = member_key(pr.x, pr.y);
   }
@@ -2665,12 +2673,14 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
     bm = fmaxf(fmaxf(s_w[0], s_w[1]), fmaxf(s_w[2], s_w[3]));
     const float Mn = fmaxf(M, bm);
     if (Mn != -INFINITY) {
-      const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+      // hardware exp2: every argument is <= 0 (a factor below 2^-126 is
+      // flushed to zero, far below the attention's tolerance)
+      const float r = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
       acc *= r;
       lac *= r;
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        const float f = (mv[u] == -INFINITY) ? 0.0f : exp2f(mv[u] - Mn);
+        const float f = (mv[u] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv[u] - Mn);
         acc = __builtin_fmaf(f, ov[u], acc);
         lac = __builtin_fmaf(f, lv[u], lac);
       }
