@@ -85,9 +85,11 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 
 // ---------------------------------------------------------------------------
 // Block-wide exclusive scan of a pair of uint32 values (NT threads): DPP
-// scans within each wave, wave totals through LDS.
+// scans within each wave, wave totals through LDS.  SYNC_AFTER: a closing
+// barrier, so the caller may write s_warp again at once; callers that do not
+// touch s_warp before another barrier leave it out.
 // ---------------------------------------------------------------------------
-template <int NT>
+template <int NT, bool SYNC_AFTER = true>
 __device__ __forceinline__ uint2 block_exscan2(uint2 v, uint2* s_warp, uint2& total) {
   constexpr int NW = NT / 64;
   // the wave index as a scalar, so the per-wave tests below are scalar
@@ -102,7 +104,7 @@ __device__ __forceinline__ uint2 block_exscan2(uint2 v, uint2* s_warp, uint2& to
     if (w < wv) { base.x += t.x; base.y += t.y; }
     tot.x += t.x; tot.y += t.y;
   }
-  __syncthreads();  // s_warp may be reused by the caller
+  if constexpr (SYNC_AFTER) __syncthreads();  // s_warp may be reused by the caller
   total = tot;
   return make_uint2(base.x + ix - v.x, base.y + iy - v.y);
 }

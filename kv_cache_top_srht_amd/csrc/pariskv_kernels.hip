@@ -696,7 +696,7 @@ __global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ ch
       eq = hc[T] - gt;
     }
     uint2 tot;
-    const uint2 ex = block_exscan2<1024>(make_uint2(eq, gt), s_w, tot);
+    const uint2 ex = block_exscan2<1024, false>(make_uint2(eq, gt), s_w, tot);
     const uint32_t tie_before = carry_tie + ex.x;
     const int64_t taken = (int64_t)tie_before < Q ? (int64_t)tie_before : Q;
     if (c < nchunks) {
@@ -705,6 +705,7 @@ __global__ __launch_bounds__(1024) void k_thresh(const uint32_t* __restrict__ ch
     }
     carry_tie += tot.x;
     carry_gt += tot.y;
+    if (c0 + 1024 < nchunks) __syncthreads();  // the next pass writes s_w again
   }
 }
 
@@ -949,7 +950,7 @@ __device__ __forceinline__ void compact_rerank(
     // one scan of (ties, keys above T): the chunks before this one hold
     // min(#ties before it, Q) of the kept ties
     uint2 tot;
-    const uint2 ex = block_exscan2<256>(make_uint2(eq, gt), s_w2, tot);
+    const uint2 ex = block_exscan2<256, false>(make_uint2(eq, gt), s_w2, tot);
     const int64_t taken = (int64_t)ex.x < Q ? (int64_t)ex.x : Q;
     // hand the two chunks' values to every thread
     __shared__ uint32_t s_co[4];
@@ -1248,7 +1249,7 @@ __device__ __forceinline__ void topk_hist_slice(
   // cumulative row #(bin >= b); thread t owns bins 2047 - 2t and 2046 - 2t
   const uint32_t hh = s_hist[2047 - 2 * tid], hl = s_hist[2046 - 2 * tid];
   uint2 tot;
-  const uint2 ex = block_exscan2<1024>(make_uint2(hh + hl, 0), s_w, tot);
+  const uint2 ex = block_exscan2<1024, false>(make_uint2(hh + hl, 0), s_w, tot);
   // 16-bit entries: a slice holds at most TK_SL candidates
   uint16_t* row = rows + ((int64_t)bh * P + p) * 2048;
   row[2047 - 2 * tid] = (uint16_t)(ex.x + hh);
@@ -1367,7 +1368,7 @@ __device__ __forceinline__ void topk_select_slice(
       nq = rb[(int64_t)q * 2048 + b1] - sq;
     }
     uint2 tt;
-    const uint2 ex = block_exscan2<1024>(make_uint2(nq, q < p ? sq : 0u), s_w, tt);
+    const uint2 ex = block_exscan2<1024, false>(make_uint2(nq, q < p ? sq : 0u), s_w, tt);
     s_pref[q] = ex.x;
     s_start[q] = sq;
     above_before = tt.y;
@@ -1420,7 +1421,7 @@ __device__ __forceinline__ void topk_select_slice(
     }
   }
   uint2 tot;
-  const uint2 ex = block_exscan2<1024>(make_uint2((uint32_t)__popc(selm), 0), s_w, tot);
+  const uint2 ex = block_exscan2<1024, false>(make_uint2((uint32_t)__popc(selm), 0), s_w, tot);
   uint32_t pos = above_before + s_sel[3] + ex.x;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -1616,7 +1617,7 @@ __global__ __launch_bounds__(1024) void k_topk_select_few(
     }
   }
   uint2 tot;
-  const uint2 ex = block_exscan2<1024>(make_uint2((uint32_t)__popc(selm), 0), s_w, tot);
+  const uint2 ex = block_exscan2<1024, false>(make_uint2((uint32_t)__popc(selm), 0), s_w, tot);
   uint32_t pos = above_before + s_sel[3] + ex.x;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
