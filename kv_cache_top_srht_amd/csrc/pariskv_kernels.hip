@@ -434,27 +434,30 @@ __device__ __forceinline__ void scan_keys(const uint4* __restrict__ src, int chu
   if (lane == 0) s_hist[wv][0] = zeros;
 }
 
-// The chunk's cumulative row from the wave histograms.
+// The chunk's cumulative row from the wave histograms: wave 0 alone, lane l
+// adding bins 4 l .. 4 l + 3 of every wave's histogram (16-byte LDS reads),
+// while the other waves are done.
 template <int NT>
 __device__ __forceinline__ void scan_rows(uint32_t (*s_hist)[256], uint32_t* __restrict__ row,
                                           int nbins, int rstride) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   __syncthreads();
-  // sum the wave histograms into row 0
-  for (int v = tid; v < nbins; v += NT) {
-    uint32_t a = s_hist[0][v];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) a += s_hist[w][v];
-    s_hist[0][v] = a;
-  }
-  __syncthreads();
   // chunk row = #(score >= v) for every v: suffix sums by wave 0, lane l
   // owning bins 4 l .. 4 l + 3 (rows rstride words apart; bins >= nbins are 0)
   if (wv == 0) {
+    uint32_t hs[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint4 x = reinterpret_cast<const uint4*>(s_hist[w])[lane];
+      hs[0] += x.x;
+      hs[1] += x.y;
+      hs[2] += x.z;
+      hs[3] += x.w;
+    }
     uint32_t h[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) h[r] = (4 * lane + r < nbins) ? s_hist[0][4 * lane + r] : 0u;
+    for (int r = 0; r < 4; ++r) h[r] = (4 * lane + r < nbins) ? hs[r] : 0u;
     const uint32_t loc = h[0] + h[1] + h[2] + h[3];
     uint32_t inc = loc;  // sum over lanes >= this one
 #pragma unroll
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(NT) void k_scan(const uint4* __restrict__ ids, int6
                                              int rstride, int unit_div) {
   const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   __shared__ uint8_t s_lut[16 * 256];
-  __shared__ uint32_t s_hist[NT / 64][256];
+  __shared__ __align__(16) uint32_t s_hist[NT / 64][256];
   // The LUT load goes out first, from every thread (a load under a branch
   // would make the compiler wait for it at the join, before the key loads
   // are issued; threads tid and tid + 256 store the same bytes).
@@ -1222,10 +1225,11 @@ __device__ __forceinline__ void topk_hist_slice(
   const float f[4] = {fv.x, fv.y, fv.z, fv.w};
   // this (b, h)'s estimate range from the per-chunk ranges
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  const uint32_t* mb = mmc + (int64_t)bh * chunk_stride * 2;
+  const uint2* mb = reinterpret_cast<const uint2*>(mmc + (int64_t)bh * chunk_stride * 2);
   for (int c = tid; c < nchunks; c += 1024) {
-    kmin = min(kmin, mb[2 * c]);
-    kmax = max(kmax, mb[2 * c + 1]);
+    const uint2 r = mb[c];
+    kmin = min(kmin, r.x);
+    kmax = max(kmax, r.y);
   }
   for (int i = tid; i < 2048; i += 1024) s_hist[i] = 0;
 #pragma unroll
