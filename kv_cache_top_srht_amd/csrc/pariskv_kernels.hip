@@ -764,6 +764,11 @@ __device__ __forceinline__ float quad_lane(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x55 * S, 0xF, 0xF, true));
 }
 
+// value of the pair lane (lane ^ 1), a DPP quad permutation [1, 0, 3, 2]
+__device__ __forceinline__ float dppf_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
 // LDS product table: subspace b's 128 entries ([j][code]) start at b * 132
 // floats, so the 4 lanes of a group (subspaces 4q + bb, q = 0..3) read
 // disjoint 16-bank ranges.
@@ -776,9 +781,9 @@ constexpr int kPtabLds = 16 * kPtabRow;
 // product table in LDS, and every lane of the group returns the sum of all
 // B terms in b order.
 template <int M>
-__device__ __forceinline__ float rerank_estimate(
+__device__ __forceinline__ void rerank_terms(
     const uint4 cw, const typename std::conditional<M == 8, uint2, uint4>::type ww,
-    const float* s_P, int q) {
+    const float* s_P, int q, float (&t)[32 / M]) {
   constexpr int NB = 32 / M;
   const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
   uint32_t wsw[NB / 2];
@@ -819,7 +824,6 @@ __device__ __forceinline__ float rerank_estimate(
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  float t[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     float p = 0.0f;
@@ -828,6 +832,18 @@ __device__ __forceinline__ float rerank_estimate(
     const uint16_t hb = (uint16_t)(wsw[i >> 1] >> ((i & 1) * 16));
     t[i] = (float)__builtin_bit_cast(_Float16, hb) * p;
   }
+}
+
+// the estimate by lanes 4 c + q of a quad (lane q of the quad holds
+// quarter q's terms): every lane of the quad returns the sum of all B terms
+// in b order
+template <int M>
+__device__ __forceinline__ float rerank_estimate(
+    const uint4 cw, const typename std::conditional<M == 8, uint2, uint4>::type ww,
+    const float* s_P, int q) {
+  constexpr int NB = 32 / M;
+  float t[NB];
+  rerank_terms<M>(cw, ww, s_P, q, t);
   float e = 0.0f;
 #pragma unroll
   for (int i = 0; i < NB; ++i) e = e + quad_lane<0>(t[i]);
@@ -837,6 +853,39 @@ __device__ __forceinline__ float rerank_estimate(
   for (int i = 0; i < NB; ++i) e = e + quad_lane<2>(t[i]);
 #pragma unroll
   for (int i = 0; i < NB; ++i) e = e + quad_lane<3>(t[i]);
+  return e;
+}
+
+// The estimate with a candidate's quarters q = 2 h + b on lanes 32 h + 2 c + b
+// of a wave (c = the candidate's slot, 0..15): a half-wave then holds two
+// quarters of 16 candidates, whose product-table reads (rows 4 q + i, 132
+// floats apart) fall in disjoint 16-bank ranges of 32.  Lane 2 c (quarter 0)
+// gathers the other quarters' terms -- quarter 1 from its pair lane by a DPP
+// move, quarters 2 and 3 from the upper half by a lane swap -- and adds all
+// B terms in b order; the other lanes' results are not used.
+template <int M>
+__device__ __forceinline__ float rerank_estimate_halves(
+    const uint4 cw, const typename std::conditional<M == 8, uint2, uint4>::type ww,
+    const float* s_P, int q) {
+  constexpr int NB = 32 / M;
+  float t[NB], u[NB];
+  rerank_terms<M>(cw, ww, s_P, q, t);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    // lanes 0..31 receive lane + 32's value
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[i]), __float_as_uint(t[i]),
+                                                     false, false);
+    u[i] = __uint_as_float(sw[1]);
+  }
+  float e = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) e = e + t[i];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) e = e + dppf_xor1(t[i]);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) e = e + u[i];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) e = e + dppf_xor1(u[i]);
   return e;
 }
 
@@ -1014,14 +1063,17 @@ __device__ __forceinline__ void compact_rerank(
   __syncthreads();
 
   const uint32_t ntot = nsel0 + nsel1;
-  // 4 lanes per candidate: lane q reads the codes of coordinates 32 q ..
-  // 32 q + 31 (16 B) and the w of their NB subspaces (NB = 32 / M; 2 NB
-  // bytes) from the candidate's record and forms w_b p_b for them; DPP
-  // broadcasts give every lane all 4 NB terms, summed in b order.  Up to 4
-  // candidates per group are fetched before any is used.
-  constexpr int NB = 32 / M;
+  // 4 lanes per candidate: the lane of quarter q reads the codes of
+  // coordinates 32 q .. 32 q + 31 (16 B) and the w of their 32 / M
+  // subspaces from the candidate's record and forms w_b p_b for them;
+  // quarter 0's lane adds all B terms in b order.  Lane 32 h + 2 c + b of
+  // wave w takes quarter q = 2 h + b of candidate slot 16 w + c (see
+  // rerank_estimate_halves).  Up to 4 candidates per slot are fetched before
+  // any is used.
   using WT = typename std::conditional<M == 8, uint2, uint4>::type;
-  const int q = tid & 3;
+  const int lane = tid & 63;
+  const int q = 2 * (lane >> 5) + (lane & 1);
+  const int slot = 16 * (tid >> 6) + ((lane >> 1) & 15);
   const uint32_t* rq = rec + (int64_t)(bh / unit_div) * cap * 32;  // the unit's KV head
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;  // order keys of this block's estimates
   for (uint32_t j0 = 0; j0 < ntot; j0 += 256) {
@@ -1030,7 +1082,7 @@ __device__ __forceinline__ void compact_rerank(
     int64_t pi[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t j = j0 + r * 64 + (tid >> 2);
+      const uint32_t j = j0 + r * 64 + slot;
       const bool has = j < ntot;
       const uint32_t ent = has ? s_list[j] : 0u;
       const int h = (int)(ent >> 14);
@@ -1044,15 +1096,16 @@ __device__ __forceinline__ void compact_rerank(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (j0 + r * 64 >= ntot) break;  // uniform across the block
-      const uint32_t j = j0 + r * 64 + (tid >> 2);
-      const float e = rerank_estimate<M>(cw[r], ww[r], s_P, q);
+      const uint32_t j = j0 + r * 64 + slot;
+      const float e = rerank_estimate_halves<M>(cw[r], ww[r], s_P, q);
       // the range update is unconditional (masked by selects), so the sum's
-      // additions stay beside their lane moves and fold into DPP adds
-      const bool valid = j < ntot;
+      // additions stay beside their lane moves and fold into DPP adds; only
+      // quarter 0's lane holds the estimate
+      const bool valid = j < ntot && q == 0;
       const uint32_t ok = order_key(e);
       kmn = min(kmn, valid ? ok : 0xFFFFFFFFu);
       kmx = max(kmx, valid ? ok : 0u);
-      if (valid && q == 0) {
+      if (valid) {
         const uint32_t o = (j >= nsel0) ? off_c[1] + (j - nsel0) : off_c[0] + j;
         if ((int64_t)o < C) {  // always true when K4a and this kernel agree
           cand[bh * cstride + o] = (int32_t)pi[r];
